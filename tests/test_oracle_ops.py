@@ -1,0 +1,273 @@
+"""Pins for the oracle's buffer operations (CPU only).
+
+Checks round trips, special cases that reduce to a library routine (torch
+CPU casts and fp32 arithmetic, math.fsum), closed forms (all-ones and
+integer norms, the tile absmax element encoding to +-Q) and the tile
+numbering on a non-square group where a transposed index would fail.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import casts as C
+from oracle import ops as O
+from oracle import plan as P
+
+
+def _setup(w, A=1):
+    items = P.items_from_specs(w.tensors)
+    p = P.plan(items, w.m, A)
+    return items, p
+
+
+def _ragged_group():
+    """Small group with ragged fragments, element/row/block granules,
+    non-square tiles and partial edge tiles."""
+    ts = (W.TensorSpec("a", 40, 24, gran_rows=8, q_rows=8, q_cols=16),
+          W.TensorSpec("v", 1, 37, gran_rows=0),
+          W.TensorSpec("b", 30, 12, gran_rows=6, q_rows=6, q_cols=8),
+          W.TensorSpec("e", 50, 10, gran_rows=1, q_rows=1, q_cols=4),
+          W.TensorSpec("c", 7, 33, gran_rows=4, q_rows=4, q_cols=16))
+    return W.Workload("ragged_small", ts, m=5, qfmt="fp8_e4m3", block=8)
+
+
+@pytest.mark.parametrize("A", [1, 16])
+def test_pack_unpack_roundtrip(A):
+    w = _ragged_group()
+    items, p = _setup(w, A)
+    inp = W.make_inputs(w)
+    buf = np.full(p.total, 7.0, dtype=np.float32)
+    packed = O.pack(inp.params, p.offsets, p.S, w.m, buf, "f32", 0, w.m)
+    dsts = [np.zeros_like(t) for t in inp.params]
+    back = O.unpack(packed, [(s.rows, s.cols) for s in w.tensors], p.offsets, p.S, w.m,
+                    dsts, "f32", 0, w.m)
+    for a, b in zip(inp.params, back):
+        assert np.array_equal(a, b)
+    # padding positions are zero; tensor positions hold the tensor
+    used = np.zeros(p.total, bool)
+    for t, l in zip(inp.params, p.offsets):
+        used[l:l + t.size] = True
+        assert np.array_equal(packed[l:l + t.size], t.reshape(-1))
+    assert np.all(packed[~used] == 0)
+    # bf16 buffer: equals torch's cast of the concatenation
+    bufh = np.zeros(p.total, dtype=np.uint16)
+    ph = O.pack(inp.params, p.offsets, p.S, w.m, bufh, "bf16", 0, w.m)
+    for t, l in zip(inp.params, p.offsets):
+        ref = torch.from_numpy(t.reshape(-1).copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(ph[l:l + t.size], ref)
+    back = O.unpack(ph, [(s.rows, s.cols) for s in w.tensors], p.offsets, p.S, w.m,
+                    [np.zeros_like(t) for t in inp.params], "f32", 0, w.m)
+    for t, b in zip(inp.params, back):
+        ref = torch.from_numpy(t.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+        assert np.array_equal(b, ref)
+
+
+def test_pack_rank_range_only():
+    w = _ragged_group()
+    items, p = _setup(w, 1)
+    inp = W.make_inputs(w)
+    buf = np.full(p.total, 7.0, dtype=np.float32)
+    k0, k1 = 1, 3
+    out = O.pack(inp.params, p.offsets, p.S, w.m, buf, "f32", k0, k1)
+    assert np.all(out[:k0 * p.S] == 7.0) and np.all(out[k1 * p.S:] == 7.0)
+    full = O.pack(inp.params, p.offsets, p.S, w.m, buf, "f32", 0, w.m)
+    assert np.array_equal(out[k0 * p.S:k1 * p.S], full[k0 * p.S:k1 * p.S])
+
+
+def test_scale_add_special_cases_and_torch():
+    w = _ragged_group()
+    items, p = _setup(w, 1)
+    rng = np.random.default_rng(2)
+    y = rng.standard_normal(p.total).astype(np.float32)
+    x = rng.standard_normal(p.total).astype(np.float32)
+    pads = np.ones(p.total, bool)
+    for it, l in zip(items, p.offsets):
+        pads[l:l + it.numel] = False
+    out, f = O.scale_add(y, x, 1.0, 0.0, items, p.offsets, p.S, w.m, 0, w.m)
+    assert np.array_equal(out, y) and not f.any()
+    out, _ = O.scale_add(y, x, 0.0, 1.5, items, p.offsets, p.S, w.m, 0, w.m)
+    assert np.array_equal(out[~pads], (np.float32(1.5) * x)[~pads])
+    assert np.array_equal(out[pads], y[pads])
+    out, _ = O.scale_add(y, x, 1.0, 1.0, items, p.offsets, p.S, w.m, 0, w.m)
+    ref = (torch.from_numpy(y) + torch.from_numpy(x)).numpy()
+    assert np.array_equal(out[~pads], ref[~pads])
+    a, b = 0.37, -1.25
+    out, _ = O.scale_add(y, x, a, b, items, p.offsets, p.S, w.m, 0, w.m)
+    ty, tx = torch.from_numpy(y), torch.from_numpy(x)
+    ref = torch.add(torch.mul(ty, a), torch.mul(tx, b)).numpy()
+    assert np.array_equal(out[~pads], ref[~pads])
+    # bf16 x is widened exactly
+    xh = C.bf16_bits_from_f32(x)
+    out, _ = O.scale_add(y, xh, 1.0, 1.0, items, p.offsets, p.S, w.m, 0, w.m)
+    ref = (ty + torch.from_numpy(x).to(torch.bfloat16).to(torch.float32)).numpy()
+    assert np.array_equal(out[~pads], ref[~pads])
+
+
+def test_scale_add_mask_and_found_inf():
+    w = _ragged_group()
+    items, p = _setup(w, 1)
+    y = np.ones(p.total, np.float32)
+    x = np.ones(p.total, np.float32)
+    fr = P.fragments(items, p.offsets, p.S, w.m)
+    # one inf in the fragment of tensor 2 that lies in its last rank
+    t2 = [f for f in fr if f[0] == 2]
+    tid, k, lo, hi = t2[-1]
+    x[lo] = np.inf
+    out, found = O.scale_add(y, x, 1.0, 1.0, items, p.offsets, p.S, w.m, 0, w.m)
+    assert found.tolist() == [1 if r == k else 0 for r in range(w.m)]
+    mask = [1, 1, 0, 1, 1]
+    out, found = O.scale_add(y, x, 1.0, 1.0, items, p.offsets, p.S, w.m, 0, w.m, mask=mask)
+    assert not found.any()
+    assert np.all(out[p.offsets[2]:p.offsets[2] + items[2].numel] == 1)
+    # outside the rank range nothing changes and nothing is flagged
+    out, found = O.scale_add(y, x, 1.0, 1.0, items, p.offsets, p.S, w.m, 0, k)
+    assert not found.any() and np.all(out[k * p.S:] == 1)
+
+
+def test_zero_mask_and_pads():
+    w = _ragged_group()
+    items, p = _setup(w, 16)
+    y = np.full(p.total, 3.0, np.float32)
+    out = O.zero(y, items, p.offsets, p.S, w.m, 1, 4)
+    assert np.all(out[p.S:4 * p.S] == 0) and np.all(out[:p.S] == 3) and np.all(out[4 * p.S:] == 3)
+    mask = [0, 1, 0, 0, 1]
+    out = O.zero(y, items, p.offsets, p.S, w.m, 0, w.m, mask=mask)
+    for t, (it, l) in enumerate(zip(items, p.offsets)):
+        assert np.all(out[l:l + it.numel] == (0 if mask[t] else 3))
+    pads = np.ones(p.total, bool)
+    for it, l in zip(items, p.offsets):
+        pads[l:l + it.numel] = False
+    assert np.all(out[pads] == 3)
+
+
+def test_sqnorm_closed_forms():
+    w = _ragged_group()
+    items, p = _setup(w, 1)
+    ones = np.ones(p.total, np.float32)
+    sq, part, found = O.sqnorm(ones, items, p.offsets, p.S, w.m, 0, w.m)
+    assert sq.tolist() == [float(it.numel) for it in items]
+    assert np.array_equal(part.sum(axis=0), sq)
+    rng = np.random.default_rng(4)
+    ints = rng.integers(-50, 51, size=p.total).astype(np.float32)
+    sq, part, _ = O.sqnorm(ints, items, p.offsets, p.S, w.m, 0, w.m)
+    for t, (it, l) in enumerate(zip(items, p.offsets)):
+        exact = sum(int(v) ** 2 for v in ints[l:l + it.numel])
+        assert sq[t] == exact
+    x = rng.standard_normal(p.total).astype(np.float32)
+    sq, part, _ = O.sqnorm(x, items, p.offsets, p.S, w.m, 0, w.m)
+    for t, (it, l) in enumerate(zip(items, p.offsets)):
+        ref = math.fsum(float(v) * float(v) for v in x[l:l + it.numel])
+        assert abs(sq[t] - ref) <= 1e-13 * ref
+        # partials are the fragment sums, in rank order
+        for k in range(w.m):
+            lo, hi = max(l, k * p.S), min(l + it.numel, (k + 1) * p.S)
+            ref_k = math.fsum(float(v) * float(v) for v in x[lo:hi]) if hi > lo else 0.0
+            assert abs(part[k, t] - ref_k) <= 1e-13 * max(ref_k, 1e-300)
+
+
+def test_sqnorm_nonfinite_classes():
+    w = _ragged_group()
+    items, p = _setup(w, 1)
+    x = np.ones(p.total, np.float32)
+    l0, l2 = p.offsets[0], p.offsets[2]
+    x[l0 + 3] = np.inf
+    x[l2 + 5] = np.nan
+    x[l2 + 6] = -np.inf
+    sq, part, found = O.sqnorm(x, items, p.offsets, p.S, w.m, 0, w.m)
+    assert sq[0] == np.inf and np.isnan(sq[2]) and np.isfinite(sq[1])
+    assert found[(l0 + 3) // p.S] == 1 and found[(l2 + 5) // p.S] == 1
+
+
+def test_quant_tile_amax_encodes_to_q():
+    rng = np.random.default_rng(9)
+    for fmt, top in (("fp8_e4m3", 0x7E), ("int8", 127)):
+        for _ in range(200):
+            t = (rng.standard_normal((8, 16)) * 10 ** rng.uniform(-30, 30)).astype(np.float32)
+            sc, cd = O.quant_tile(t, fmt)
+            i = np.unravel_index(np.argmax(np.abs(t)), t.shape)
+            c = int(cd[i])
+            if fmt == "fp8_e4m3":
+                assert c & 0x7F == top and (c >> 7) == int(t[i] < 0)
+            else:
+                assert np.int8(np.uint8(c)) == (top if t[i] > 0 else -top)
+
+
+def test_quant_dequant_error_bound_and_torch_fp8():
+    rng = np.random.default_rng(10)
+    t = (rng.standard_normal((32, 32)) * 0.02).astype(np.float32)
+    sc, cd = O.quant_tile(t, "fp8_e4m3")
+    q = (t / sc).astype(np.float32)
+    ref = torch.from_numpy(np.clip(q, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(cd, ref)
+    dq = C.e4m3fn_to_f64(cd) * np.float64(sc)
+    # relative error of a normal E4M3 value is at most 2^-4; subnormals 2^-10 * scale
+    err = np.abs(dq - t)
+    bound = np.maximum(np.abs(t) * 2.0 ** -4, 2.0 ** -10 * sc) * 1.0001
+    assert np.all(err <= bound)
+    sc, cd = O.quant_tile(t, "int8")
+    dq = cd.view(np.int8).astype(np.float64) * sc
+    assert np.all(np.abs(dq - t) <= 0.5 * sc * 1.0001)
+
+
+def test_quant_special_tiles():
+    z = np.zeros((4, 4), np.float32)
+    sc, cd = O.quant_tile(z, "fp8_e4m3")
+    assert sc == 0 and not cd.any()
+    n = np.ones((4, 4), np.float32)
+    n[1, 2] = np.nan
+    sc, cd = O.quant_tile(n, "fp8_e4m3")
+    assert np.float32(sc).view(np.uint32) == 0x7FC00000 and np.all(cd == 0x7F)
+    sc, cd = O.quant_tile(n, "int8")
+    assert np.all(cd == 0)
+    i = np.ones((4, 4), np.float32)
+    i[0, 0] = -np.inf
+    sc, cd = O.quant_tile(i, "fp8_e4m3")
+    assert sc == np.inf and cd[0, 0] == 0x7F and np.all(cd.reshape(-1)[1:] == 0x00)
+    i[0, 1] = -1.0
+    sc, cd = O.quant_tile(i, "fp8_e4m3")
+    assert cd[0, 1] == 0x80     # -1/inf = -0
+    tiny = np.full((2, 2), 1e-44, np.float32)   # amax/448 underflows to 0
+    sc, cd = O.quant_tile(tiny, "int8")
+    assert sc == 0 and not cd.any()
+
+
+def test_block_quant_tile_numbering_and_positions():
+    w = _ragged_group()
+    items, p = _setup(w, 1)
+    x = np.zeros(p.total, np.float32)
+    # give every tile a distinct amax at a known element
+    tiles = []
+    for s, l in zip(w.tensors, p.offsets):
+        if s.q_rows:
+            for (r0, r1, c0, c1) in O.tile_grid(s.rows, s.cols, s.q_rows, s.q_cols):
+                tiles.append((l, s.cols, r0, r1, c0, c1))
+    for j, (l, C_, r0, r1, c0, c1) in enumerate(tiles):
+        rr, cc = r1 - 1, c1 - 1           # bottom-right element of the tile
+        x[l + rr * C_ + cc] = np.float32(448.0 * (j + 1))
+        x[l + r0 * C_ + c0] = np.float32(-1.0)
+    assert len(tiles) == O.num_tiles(w.tensors)
+    codes = np.full(p.total, 0xAB, np.uint8)
+    scales = np.full(len(tiles), -1.0, np.float32)
+    cd, sc = O.block_quant(x, w.tensors, p.offsets, p.S, w.m, "fp8_e4m3", 0, w.m, codes, scales)
+    for j, (l, C_, r0, r1, c0, c1) in enumerate(tiles):
+        assert sc[j] == np.float32(j + 1)
+        assert cd[l + (r1 - 1) * C_ + (c1 - 1)] == 0x7E
+        if (r1 - 1, c1 - 1) != (r0, c0):
+            # -1/(j+1) encodes as a negative code
+            assert cd[l + r0 * C_ + c0] & 0x80
+    # non-quantised tensor and padding positions untouched
+    v = p.offsets[1]
+    assert np.all(cd[v:v + 37] == 0xAB)
+
+
+def test_block_quant_straddle_rejected():
+    ts = (W.TensorSpec("a", 8, 4, gran_rows=0, q_rows=4, q_cols=4),)
+    items = P.items_from_specs(ts)
+    p = P.plan(items, 3, 1)
+    x = np.ones(p.total, np.float32)
+    with pytest.raises(ValueError):
+        O.block_quant(x, ts, p.offsets, p.S, 3, "int8", 0, 3,
+                      np.zeros(p.total, np.uint8), np.zeros(2, np.float32))
