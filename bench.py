@@ -1,0 +1,251 @@
+"""Benchmark of the RaggedShard flat-buffer hot path on one MI355X.
+
+One step = one pass of every grouped operation over one FSDP unit's planned
+buffer, all ranks (the whole buffer):
+  pack (fp32 params -> bf16 buffer), unpack (bf16 buffer -> bf16 tensors),
+  group scale-add (fp32 grad accumulation with found-inf), ragged squared
+  norms (fp64), block quantisation (FP8 E4M3 / INT8 codes + fp32 scales) and
+  group zero (fp32 grad buffer, padding included).
+Inputs are resident in HBM before timing.  Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "HBM GB/s and % of MI355X peak per DBuffer op on the Llama-8B-layer group"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "fsdp_sharded_buffer_amd", "csrc", "rs_kernels.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def op_bytes(w, S, n_tiles):
+    """Algorithmic bytes per launch of each operation (whole buffer)."""
+    E = w.numel
+    mS = w.m * S
+    Eq = sum(t.numel for t in w.tensors if t.q_rows)
+    return {
+        "pack": 4 * E + 2 * mS,          # fp32 tensors in, whole bf16 buffer out (pads zeroed)
+        "unpack": 2 * E + 2 * E,         # bf16 buffer in, bf16 tensors out
+        "scale_add": 12 * E,             # y in, x in, y out (fp32)
+        "sqnorm": 4 * E,                 # fp32 in
+        "block_quant": 5 * Eq + 4 * n_tiles,  # fp32 in, codes + scales out
+        "zero": 4 * mS,                  # whole fp32 buffer out
+    }
+
+
+def read_counters(workload: str):
+    """HBM traffic of the scale-add kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"counters_scale_add_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_sha256_16") != source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, offs, S, inp, k1):
+    """The oracle, untuned, on ranks [0, k1) of the same workload."""
+    from oracle import casts as OC
+    from oracle import ops as O
+    from oracle import plan as P
+
+    items = P.items_from_specs(w.tensors)
+    total = w.m * S
+    m = w.m
+    fmt = w.qfmt
+    y0 = np.zeros(total, np.float32)
+    x0 = np.zeros(total, np.float32)
+    for a, g, l in zip(inp.params, inp.grads, offs):
+        y0[l:l + a.size] = g.reshape(-1)
+        x0[l:l + a.size] = g.reshape(-1)
+    t0 = time.perf_counter()
+    buf = O.pack(inp.params, offs, S, m, np.zeros(total, np.uint16), "bf16", 0, k1)
+    O.unpack(buf, [(s.rows, s.cols) for s in w.tensors], offs, S, m,
+             [np.zeros(s.numel, np.uint16) for s in w.tensors], "bf16", 0, k1)
+    y, _ = O.scale_add(y0, x0, 1.0, 1.0, items, offs, S, m, 0, k1)
+    O.sqnorm(y, items, offs, S, m, 0, k1)
+    nt = O.num_tiles(w.tensors)
+    O.block_quant(y, w.tensors, offs, S, m, fmt, 0, k1, np.zeros(total, np.uint8),
+                  np.zeros(nt, np.float32))
+    O.zero(x0, items, offs, S, m, 0, k1)
+    dt = time.perf_counter() - t0
+    # algorithmic bytes of the sample: the ranks' share of every operation
+    frac_e = sum(max(0, min(l + it.numel, k1 * S) - l) for it, l in zip(items, offs)) / w.numel
+    qs = [(t, l) for t, l in zip(w.tensors, offs) if t.q_rows]
+    eq_in = sum(max(0, min(l + t.numel, k1 * S) - l) for t, l in qs)
+    E_in = frac_e * w.numel
+    b = (4 * E_in + 2 * k1 * S) + 4 * E_in + 12 * E_in + 4 * E_in + 5 * eq_in + 4 * k1 * S
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"ranks [0,{k1}) of {m} ({k1 * S} buffer positions), one pass of all six "
+                      f"operations, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_layer")
+    ap.add_argument("--align", type=int, default=16)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--samples", type=int, default=15)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-ranks", type=int, default=0)
+    ap.add_argument("--only", default="", help="comma list of ops to time per op (default all)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the m virtual ranks are slices of one device buffer "
+              "and this build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fsdp_sharded_buffer_amd as R
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    log(f"bench: {w.name} m={w.m} elements={w.numel}")
+    offs, pinfo = R.rs_plan(w.tensors, w.m, args.align)
+    S = pinfo["S"]
+    lay = R.Layout(w.tensors, w.m, S, offs, args.chunk)
+    total = w.m * S
+    m = w.m
+    log(f"planned S={S} pad={pinfo['pad_frac']*100:.2f}% in {pinfo['seconds']*1e3:.1f} ms; "
+        f"chunks={lay.info['num_chunks']} tiles={lay.info['num_tiles']}")
+    inp = W.make_inputs(w)
+    log("inputs drawn")
+    dev = torch.device("cuda", 0)
+    params = [torch.from_numpy(a).to(dev) for a in inp.params]
+    pbuf = torch.empty(total, dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty(t.numel, dtype=torch.bfloat16, device=dev) for t in w.tensors]
+    acc = torch.zeros(total, dtype=torch.float32, device=dev)
+    grad = torch.zeros(total, dtype=torch.float32, device=dev)
+    for g, l in zip(inp.grads, offs):
+        grad[l:l + g.size].copy_(torch.from_numpy(g.reshape(-1)))
+        acc[l:l + g.size].copy_(torch.from_numpy(g.reshape(-1)))
+    found = torch.zeros(m, dtype=torch.int32, device=dev)
+    sq = torch.empty(len(w.tensors), dtype=torch.float64, device=dev)
+    codes = torch.empty(total, dtype=torch.uint8, device=dev)
+    scales = torch.empty(lay.info["num_tiles"], dtype=torch.float32, device=dev)
+    ptab, otab = R.ptr_table(params), R.ptr_table(outs)
+    qfmt = R.RS_Q_FP8_E4M3 if w.qfmt == "fp8_e4m3" else R.RS_Q_INT8
+    h = lay.handle
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    ops = {
+        "pack": lambda: R.rs_pack(h, ptab, R.RS_F32, pbuf, R.RS_BF16, 0, m, sp),
+        "unpack": lambda: R.rs_unpack(h, pbuf, R.RS_BF16, otab, R.RS_BF16, 0, m, sp),
+        "scale_add": lambda: R.rs_group_scale_add(h, acc, grad, R.RS_F32, 1.0, 1.0, None, found,
+                                                  0, m, sp),
+        "sqnorm": lambda: R.rs_ragged_sqnorm(h, acc, sq, None, None, lay.ws, 0, m, sp),
+        "block_quant": lambda: R.rs_block_quant(h, acc, qfmt, codes, scales, 0, m, sp),
+        "zero": lambda: R.rs_group_zero(h, grad, R.RS_F32, None, 0, m, sp),
+    }
+    nbytes = op_bytes(w, S, lay.info["num_tiles"])
+
+    def step():
+        for f in ops.values():
+            f()
+
+    # whole-step throughput
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt / args.steps * 1e3
+    step_bytes = sum(nbytes.values())
+    value = step_bytes * args.steps / dt / 1e9
+    log(f"step: {ms_step:.3f} ms, {value:.1f} GB/s")
+
+    # per-operation launch time with HIP events on the launch stream
+    only = [o for o in args.only.split(",") if o] or list(ops)
+    per_op = {}
+    for name in only:
+        f = ops[name]
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        one = max(e0.elapsed_time(e1), 1e-3)
+        reps = max(1, int(20.0 / one))
+        samples = []
+        for _ in range(args.samples):
+            e0.record(stream)
+            for _ in range(reps):
+                f()
+            e1.record(stream)
+            e1.synchronize()
+            samples.append(e0.elapsed_time(e1) / reps)
+        med = float(np.median(samples))
+        gbs = nbytes[name] / (med * 1e-3) / 1e9
+        per_op[name] = {"us": round(med * 1e3, 2), "min_us": round(min(samples) * 1e3, 2),
+                        "bytes": nbytes[name], "GB/s": round(gbs, 1),
+                        "frac_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps}
+        log(f"{name:12s} {med*1e3:9.1f} us  {gbs:8.1f} GB/s  {gbs/HBM_PEAK_GBS*100:5.1f}% of peak")
+
+    dom = "scale_add" if "scale_add" in per_op else next(iter(per_op))
+    roof = {"kernel": "scale_add_kernel<fp32>" if dom == "scale_add" else dom,
+            "bound": "hbm", "achieved": per_op[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": per_op[dom]["frac_peak"], "traffic": read_counters(w.name),
+            "bytes_per_launch": nbytes[dom], "avg_launch_us": per_op[dom]["us"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        k1 = args.cpu_ranks or max(1, m // 4)
+        log(f"cpu baseline: oracle on ranks [0,{k1})")
+        cpu = cpu_baseline(w, offs, S, inp, k1)
+        log(f"cpu baseline {cpu['value']} GB/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "elements": w.numel, "m": m, "S": S,
+                   "align": args.align, "chunk_elems": lay.info["chunk_elems"],
+                   "qfmt": w.qfmt, "step_bytes": step_bytes, "planner_ms": round(pinfo["seconds"] * 1e3, 3),
+                   "pad_frac": round(pinfo["pad_frac"], 5)},
+        "frac_peak": round(value / HBM_PEAK_GBS, 4),
+        "ops": per_op,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+        "host": platform.processor() or platform.machine(),
+    }
+    print(json.dumps(out), flush=True)
+    lay.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,101 @@
+// Internal types shared by the planner, the layout builder and the kernels.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "rs.h"
+
+namespace rs {
+
+// One work chunk: a run of buffer positions inside one rank that is either
+// part of one tensor or padding.  Chunks partition the whole buffer in
+// buffer order, so a rank range maps to one contiguous run of chunks.
+struct ChunkDesc {
+  int64_t buf_off;  // first buffer position
+  int64_t ten_off;  // first tensor element, -1 for padding
+  int32_t len;      // elements
+  int32_t tensor;   // -1 for padding
+  int32_t rank;
+  int32_t frag;     // fragment index, -1 for padding
+};
+static_assert(sizeof(ChunkDesc) == 32, "ChunkDesc layout");
+
+// A tensor-rank intersection; its chunks are [chunk_begin, chunk_end).
+struct FragDesc {
+  int32_t tensor;
+  int32_t rank;
+  int32_t chunk_begin;
+  int32_t chunk_end;
+};
+static_assert(sizeof(FragDesc) == 16, "FragDesc layout");
+
+// Per tensor: its fragments (all ranks) are [frag_begin, frag_end) and the
+// ranks it touches are [rank_lo, rank_hi).
+struct TensorDesc {
+  int32_t frag_begin;
+  int32_t frag_end;
+  int32_t rank_lo;
+  int32_t rank_hi;
+};
+static_assert(sizeof(TensorDesc) == 16, "TensorDesc layout");
+
+// One quantisation tile: rows x cols elements at buffer position buf_off
+// with row stride ld; its scale goes to scales[scale_idx].
+struct TileDesc {
+  int64_t buf_off;
+  int64_t ld;
+  int32_t rows;
+  int32_t cols;
+  int32_t scale_idx;
+  int32_t rank;
+};
+static_assert(sizeof(TileDesc) == 32, "TileDesc layout");
+
+// One workgroup of the quantisation kernel: `count` consecutive tiles, each
+// handled by a team of `team` lanes (power of two, 8..256); vec = 1 when
+// every tile of the item allows 16-byte loads.
+struct QuantWork {
+  int32_t tile_begin;
+  int32_t count;
+  int32_t team;
+  int32_t vec;
+};
+static_assert(sizeof(QuantWork) == 16, "QuantWork layout");
+
+constexpr int kMaxTileElems = 16384;  // 256 lanes x 64 elements held in registers
+constexpr int64_t kDefaultChunk = 16384;
+
+}  // namespace rs
+
+struct rs_layout {
+  int32_t n = 0, m = 0;
+  int64_t S = 0;
+  std::vector<rs_tensor_spec> specs;
+  std::vector<int64_t> offsets;
+  int64_t chunk_elems = 0;
+
+  std::vector<rs::TensorDesc> tensors;
+  std::vector<rs::FragDesc> frags;
+  std::vector<rs::ChunkDesc> chunks;
+  std::vector<rs::TileDesc> tiles;
+  std::vector<rs::QuantWork> work;
+
+  // per-rank begin indices, size m + 1
+  std::vector<int64_t> rank_chunk, rank_frag, rank_tile, rank_work;
+
+  // byte offsets of each table inside the device blob
+  size_t off_tensors = 0, off_frags = 0, off_chunks = 0, off_tiles = 0, off_work = 0;
+  size_t device_bytes = 0;
+  size_t workspace_bytes = 0;
+
+  // device copy (caller-owned), set by rs_layout_upload
+  void* dev = nullptr;
+};
+
+namespace rs {
+// Records a message for rs_last_error() and returns `st`.
+rs_status fail(rs_status st, const std::string& msg);
+void clear_error();
+}  // namespace rs

@@ -1,0 +1,259 @@
+// Layout validation and descriptor tables (host side).
+//
+// The tables are the device-resident group description every grouped kernel
+// reads, so one launch covers a whole tensor group (veScale-FSDP: Flexible
+// and High-Performance FSDP at Scale, "DBuffer": group-level operators and a
+// persistent mapping from each tensor to its place in the buffer).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "rs_internal.h"
+
+using namespace rs;
+
+namespace {
+
+int64_t granule_of(const rs_tensor_spec& s) { return s.gran_rows > 0 ? s.gran_rows * s.cols : 1; }
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Lanes per tile: enough that no lane holds more than 64 elements.
+int team_for(int64_t elems) {
+  int team = 8;
+  while (team < 256 && int64_t(team) * 64 < elems) team *= 2;
+  return team;
+}
+
+rs_status build(rs_layout* L) {
+  const int32_t n = L->n, m = L->m;
+  const int64_t S = L->S, CH = L->chunk_elems;
+  L->tensors.assign(n, TensorDesc{});
+  L->frags.clear();
+  L->chunks.clear();
+  L->tiles.clear();
+  L->work.clear();
+  L->rank_chunk.assign(m + 1, 0);
+  L->rank_frag.assign(m + 1, 0);
+  L->rank_tile.assign(m + 1, 0);
+  L->rank_work.assign(m + 1, 0);
+
+  auto add_chunks = [&](int64_t lo, int64_t hi, int32_t tensor, int64_t ten_lo, int32_t rank,
+                        int32_t frag) {
+    for (int64_t p = lo; p < hi; p += CH) {
+      ChunkDesc c;
+      c.buf_off = p;
+      c.ten_off = tensor >= 0 ? ten_lo + (p - lo) : -1;
+      c.len = int32_t(std::min(CH, hi - p));
+      c.tensor = tensor;
+      c.rank = rank;
+      c.frag = frag;
+      L->chunks.push_back(c);
+    }
+  };
+
+  // Walk ranks in buffer order; inside a rank, tensors in order (offsets are
+  // increasing), padding chunks in the gaps.
+  int32_t t_first = 0;
+  for (int32_t k = 0; k < m; ++k) {
+    const int64_t rlo = int64_t(k) * S, rhi = rlo + S;
+    L->rank_chunk[k] = int64_t(L->chunks.size());
+    L->rank_frag[k] = int64_t(L->frags.size());
+    int64_t pos = rlo;
+    while (t_first < n && L->offsets[t_first] + L->specs[t_first].rows * L->specs[t_first].cols <= rlo)
+      ++t_first;
+    for (int32_t t = t_first; t < n; ++t) {
+      const int64_t l = L->offsets[t];
+      const int64_t r = l + L->specs[t].rows * L->specs[t].cols;
+      if (l >= rhi) break;
+      const int64_t lo = std::max(l, rlo), hi = std::min(r, rhi);
+      if (lo >= hi) continue;
+      if (lo > pos) add_chunks(pos, lo, -1, -1, k, -1);
+      const int32_t f = int32_t(L->frags.size());
+      FragDesc fd;
+      fd.tensor = t;
+      fd.rank = k;
+      fd.chunk_begin = int32_t(L->chunks.size());
+      add_chunks(lo, hi, t, lo - l, k, f);
+      fd.chunk_end = int32_t(L->chunks.size());
+      L->frags.push_back(fd);
+      pos = hi;
+    }
+    if (pos < rhi) add_chunks(pos, rhi, -1, -1, k, -1);
+  }
+  L->rank_chunk[m] = int64_t(L->chunks.size());
+  L->rank_frag[m] = int64_t(L->frags.size());
+  if (L->chunks.size() > size_t(INT32_MAX) || L->frags.size() > size_t(INT32_MAX))
+    return fail(RS_ERR_INVALID_ARG, "rs_layout_create: too many chunks; raise chunk_elems");
+
+  // tensor -> fragment range and rank range
+  for (int32_t t = 0; t < n; ++t) {
+    L->tensors[t].frag_begin = -1;
+  }
+  for (int32_t f = 0; f < int32_t(L->frags.size()); ++f) {
+    TensorDesc& td = L->tensors[L->frags[f].tensor];
+    if (td.frag_begin < 0) {
+      td.frag_begin = f;
+      td.rank_lo = L->frags[f].rank;
+    }
+    td.frag_end = f + 1;
+    td.rank_hi = L->frags[f].rank + 1;
+  }
+
+  // quantisation tiles, tensor by tensor, row-major; ranks are
+  // non-decreasing in this order because tensors and tile rows are
+  int32_t scale_idx = 0;
+  for (int32_t t = 0; t < n; ++t) {
+    const rs_tensor_spec& s = L->specs[t];
+    if (s.q_rows <= 0) continue;
+    for (int64_t r0 = 0; r0 < s.rows; r0 += s.q_rows) {
+      const int64_t r1 = std::min(s.rows, r0 + s.q_rows);
+      for (int64_t c0 = 0; c0 < s.cols; c0 += s.q_cols) {
+        const int64_t c1 = std::min(s.cols, c0 + s.q_cols);
+        TileDesc td;
+        td.buf_off = L->offsets[t] + r0 * s.cols + c0;
+        td.ld = s.cols;
+        td.rows = int32_t(r1 - r0);
+        td.cols = int32_t(c1 - c0);
+        td.scale_idx = scale_idx++;
+        const int64_t last = L->offsets[t] + (r1 - 1) * s.cols + (c1 - 1);
+        td.rank = int32_t(td.buf_off / S);
+        if (last / S != td.buf_off / S)
+          return fail(RS_ERR_INVALID_ARG,
+                      "rs_layout_create: a quantisation tile of tensor " + std::to_string(t) +
+                          " crosses a shard boundary");
+        L->tiles.push_back(td);
+      }
+    }
+  }
+  // tiles per rank and workgroup items (consecutive tiles of one rank with
+  // the same team size and vector flag)
+  size_t i = 0;
+  for (int32_t k = 0; k < m; ++k) {
+    L->rank_tile[k] = int64_t(i);
+    L->rank_work[k] = int64_t(L->work.size());
+    while (i < L->tiles.size() && L->tiles[i].rank == k) {
+      const TileDesc& a = L->tiles[i];
+      const int team = team_for(int64_t(a.rows) * a.cols);
+      const int vec = (a.cols % 4 == 0 && a.ld % 4 == 0 && a.buf_off % 4 == 0) ? 1 : 0;
+      QuantWork w{int32_t(i), 0, team, vec};
+      const int cap = 256 / team;
+      while (i < L->tiles.size() && L->tiles[i].rank == k && w.count < cap) {
+        const TileDesc& b = L->tiles[i];
+        const int vb = (b.cols % 4 == 0 && b.ld % 4 == 0 && b.buf_off % 4 == 0) ? 1 : 0;
+        if (team_for(int64_t(b.rows) * b.cols) != team || vb != vec) break;
+        ++w.count;
+        ++i;
+      }
+      L->work.push_back(w);
+    }
+  }
+  L->rank_tile[m] = int64_t(L->tiles.size());
+  L->rank_work[m] = int64_t(L->work.size());
+
+  size_t off = 0;
+  L->off_tensors = off;
+  off = align256(off + sizeof(TensorDesc) * L->tensors.size());
+  L->off_frags = off;
+  off = align256(off + sizeof(FragDesc) * L->frags.size());
+  L->off_chunks = off;
+  off = align256(off + sizeof(ChunkDesc) * L->chunks.size());
+  L->off_tiles = off;
+  off = align256(off + sizeof(TileDesc) * L->tiles.size());
+  L->off_work = off;
+  off = align256(off + sizeof(QuantWork) * L->work.size());
+  L->device_bytes = std::max<size_t>(off, 256);
+  // sqnorm scratch: one fp64 partial per chunk plus one per fragment
+  L->workspace_bytes = align256(sizeof(double) * L->chunks.size()) +
+                       align256(sizeof(double) * L->frags.size());
+  return RS_OK;
+}
+
+}  // namespace
+
+extern "C" rs_status rs_layout_create(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t S,
+                                      const int64_t* offsets, int64_t chunk_elems,
+                                      rs_layout** out) {
+  if (!specs || !offsets || !out || n <= 0 || m <= 0 || S <= 0)
+    return fail(RS_ERR_INVALID_ARG, "rs_layout_create: null pointer or non-positive n/m/S");
+  if (chunk_elems == 0) chunk_elems = kDefaultChunk;
+  if (chunk_elems < 64 || chunk_elems % 64 || chunk_elems > (int64_t(1) << 30))
+    return fail(RS_ERR_INVALID_ARG, "rs_layout_create: chunk_elems must be a multiple of 64");
+  int64_t prev_end = 0;
+  for (int32_t t = 0; t < n; ++t) {
+    const rs_tensor_spec& s = specs[t];
+    const std::string name = "tensor " + std::to_string(t);
+    if (s.rows <= 0 || s.cols <= 0 || s.gran_rows < 0)
+      return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name + " has a bad shape");
+    if ((s.q_rows > 0) != (s.q_cols > 0) || s.q_rows < 0 || s.q_cols < 0 ||
+        int64_t(s.q_rows) * s.q_cols > kMaxTileElems)
+      return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name +
+                                          " has a bad quantisation tile (at most 16384 elements)");
+    const int64_t l = offsets[t], E = s.rows * s.cols, g = granule_of(s);
+    if (l < prev_end)
+      return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name + " overlaps the previous tensor");
+    if (l + E > S * m)
+      return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name + " ends past the buffer");
+    for (int64_t b = (l / S + 1) * S; b < l + E; b += S)
+      if ((b - l) % g)
+        return fail(RS_ERR_INVALID_ARG,
+                    "rs_layout_create: " + name + " has a granule cut by a shard boundary");
+    prev_end = l + E;
+  }
+  rs_layout* L = new rs_layout;
+  L->n = n;
+  L->m = m;
+  L->S = S;
+  L->specs.assign(specs, specs + n);
+  L->offsets.assign(offsets, offsets + n);
+  L->chunk_elems = chunk_elems;
+  rs_status st = build(L);
+  if (st != RS_OK) {
+    delete L;
+    return st;
+  }
+  *out = L;
+  clear_error();
+  return RS_OK;
+}
+
+extern "C" rs_status rs_layout_get_info(const rs_layout* L, rs_layout_info* info) {
+  if (!L || !info) return fail(RS_ERR_INVALID_ARG, "rs_layout_get_info: null pointer");
+  info->n = L->n;
+  info->m = L->m;
+  info->S = L->S;
+  info->total = L->S * L->m;
+  info->num_chunks = int64_t(L->chunks.size());
+  info->num_frags = int64_t(L->frags.size());
+  info->num_tiles = int64_t(L->tiles.size());
+  info->chunk_elems = L->chunk_elems;
+  info->device_bytes = int64_t(L->device_bytes);
+  info->workspace_bytes = int64_t(L->workspace_bytes);
+  return RS_OK;
+}
+
+extern "C" rs_status rs_layout_upload(rs_layout* L, void* dev_table, void* stream) {
+  if (!L || !dev_table) return fail(RS_ERR_INVALID_ARG, "rs_layout_upload: null pointer");
+  if (reinterpret_cast<uintptr_t>(dev_table) % 256)
+    return fail(RS_ERR_ALIGN, "rs_layout_upload: dev_table must be 256-byte aligned");
+  std::vector<unsigned char> blob(L->device_bytes, 0);
+  auto put = [&](size_t off, const void* p, size_t bytes) {
+    if (bytes) std::memcpy(blob.data() + off, p, bytes);
+  };
+  put(L->off_tensors, L->tensors.data(), sizeof(TensorDesc) * L->tensors.size());
+  put(L->off_frags, L->frags.data(), sizeof(FragDesc) * L->frags.size());
+  put(L->off_chunks, L->chunks.data(), sizeof(ChunkDesc) * L->chunks.size());
+  put(L->off_tiles, L->tiles.data(), sizeof(TileDesc) * L->tiles.size());
+  put(L->off_work, L->work.data(), sizeof(QuantWork) * L->work.size());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dev_table, blob.data(), blob.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess)
+    return fail(RS_ERR_HIP, std::string("rs_layout_upload: ") + hipGetErrorString(e));
+  L->dev = dev_table;
+  clear_error();
+  return RS_OK;
+}
+
+extern "C" void rs_layout_destroy(rs_layout* L) { delete L; }

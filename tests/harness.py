@@ -1,0 +1,142 @@
+"""Shared helpers for the GPU parity tests: run an operation through the
+C-ABI on seeded inputs and run the oracle on the same bytes."""
+from __future__ import annotations
+
+import os
+import sys
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+
+import workloads as W
+from oracle import casts as OC
+from oracle import ops as O
+from oracle import plan as P
+
+GUARD = 64  # canary elements before and after every device output
+
+
+def log(msg: str) -> None:
+    """Progress line naming the case, flushed before each GPU step."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+_INT_VIEW = {4: "int32", 2: "int16", 1: "uint8", 8: "int64"}
+
+
+def guarded(n: int, dtype, bits: int):
+    """Device tensor of n elements with GUARD canaries on each side, every
+    element preset to the bit pattern `bits`; returns (whole, view)."""
+    torch = torch_mod()
+    whole = torch.empty(n + 2 * GUARD, dtype=dtype, device="cuda")
+    iv = getattr(torch, _INT_VIEW[whole.element_size()])
+    width = 8 * whole.element_size()
+    sval = bits - (1 << width) if (iv != torch.uint8 and bits >= 1 << (width - 1)) else bits
+    whole.view(iv).fill_(sval)
+    return whole, whole[GUARD:GUARD + n]
+
+
+def check_guards(whole, bits: int, what: str) -> None:
+    h = to_np(whole)
+    u = h.view({4: np.uint32, 2: np.uint16, 1: np.uint8, 8: np.uint64}[h.itemsize])
+    assert np.all(u[:GUARD] == bits), f"{what}: write before the buffer"
+    assert np.all(u[-GUARD:] == bits), f"{what}: write past the buffer"
+
+
+def to_np(t) -> np.ndarray:
+    torch = torch_mod()
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def from_np(a: np.ndarray, dtype=None):
+    torch = torch_mod()
+    if a.dtype == np.uint16 and dtype is None:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@dataclass
+class Case:
+    """A workload planned by both sides, with its inputs on host and device."""
+
+    w: W.Workload
+    A: int
+    chunk: int
+
+    def __post_init__(self):
+        import fsdp_sharded_buffer_amd as R
+        self.R = R
+        self.items = P.items_from_specs(self.w.tensors)
+        offs, info = R.rs_plan(self.w.tensors, self.w.m, self.A)
+        self.S = info["S"]
+        self.offsets = offs
+        # the oracle's own planner must agree (both are exact, same tie-break)
+        if len(self.items) <= 40:
+            p = P.plan(self.items, self.w.m, self.A)
+            assert (p.S, p.offsets) == (self.S, offs)
+        self.lay = R.Layout(self.w.tensors, self.w.m, self.S, offs, self.chunk)
+        self.total = self.w.m * self.S
+        self.inp = None
+
+    @property
+    def m(self) -> int:
+        return self.w.m
+
+    def inputs(self):
+        if self.inp is None:
+            self.inp = W.make_inputs(self.w)
+        return self.inp
+
+    def flat(self, arrays: List[np.ndarray], fill=0.0) -> np.ndarray:
+        """Host fp32 buffer image: arrays at their offsets, fill elsewhere."""
+        buf = np.full(self.total, fill, dtype=np.float32)
+        for a, l in zip(arrays, self.offsets):
+            buf[l:l + a.size] = a.reshape(-1)
+        return buf
+
+    def ranges(self):
+        m = self.m
+        rs = [(0, m), (0, 1), (m - 1, m)]
+        if m > 2:
+            rs.append((1, m - 1))
+        return rs
+
+
+def assert_bits_equal(got: np.ndarray, exp: np.ndarray, what: str) -> None:
+    if got.dtype == np.float32:
+        g, e = got.view(np.uint32), exp.astype(np.float32).view(np.uint32)
+    elif got.dtype == np.float64:
+        g, e = got.view(np.uint64), exp.astype(np.float64).view(np.uint64)
+    else:
+        g, e = got, exp
+    if not np.array_equal(g, e):
+        bad = np.flatnonzero(g.reshape(-1) != e.reshape(-1))
+        i = bad[0]
+        raise AssertionError(f"{what}: {bad.size} mismatches, first at {i}: got {got.reshape(-1)[i]!r} "
+                             f"({g.reshape(-1)[i]:#x}) expected {exp.reshape(-1)[i]!r} ({e.reshape(-1)[i]:#x})")
+
+
+def assert_f32_equal_nan_class(got: np.ndarray, exp: np.ndarray, what: str, max_ulp: int = 0) -> None:
+    """Equal bits for non-NaN values (or within max_ulp), NaN where NaN."""
+    gn, en = np.isnan(got), np.isnan(exp)
+    assert np.array_equal(gn, en), f"{what}: NaN positions differ"
+    g = got[~gn].view(np.int32).astype(np.int64)
+    e = exp[~en].astype(np.float32).view(np.int32).astype(np.int64)
+    # map sign-magnitude to a monotone integer line
+    g = np.where(g < 0, -(g & 0x7FFFFFFF), g)
+    e = np.where(e < 0, -(e & 0x7FFFFFFF), e)
+    d = np.abs(g - e)
+    if d.size and d.max() > max_ulp:
+        i = int(np.argmax(d))
+        raise AssertionError(f"{what}: {int((d > max_ulp).sum())} values off by more than {max_ulp} ulp; "
+                             f"worst {int(d[i])} ulp")

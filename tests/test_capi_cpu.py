@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads and exports every entry
+point of include/rs.h, the host planner agrees with the oracle, layouts are
+validated, and hot calls reject bad arguments before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import plan as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rs.h")
+
+R = pytest.importorskip("fsdp_sharded_buffer_amd")
+from fsdp_sharded_buffer_amd import _lib  # noqa: E402
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(rs_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 13
+    lib = _lib.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (rs_\w+)", out))
+    assert set(names) <= exported
+    # the binding declares exactly the header's entry points
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_binding_has_same_names():
+    for n in _declared():
+        assert callable(getattr(R, n)), n
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+@pytest.mark.parametrize("A", [1, 16])
+def test_planner_matches_oracle(name, A):
+    w = W.WORKLOADS[name]
+    if name == "moe_experts" and A == 1:
+        pytest.skip("oracle scan at A=1 on 193 tensors takes ~50 s; A=16 covers it")
+    offs, info = R.rs_plan(w.tensors, w.m, A)
+    p = P.plan(P.items_from_specs(w.tensors), w.m, A)
+    assert info["S"] == p.S and offs == p.offsets
+    assert info["total"] == w.m * p.S
+    assert info["numel"] == w.numel
+    assert info["pad_elems"] == w.m * p.S - w.numel
+    assert info["lower_bound"] == P.lower_bound(P.items_from_specs(w.tensors), w.m, A)
+    assert info["peak_param_bytes"] == P.peak_param_bytes(p.S, w.m)
+    assert info["seconds"] < 0.3     # the pages' planner budget
+
+
+def test_planner_matches_bruteforce_random():
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        pairs = W.random_tiny_specs(rng, max_t=4, max_e=16, max_g=6)
+        m = int(rng.integers(1, 5))
+        A = int(rng.choice([1, 2, 4]))
+        specs = [W.TensorSpec("t", 1, e, 0) if g == 1 else W.TensorSpec("t", e, 1, g)
+                 for e, g in pairs]
+        items = P.items_from_specs(specs)
+        assert [(i.numel, i.granule) for i in items] == [(e, g) for e, g in pairs]
+        bf = P.plan_bruteforce(items, m, A)
+        offs, info = R.rs_plan(specs, m, A)
+        assert (info["S"], offs) == (bf[0], bf[1]), (pairs, m, A)
+
+
+def test_planner_infeasible_cap_and_bad_args():
+    specs = [W.TensorSpec("a", 12, 1, 4)]
+    with pytest.raises(R.RsError) as e:
+        R.rs_plan(specs, 3, 1, S_cap=3)
+    assert e.value.status == -4
+    with pytest.raises(R.RsError) as e:
+        R.rs_plan(specs, 0, 1)
+    assert e.value.status == -1
+    with pytest.raises(R.RsError):
+        R.rs_plan([W.TensorSpec("a", 0, 4, 0)], 2, 1)
+    assert "rs_plan" in R.rs_last_error()
+
+
+def test_layout_create_validates():
+    w = W.toy_unit()
+    offs, info = R.rs_plan(w.tensors, w.m, 16)
+    h = R.rs_layout_create(w.tensors, w.m, info["S"], offs)
+    li = R.rs_layout_get_info(h)
+    assert li["num_tiles"] == 384 and li["total"] == w.m * info["S"]
+    R.rs_layout_destroy(h)
+    bad = list(offs)
+    bad[2] = bad[1] + 100            # overlaps and misplaces W1
+    with pytest.raises(R.RsError) as e:
+        R.rs_layout_create(w.tensors, w.m, info["S"], bad)
+    assert e.value.status == -1
+    # a granule cut by a boundary
+    specs = [W.TensorSpec("a", 8, 4, 4)]
+    with pytest.raises(R.RsError):
+        R.rs_layout_create(specs, 3, 12, [2])
+    # a quantisation tile crossing a boundary (element granular tensor)
+    specs = [W.TensorSpec("a", 8, 4, 0, 4, 4)]
+    with pytest.raises(R.RsError) as e:
+        R.rs_layout_create(specs, 3, 11, [0])
+    assert "tile" in R.rs_last_error()
+    # oversized tile
+    with pytest.raises(R.RsError):
+        R.rs_layout_create([W.TensorSpec("a", 256, 256, 256, 256, 256)], 1, 65536, [0])
+    with pytest.raises(R.RsError):
+        R.rs_layout_create(w.tensors, w.m, info["S"], offs, chunk_elems=100)
+
+
+def test_layout_tables_partition_buffer():
+    """Chunks cover the buffer exactly, never cross a rank or tensor edge."""
+    w = W.scaled_workload(W.moe_experts(), 16, 8, max_tensors=13, m=5)
+    offs, info = R.rs_plan(w.tensors, w.m, 1)
+    h = R.rs_layout_create(w.tensors, w.m, info["S"], offs, chunk_elems=256)
+    li = R.rs_layout_get_info(h)
+    R.rs_layout_destroy(h)
+    items = P.items_from_specs(w.tensors)
+    fr = P.fragments(items, offs, info["S"], w.m)
+    assert li["num_frags"] == len(fr)
+    # every fragment splits into ceil(len/256) chunks; padding gaps likewise
+    used = sum(-(-(hi - lo) // 256) for _, _, lo, hi in fr)
+    assert li["num_chunks"] >= used
+
+
+def test_hot_calls_reject_before_launch():
+    """Calls on a layout that was never uploaded fail with RS_ERR_STATE and
+    range errors are reported; no device is touched."""
+    w = W.toy_unit()
+    offs, info = R.rs_plan(w.tensors, w.m, 16)
+    h = R.rs_layout_create(w.tensors, w.m, info["S"], offs)
+    lib = _lib.lib()
+    st = lib.rs_pack(h, 16, 0, 16, 1, 0, 1, None)
+    assert st == -7 and "not uploaded" in R.rs_last_error()
+    st = lib.rs_block_quant(None, 16, 0, 16, 16, 0, 1, None)
+    assert st == -1
+    R.rs_layout_destroy(h)
+    assert R.rs_status_str(-5) == "rank range out of bounds"
+    assert R.rs_status_str(0) == "ok"

@@ -1,0 +1,428 @@
+"""GPU parity: every entry point of include/rs.h, called through the C-ABI,
+against the CPU oracle on the same seeded inputs.
+
+Bar: bit-exact for copies, casts, zeros, block scales and FP8/INT8 codes;
+scale/add bit-exact on non-NaN values (the kernel keeps the two products
+and the sum as separate fp32 roundings; the 1-ulp allowance is checked
+too) with NaN where the oracle has NaN; squared norms within 1e-5 relative
+of the fp64 oracle with the same non-finite class.  Every device output is
+surrounded by canary elements that must survive.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import casts as OC
+from oracle import ops as O
+from oracle import plan as P
+
+from harness import (GUARD, Case, assert_bits_equal, assert_f32_equal_nan_class, check_guards,
+                     from_np, guarded, log, to_np)
+
+pytestmark = pytest.mark.gpu
+
+F32_CANARY = 0x7FA5A5A5
+BF16_CANARY = 0x7FA5
+U8_CANARY = 0xAB
+F64_CANARY = 0x7FF5A5A5A5A5A5A5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fsdp_sharded_buffer_amd  # noqa: F401  (fails loudly if librs.so is missing)
+    yield
+
+
+def _moe_small():
+    w = W.moe_experts()
+    ts = list(w.tensors[:12]) + [w.tensors[-1]]
+    return W.scaled_workload(W.Workload("moe4", tuple(ts), m=16, qfmt="fp8_e4m3", block=128,
+                                        grad_dist="student_t3"), 8, 8)
+
+
+def _mixed_small():
+    w = W.ragged_mixed()
+    return W.scaled_workload(W.Workload("mixed2", w.tensors[:19], m=32, qfmt="int8", block=128,
+                                        nonfinite_frac=1e-3), 32, 16)
+
+
+SMALL = {
+    "toy": lambda: (W.toy_unit(), 16, 0),
+    "toy_a1_c64": lambda: (W.toy_unit(), 1, 64),
+    "ragged_a1_c64": lambda: (W.ragged_small(), 1, 64),
+    "ragged_a16_c256": lambda: (W.ragged_small(), 16, 256),
+    "llama8b_div16": lambda: (W.scaled_workload(W.llama8b_layer(), 16, 16), 16, 320),
+    "llama8b_div16_a1": lambda: (W.scaled_workload(W.llama8b_layer(), 16, 16), 1, 1024),
+    "mixed_div": lambda: (_mixed_small(), 16, 512),
+    "moe_div8": lambda: (_moe_small(), 16, 2048),
+    "llama70b_div32": lambda: (W.scaled_workload(W.llama70b_layer(), 32, 32), 16, 0),
+}
+
+_cases = {}
+
+
+def case(name) -> Case:
+    if name not in _cases:
+        w, A, ch = SMALL[name]()
+        _cases[name] = Case(w, A, ch)
+    return _cases[name]
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _dev_tensors(arrays, bf16=False):
+    import torch
+    ts = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in arrays]
+    if bf16:
+        ts = [t.to(torch.bfloat16) for t in ts]
+    return ts
+
+
+# ------------------------------------------------------------------ pack
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("kinds", [("f32", "bf16"), ("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_pack(name, kinds):
+    import torch
+    c = case(name)
+    R = c.R
+    src_k, buf_k = kinds
+    ps = c.inputs().params
+    src = _dev_tensors(ps, bf16=(src_k == "bf16"))
+    src_host = [to_np(t) for t in src]          # bf16 bits or fp32
+    table = R.ptr_table(src)
+    bdt = torch.bfloat16 if buf_k == "bf16" else torch.float32
+    canary = BF16_CANARY if buf_k == "bf16" else F32_CANARY
+    for k0, k1 in c.ranges():
+        log(f"pack {name} {kinds} ranks [{k0},{k1})")
+        whole, buf = guarded(c.total, bdt, canary)
+        R.rs_pack(c.lay.handle, table, R.RS_BF16 if src_k == "bf16" else R.RS_F32, buf,
+                  R.RS_BF16 if buf_k == "bf16" else R.RS_F32, k0, k1)
+        _sync()
+        init = np.full(c.total, canary, dtype=np.uint16 if buf_k == "bf16" else np.uint32)
+        if buf_k == "f32":
+            init = init.view(np.float32)
+        exp = O.pack(src_host, c.offsets, c.S, c.m, init, buf_k, k0, k1)
+        assert_bits_equal(to_np(buf), exp, f"pack {name} {kinds} [{k0},{k1})")
+        check_guards(whole, canary, "pack")
+
+
+# ---------------------------------------------------------------- unpack
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("kinds", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
+def test_unpack(name, kinds):
+    import torch
+    c = case(name)
+    R = c.R
+    buf_k, dst_k = kinds
+    ps = c.inputs().params
+    host_buf = c.flat(ps, fill=np.float32(-7.0))
+    if buf_k == "bf16":
+        host_buf = OC.bf16_bits_from_f32(host_buf)
+    dbuf = from_np(host_buf)
+    ddt = torch.bfloat16 if dst_k == "bf16" else torch.float32
+    canary = BF16_CANARY if dst_k == "bf16" else F32_CANARY
+    for k0, k1 in c.ranges():
+        log(f"unpack {name} {kinds} ranks [{k0},{k1})")
+        outs = [guarded(s.numel, ddt, canary) for s in c.w.tensors]
+        table = R.ptr_table([v for _, v in outs])
+        R.rs_unpack(c.lay.handle, dbuf, R.RS_BF16 if buf_k == "bf16" else R.RS_F32, table,
+                    R.RS_BF16 if dst_k == "bf16" else R.RS_F32, k0, k1)
+        _sync()
+        init_dt = np.uint16 if dst_k == "bf16" else np.uint32
+        inits = [np.full(s.numel, canary, dtype=init_dt) for s in c.w.tensors]
+        if dst_k == "f32":
+            inits = [a.view(np.float32) for a in inits]
+        exp = O.unpack(host_buf, [(s.rows, s.cols) for s in c.w.tensors], c.offsets, c.S, c.m,
+                       inits, dst_k, k0, k1)
+        for t, ((whole, v), e) in enumerate(zip(outs, exp)):
+            assert_bits_equal(to_np(v), e.reshape(-1), f"unpack {name} {kinds} t{t} [{k0},{k1})")
+            check_guards(whole, canary, f"unpack t{t}")
+
+
+def test_pack_unpack_roundtrip_identity():
+    import torch
+    c = case("ragged_a1_c64")
+    R = c.R
+    src = _dev_tensors(c.inputs().params)
+    buf = torch.empty(c.total, dtype=torch.float32, device="cuda")
+    R.rs_pack(c.lay.handle, R.ptr_table(src), R.RS_F32, buf, R.RS_F32, 0, c.m)
+    dst = [torch.empty_like(t) for t in src]
+    R.rs_unpack(c.lay.handle, buf, R.RS_F32, R.ptr_table(dst), R.RS_F32, 0, c.m)
+    _sync()
+    for a, b in zip(src, dst):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------- scale/add
+
+
+def _mask(c, seed):
+    rng = np.random.default_rng(seed)
+    m = rng.integers(0, 2, size=len(c.w.tensors)).astype(np.uint8)
+    m[0] = 1
+    return m
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("xk", ["f32", "bf16"])
+def test_scale_add(name, xk):
+    import torch
+    c = case(name)
+    R = c.R
+    inp = c.inputs()
+    y0 = c.flat(inp.grads, fill=np.float32(12345.0))
+    x0 = c.flat(inp.params, fill=np.float32(-3.0))
+    if xk == "bf16":
+        x0 = OC.bf16_bits_from_f32(x0)
+    dx = from_np(x0)
+    for (alpha, beta) in [(1.0, 1.0), (0.75, -1.5), (1.0, 0.0), (0.0, 2.0), (1.0 / 1024, 3.0e38)]:
+        for use_mask in (False, True):
+            for k0, k1 in c.ranges()[:3]:
+                log(f"scale_add {name} x={xk} a={alpha} b={beta} mask={use_mask} [{k0},{k1})")
+                whole, y = guarded(c.total, torch.float32, F32_CANARY)
+                y.copy_(torch.from_numpy(y0))
+                fi_whole, fi = guarded(c.m, torch.int32, 0)
+                fi.zero_()
+                mask = _mask(c, 3) if use_mask else None
+                dmask = from_np(mask) if use_mask else None
+                R.rs_group_scale_add(c.lay.handle, y, dx, R.RS_BF16 if xk == "bf16" else R.RS_F32,
+                                     alpha, beta, dmask, fi, k0, k1)
+                _sync()
+                ey, ef = O.scale_add(y0, x0, alpha, beta, c.items, c.offsets, c.S, c.m, k0, k1,
+                                     mask=None if mask is None else list(mask))
+                got = to_np(y)
+                what = f"scale_add {name} {xk} a={alpha} b={beta} [{k0},{k1})"
+                assert_f32_equal_nan_class(got, ey, what, max_ulp=1)
+                assert_f32_equal_nan_class(got, ey, what + " (exact)", max_ulp=0)
+                assert np.array_equal(to_np(fi).astype(np.uint32), ef), what + " found_inf"
+                check_guards(whole, F32_CANARY, "scale_add y")
+                check_guards(fi_whole, 0, "found_inf")
+
+
+def test_scale_add_found_inf_ors():
+    import torch
+    c = case("mixed_div")
+    R = c.R
+    inp = c.inputs()
+    y0 = c.flat(inp.params)
+    x0 = c.flat(inp.grads)        # holds +-Inf / NaN
+    ey, ef = O.scale_add(y0, x0, 1.0, 1.0, c.items, c.offsets, c.S, c.m, 0, c.m)
+    assert ef.any() and not ef.all()
+    y = from_np(y0)
+    fi = torch.zeros(c.m, dtype=torch.int32, device="cuda")
+    clean = int(np.flatnonzero(ef == 0)[0])
+    fi[clean] = 1                 # set before the call: must stay set
+    R.rs_group_scale_add(c.lay.handle, y, from_np(x0), R.RS_F32, 1.0, 1.0, None, fi, 0, c.m)
+    _sync()
+    exp = ef.copy()
+    exp[clean] = 1
+    assert np.array_equal(to_np(fi).astype(np.uint32), exp)
+    assert_f32_equal_nan_class(to_np(y), ey, "scale_add nonfinite")
+
+
+# ------------------------------------------------------------------ zero
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("k", ["f32", "bf16"])
+def test_zero(name, k):
+    import torch
+    c = case(name)
+    R = c.R
+    dt = torch.bfloat16 if k == "bf16" else torch.float32
+    canary = BF16_CANARY if k == "bf16" else F32_CANARY
+    for use_mask in (False, True):
+        for k0, k1 in c.ranges():
+            log(f"zero {name} {k} mask={use_mask} [{k0},{k1})")
+            whole, y = guarded(c.total, dt, canary)
+            mask = _mask(c, 5) if use_mask else None
+            R.rs_group_zero(c.lay.handle, y, R.RS_BF16 if k == "bf16" else R.RS_F32,
+                            from_np(mask) if use_mask else None, k0, k1)
+            _sync()
+            init = np.full(c.total, canary, dtype=np.uint16 if k == "bf16" else np.uint32)
+            if k == "f32":
+                init = init.view(np.float32)
+            exp = O.zero(init, c.items, c.offsets, c.S, c.m, k0, k1,
+                         mask=None if mask is None else list(mask))
+            assert_bits_equal(to_np(y), exp, f"zero {name} {k} [{k0},{k1})")
+            check_guards(whole, canary, "zero")
+
+
+# ---------------------------------------------------------------- sqnorm
+
+
+def _check_sq(got, exp, what):
+    gn, en = np.isnan(got), np.isnan(exp)
+    assert np.array_equal(gn, en), what + ": NaN class"
+    gi, ei = np.isinf(got), np.isinf(exp)
+    assert np.array_equal(gi, ei), what + ": Inf class"
+    f = ~(gn | gi)
+    rel = np.abs(got[f] - exp[f]) / np.maximum(np.abs(exp[f]), 1e-300)
+    assert np.all((rel <= 1e-5) | (exp[f] == got[f])), f"{what}: rel err {rel.max()}"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("src", ["params", "grads"])
+def test_sqnorm(name, src):
+    import torch
+    c = case(name)
+    R = c.R
+    inp = c.inputs()
+    x0 = c.flat(getattr(inp, src), fill=np.float32(1e30))   # padding must not count
+    dx = from_np(x0)
+    n = len(c.w.tensors)
+    for k0, k1 in c.ranges():
+        log(f"sqnorm {name} {src} [{k0},{k1})")
+        sw, sq = guarded(n, torch.float64, F64_CANARY)
+        pw, part = guarded(c.m * n, torch.float64, F64_CANARY)
+        fw, fi = guarded(c.m, torch.int32, 0)
+        R.rs_ragged_sqnorm(c.lay.handle, dx, sq, part, fi, c.lay.ws, k0, k1)
+        _sync()
+        esq, epart, ef = O.sqnorm(x0, c.items, c.offsets, c.S, c.m, k0, k1)
+        what = f"sqnorm {name} {src} [{k0},{k1})"
+        _check_sq(to_np(sq), esq, what)
+        gp = to_np(part).reshape(c.m, n)
+        _check_sq(gp[k0:k1], epart[k0:k1], what + " partial")
+        # rows outside the range are not written
+        assert np.all(gp[:k0].view(np.uint64) == F64_CANARY) and np.all(gp[k1:].view(np.uint64) == F64_CANARY)
+        assert np.array_equal(to_np(fi).astype(np.uint32), ef), what + " found_inf"
+        for wh, bits in ((sw, F64_CANARY), (pw, F64_CANARY), (fw, 0)):
+            check_guards(wh, bits, what)
+        # bit-identical on a second run (fixed-order combine)
+        sq2 = torch.empty_like(sq)
+        R.rs_ragged_sqnorm(c.lay.handle, dx, sq2, None, None, c.lay.ws, k0, k1)
+        _sync()
+        assert np.array_equal(to_np(sq2).view(np.uint64), to_np(sq).view(np.uint64)), what + " rerun"
+
+
+def test_sqnorm_closed_forms():
+    import torch
+    c = case("ragged_a1_c64")
+    R = c.R
+    n = len(c.w.tensors)
+    for fill, f in ((1.0, lambda E: float(E)), (3.0, lambda E: 9.0 * E)):
+        x = torch.full((c.total,), fill, dtype=torch.float32, device="cuda")
+        sq = torch.empty(n, dtype=torch.float64, device="cuda")
+        R.rs_ragged_sqnorm(c.lay.handle, x, sq, None, None, c.lay.ws, 0, c.m)
+        _sync()
+        assert to_np(sq).tolist() == [f(s.numel) for s in c.w.tensors]
+
+
+# ----------------------------------------------------------------- quant
+
+
+def _quant_case(c, x0, fmt, k0, k1, what, only_tiles=None):
+    import torch
+    R = c.R
+    nt = c.lay.info["num_tiles"]
+    cw, codes = guarded(c.total, torch.uint8, U8_CANARY)
+    sw, scales = guarded(max(nt, 1), torch.float32, F32_CANARY)
+    R.rs_block_quant(c.lay.handle, from_np(x0), R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8,
+                     codes, scales, k0, k1)
+    _sync()
+    ecodes, escales = O.block_quant(x0, c.w.tensors, c.offsets, c.S, c.m, fmt, k0, k1,
+                                    np.full(c.total, U8_CANARY, np.uint8),
+                                    np.full(max(nt, 1), F32_CANARY, np.uint32).view(np.float32),
+                                    only_tiles=only_tiles)
+    gc, gs = to_np(codes), to_np(scales)
+    if only_tiles is None:
+        assert_bits_equal(gc, ecodes, what + " codes")
+        assert_bits_equal(gs, escales, what + " scales")
+    else:
+        return gc, gs, ecodes, escales
+    check_guards(cw, U8_CANARY, what + " codes")
+    check_guards(sw, F32_CANARY, what + " scales")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "int8"])
+def test_block_quant(name, fmt):
+    c = case(name)
+    inp = c.inputs()
+    for src in ("params", "grads"):
+        x0 = c.flat(getattr(inp, src), fill=np.float32(np.nan))  # padding is never read
+        for k0, k1 in c.ranges():
+            log(f"quant {name} {fmt} {src} [{k0},{k1})")
+            _quant_case(c, x0, fmt, k0, k1, f"quant {name} {fmt} {src} [{k0},{k1})")
+
+
+def _tie_stress_values(rng, scale, fmt, n):
+    """x such that x/scale lands on or next to a rounding midpoint of the
+    code grid, where a wrongly rounded division changes the code."""
+    if fmt == "fp8_e4m3":
+        codes = np.arange(0, 0x7E)
+        mids = (OC.e4m3fn_to_f64(codes) + OC.e4m3fn_to_f64(codes + 1)) / 2
+    else:
+        mids = np.arange(0, 127) + 0.5
+    mids = rng.choice(mids, size=n)
+    x = (mids * scale).astype(np.float32)
+    bump = rng.integers(-2, 3, size=n).astype(np.int32)
+    x = (x.view(np.int32) + bump).view(np.float32)
+    sign = np.where(rng.random(n) < 0.5, -1, 1).astype(np.float32)
+    return x * sign
+
+
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "int8"])
+def test_block_quant_special_values(fmt):
+    """Zero tiles, underflowing scales, huge values, infinities, NaN,
+    subnormals and division results next to code midpoints."""
+    c = case("toy")
+    rng = np.random.default_rng(17)
+    x0 = c.flat(c.inputs().params, fill=np.float32(np.nan))
+    tiles = []
+    for s, l in zip(c.w.tensors, c.offsets):
+        for (r0, r1, c0, c1) in O.tile_grid(s.rows, s.cols, s.q_rows, s.q_cols):
+            pos = l + (np.arange(r0, r1)[:, None] * s.cols + np.arange(c0, c1)[None, :])
+            tiles.append(pos.reshape(-1))
+    Q = 448.0 if fmt == "fp8_e4m3" else 127.0
+    for j, pos in enumerate(tiles):
+        kind = j % 9
+        n = pos.size
+        if kind == 0:
+            x0[pos] = 0.0
+        elif kind == 1:
+            x0[pos] = (rng.standard_normal(n) * 1e-42).astype(np.float32)   # subnormal, scale 0
+        elif kind == 2:
+            x0[pos] = (rng.standard_normal(n) * 1e37).astype(np.float32)
+        elif kind == 3:
+            x0[pos[rng.integers(0, n)]] = np.float32(np.inf) * (1 if j % 2 else -1)
+        elif kind == 4:
+            x0[pos[rng.integers(0, n)]] = np.nan
+        elif kind in (5, 6, 7):
+            amax = np.float32(Q * 10 ** rng.uniform(-3, 3))
+            scale = np.float32(amax / np.float32(Q))
+            v = _tie_stress_values(rng, float(scale), fmt, n - 1)
+            v = np.clip(v, -amax, amax)
+            x0[pos[0]] = amax
+            x0[pos[1:]] = v
+        else:
+            x0[pos] = (rng.standard_normal(n) * 2.0 ** rng.integers(-140, -100)).astype(np.float32)
+    for k0, k1 in c.ranges():
+        _quant_case(c, x0, fmt, k0, k1, f"quant special {fmt} [{k0},{k1})")
+
+
+def test_rank_range_errors():
+    import torch
+    c = case("toy")
+    R = c.R
+    x = torch.zeros(c.total, dtype=torch.float32, device="cuda")
+    for k0, k1 in ((0, 0), (2, 1), (-1, 2), (0, c.m + 1)):
+        with pytest.raises(R.RsError) as e:
+            R.rs_group_zero(c.lay.handle, x, R.RS_F32, None, k0, k1)
+        assert e.value.status == -5
+    with pytest.raises(R.RsError) as e:
+        R.rs_group_zero(c.lay.handle, x, R.RS_U8, None, 0, 1)
+    assert e.value.status == -2
+    with pytest.raises(R.RsError) as e:   # fp32 data at an odd byte address
+        R.rs_group_zero(c.lay.handle, x.view(torch.uint8)[1:].data_ptr(), R.RS_F32, None, 0, 1)
+    assert e.value.status == -3

@@ -22,6 +22,8 @@ element-granular. Quantisation tiles are granule-rows x b columns.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, List, Sequence, Tuple
 
@@ -137,6 +139,17 @@ def llama70b_layer() -> Workload:
                     description="one Llama-70B decoder layer, m=128, FP8 e4m3")
 
 
+def ragged_small() -> Workload:
+    """A small group for parity cases: element-, row- and block-granular
+    tensors, non-square and partial edge tiles, odd sizes, five ranks."""
+    ts = (TensorSpec("a", 40, 24, gran_rows=8, q_rows=8, q_cols=16),
+          TensorSpec("v", 1, 37, gran_rows=0),
+          TensorSpec("b", 30, 12, gran_rows=6, q_rows=6, q_cols=8),
+          TensorSpec("e", 50, 10, gran_rows=1, q_rows=1, q_cols=4),
+          TensorSpec("c", 7, 33, gran_rows=4, q_rows=4, q_cols=16))
+    return Workload("ragged_small", ts, m=5, qfmt="fp8_e4m3", block=8)
+
+
 WORKLOADS = {w.name: w for w in (toy_unit(), llama8b_layer(), ragged_mixed(),
                                   moe_experts(), llama70b_layer())}
 
@@ -168,35 +181,66 @@ class GroupInputs:
     nonfinite_positions: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
 
 
-def make_inputs(w: Workload, seed: int | None = None, grads: bool = True) -> GroupInputs:
-    """Draw params N(0, sigma_p) then grads (N(0, sigma_g) or Student-t(3)*sigma_g).
+PIECE = 1 << 22   # elements drawn from one generator
 
-    One PCG64 generator per workload; params tensor by tensor in group order,
-    then grads in the same order, then the non-finite injection positions.
+
+def _pieces(numel: int, ss: np.random.SeedSequence, kind: str, sigma: float, out: np.ndarray):
+    """Jobs filling out[numel]: piece j of PIECE elements comes from its own
+    PCG64 seeded by the j-th child of ss, so pieces can be drawn in parallel."""
+    n_pieces = max(1, -(-numel // PIECE))
+    kids = ss.spawn(n_pieces)
+
+    def one(j):
+        lo, hi = j * PIECE, min(numel, (j + 1) * PIECE)
+        rng = np.random.default_rng(kids[j])
+        if kind == "student_t3":
+            out[lo:hi] = (rng.standard_t(3, size=hi - lo) * sigma).astype(np.float32)
+        else:
+            v = rng.standard_normal(hi - lo, dtype=np.float32)
+            np.multiply(v, np.float32(sigma), out=out[lo:hi])
+
+    return [lambda j=j: one(j) for j in range(n_pieces)]
+
+
+def make_inputs(w: Workload, seed: int | None = None, grads: bool = True,
+                threads: int | None = None) -> GroupInputs:
+    """Seeded synthetic params and grads for a workload.
+
+    Root SeedSequence(seed); its first T children draw the params of each
+    tensor (N(0, param_sigma)), the next T the grads (N(0, grad_sigma), or
+    Student-t(3) * grad_sigma), and one more child picks the non-finite
+    positions: floor(frac * numel) distinct flat positions over the
+    concatenated tensors, set in turn to +Inf, -Inf, NaN.
     """
-    rng = np.random.default_rng(w.seed if seed is None else seed)
-    ps = [(rng.standard_normal(t.numel, dtype=np.float32) * np.float32(w.param_sigma))
-          .reshape(t.rows, t.cols) for t in w.tensors]
-    gs: List[np.ndarray] = []
+    root = np.random.SeedSequence(w.seed if seed is None else seed)
+    ss_p = root.spawn(len(w.tensors))
+    ss_g = root.spawn(len(w.tensors))
+    ss_i = root.spawn(1)[0]
+    nthr = threads or min(16, os.cpu_count() or 1)
+    ps = [np.empty(t.numel, np.float32) for t in w.tensors]
+    gs = [np.empty(t.numel, np.float32) for t in w.tensors] if grads else []
+    jobs = []
+    for t, ss, out in zip(w.tensors, ss_p, ps):
+        jobs += _pieces(t.numel, ss, "normal", w.param_sigma, out)
+    for t, ss, out in zip(w.tensors, ss_g, gs):
+        jobs += _pieces(t.numel, ss, w.grad_dist, w.grad_sigma, out)
+    with ThreadPoolExecutor(max_workers=nthr) as pool:
+        list(pool.map(lambda f: f(), jobs))
+    ps = [a.reshape(t.rows, t.cols) for a, t in zip(ps, w.tensors)]
+    gs = [a.reshape(t.rows, t.cols) for a, t in zip(gs, w.tensors)]
     pos = np.zeros(0, np.int64)
-    if grads:
-        for t in w.tensors:
-            if w.grad_dist == "student_t3":
-                g = (rng.standard_t(3, size=t.numel) * w.grad_sigma).astype(np.float32)
-            else:
-                g = rng.standard_normal(t.numel, dtype=np.float32) * np.float32(w.grad_sigma)
-            gs.append(g.reshape(t.rows, t.cols))
-        if w.nonfinite_frac > 0:
-            total = w.numel
-            k = int(w.nonfinite_frac * total)
-            pos = rng.choice(total, size=k, replace=False).astype(np.int64)
-            specials = np.array([np.inf, -np.inf, np.nan], dtype=np.float32)
-            starts = np.cumsum([0] + [t.numel for t in w.tensors])
-            tid = np.searchsorted(starts, pos, side="right") - 1
-            cyc = specials[np.arange(k) % 3]
-            for t in np.unique(tid):
-                sel = tid == t
-                gs[t].reshape(-1)[pos[sel] - starts[t]] = cyc[sel]
+    if grads and w.nonfinite_frac > 0:
+        total = w.numel
+        k = int(w.nonfinite_frac * total)
+        rng = np.random.default_rng(ss_i)
+        pos = rng.choice(total, size=k, replace=False).astype(np.int64)
+        specials = np.array([np.inf, -np.inf, np.nan], dtype=np.float32)
+        starts = np.cumsum([0] + [t.numel for t in w.tensors])
+        tid = np.searchsorted(starts, pos, side="right") - 1
+        cyc = specials[np.arange(k) % 3]
+        for t in np.unique(tid):
+            sel = tid == t
+            gs[t].reshape(-1)[pos[sel] - starts[t]] = cyc[sel]
     return GroupInputs(ps, gs, pos)
 
 
