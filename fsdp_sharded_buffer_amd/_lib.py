@@ -23,7 +23,7 @@ class rs_plan_info(ctypes.Structure):
 
 class rs_layout_info(ctypes.Structure):
     _fields_ = [("n", c_int32), ("m", c_int32), ("S", c_int64), ("total", c_int64),
-                ("num_chunks", c_int64), ("num_frags", c_int64), ("num_tiles", c_int64),
+                ("num_chunks", c_int64), ("num_coarse_chunks", c_int64), ("num_frags", c_int64), ("num_tiles", c_int64),
                 ("chunk_elems", c_int64), ("device_bytes", c_int64), ("workspace_bytes", c_int64)]
 
 

@@ -22,14 +22,18 @@ struct ChunkDesc {
 };
 static_assert(sizeof(ChunkDesc) == 32, "ChunkDesc layout");
 
-// A tensor-rank intersection; its chunks are [chunk_begin, chunk_end).
+// A tensor-rank intersection; its chunks are [chunk_begin, chunk_end) in
+// the fine chunk table and [cchunk_begin, cchunk_end) in the coarse one.
 struct FragDesc {
   int32_t tensor;
   int32_t rank;
   int32_t chunk_begin;
   int32_t chunk_end;
+  int32_t cchunk_begin;
+  int32_t cchunk_end;
+  int32_t pad0, pad1;
 };
-static_assert(sizeof(FragDesc) == 16, "FragDesc layout");
+static_assert(sizeof(FragDesc) == 32, "FragDesc layout");
 
 // Per tensor: its fragments (all ranks) are [frag_begin, frag_end) and the
 // ranks it touches are [rank_lo, rank_hi).
@@ -65,7 +69,14 @@ struct QuantWork {
 static_assert(sizeof(QuantWork) == 16, "QuantWork layout");
 
 constexpr int kMaxTileElems = 16384;  // 256 lanes x 64 elements held in registers
-constexpr int64_t kDefaultChunk = 16384;
+#ifndef RS_DEFAULT_CHUNK
+#define RS_DEFAULT_CHUNK 2048
+#endif
+#ifndef RS_COARSE_FACTOR
+#define RS_COARSE_FACTOR 32
+#endif
+constexpr int64_t kDefaultChunk = RS_DEFAULT_CHUNK;   // fine chunk
+constexpr int64_t kCoarseFactor = RS_COARSE_FACTOR;   // coarse chunk = factor x fine
 
 }  // namespace rs
 
@@ -78,15 +89,17 @@ struct rs_layout {
 
   std::vector<rs::TensorDesc> tensors;
   std::vector<rs::FragDesc> frags;
-  std::vector<rs::ChunkDesc> chunks;
+  std::vector<rs::ChunkDesc> chunks;   // fine chunks (copies, scale/add)
+  std::vector<rs::ChunkDesc> cchunks;  // coarse chunks (norms, masked zero)
   std::vector<rs::TileDesc> tiles;
   std::vector<rs::QuantWork> work;
 
   // per-rank begin indices, size m + 1
-  std::vector<int64_t> rank_chunk, rank_frag, rank_tile, rank_work;
+  std::vector<int64_t> rank_chunk, rank_cchunk, rank_frag, rank_tile, rank_work;
 
   // byte offsets of each table inside the device blob
-  size_t off_tensors = 0, off_frags = 0, off_chunks = 0, off_tiles = 0, off_work = 0;
+  size_t off_tensors = 0, off_frags = 0, off_chunks = 0, off_cchunks = 0, off_tiles = 0,
+         off_work = 0;
   size_t device_bytes = 0;
   size_t workspace_bytes = 0;
 

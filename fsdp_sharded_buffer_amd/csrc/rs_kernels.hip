@@ -63,34 +63,85 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 
 // ------------------------------------------------------- 8-element vectors
 
-// Element kinds: 0 = fp32, 1 = bf16.
+// Tuning knobs (compile-time).  RS_UNROLL: 8-element vectors in flight per
+// lane in the copy and scale/add loops.  The *_NT switches choose, per
+// operation, whether streaming loads and stores carry the nontemporal hint
+// (measured on MI355X: it helps the pure streams - copies, the norm read -
+// and hurts the read-modify-write of scale/add).
+#ifndef RS_UNROLL
+#define RS_UNROLL 2
+#endif
+#ifndef RS_PACK_NT
+#define RS_PACK_NT 1
+#endif
+#ifndef RS_SCALE_NT
+#define RS_SCALE_NT 0
+#endif
+#ifndef RS_SQNORM_NT
+#define RS_SQNORM_NT 1
+#endif
+#ifndef RS_ZERO_NT
+#define RS_ZERO_NT 0
+#endif
+#ifndef RS_QUANT_NT
+#define RS_QUANT_NT 1
+#endif
+#ifndef RS_FILL_BYTES
+#define RS_FILL_BYTES 262144
+#endif
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// one 128-bit global load / store (global_load_dwordx4 / global_store_dwordx4)
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  else
+    return *static_cast<const u32x4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
+  else
+    *static_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ float f32(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t u32(float f) { return __float_as_uint(f); }
+
+// Element kinds: 0 = fp32, 1 = bf16.  Eight elements as raw bits.
 template <int K> struct Pack8;
-template <> struct Pack8<0> { float4 a, b; };
-template <> struct Pack8<1> { uint4 a; };
+template <> struct Pack8<0> { u32x4 a, b; };
+template <> struct Pack8<1> { u32x4 a; };
 
 template <int K> constexpr int esize() { return K == 0 ? 4 : 2; }
 
-template <int K> __device__ __forceinline__ Pack8<K> ld8(const void* p, int64_t i);
-template <> __device__ __forceinline__ Pack8<0> ld8<0>(const void* p, int64_t i) {
-  const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-  return Pack8<0>{q[0], q[1]};
-}
-template <> __device__ __forceinline__ Pack8<1> ld8<1>(const void* p, int64_t i) {
-  return Pack8<1>{*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i)};
-}
-
-template <int K> __device__ __forceinline__ void st8(void* p, int64_t i, const Pack8<K>& v);
-template <> __device__ __forceinline__ void st8<0>(void* p, int64_t i, const Pack8<0>& v) {
-  float4* q = reinterpret_cast<float4*>(static_cast<float*>(p) + i);
-  q[0] = v.a;
-  q[1] = v.b;
-}
-template <> __device__ __forceinline__ void st8<1>(void* p, int64_t i, const Pack8<1>& v) {
-  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + i) = v.a;
+template <int K, bool NT>
+__device__ __forceinline__ Pack8<K> ld8(const void* p, int64_t i) {
+  if constexpr (K == 0) {
+    const float* q = static_cast<const float*>(p) + i;
+    return Pack8<0>{ld16<NT>(q), ld16<NT>(q + 4)};
+  } else {
+    return Pack8<1>{ld16<NT>(static_cast<const uint16_t*>(p) + i)};
+  }
 }
 
-__device__ __forceinline__ uint32_t pk2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+template <int K, bool NT>
+__device__ __forceinline__ void st8(void* p, int64_t i, const Pack8<K>& v) {
+  if constexpr (K == 0) {
+    float* q = static_cast<float*>(p) + i;
+    st16<NT>(q, v.a);
+    st16<NT>(q + 4, v.b);
+  } else {
+    st16<NT>(static_cast<uint16_t*>(p) + i, v.a);
+  }
+}
+
+__device__ __forceinline__ uint32_t pk2(uint32_t lo, uint32_t hi) {
+  return bf16_rne(f32(lo)) | (bf16_rne(f32(hi)) << 16);
 }
 
 template <int SK, int DK> struct Conv;
@@ -99,17 +150,27 @@ template <int K> struct Conv<K, K> {
 };
 template <> struct Conv<0, 1> {
   static __device__ __forceinline__ Pack8<1> run(const Pack8<0>& v) {
-    return Pack8<1>{make_uint4(pk2(v.a.x, v.a.y), pk2(v.a.z, v.a.w), pk2(v.b.x, v.b.y),
-                               pk2(v.b.z, v.b.w))};
+    u32x4 o;
+    o.x = pk2(v.a.x, v.a.y);
+    o.y = pk2(v.a.z, v.a.w);
+    o.z = pk2(v.b.x, v.b.y);
+    o.w = pk2(v.b.z, v.b.w);
+    return Pack8<1>{o};
   }
 };
 template <> struct Conv<1, 0> {
   static __device__ __forceinline__ Pack8<0> run(const Pack8<1>& v) {
-    const uint4 u = v.a;
-    return Pack8<0>{make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
-                                bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16)),
-                    make_float4(bf16_to_f32(u.z & 0xffffu), bf16_to_f32(u.z >> 16),
-                                bf16_to_f32(u.w & 0xffffu), bf16_to_f32(u.w >> 16))};
+    const u32x4 u = v.a;
+    u32x4 a, b;
+    a.x = u.x << 16;
+    a.y = u.x & 0xffff0000u;
+    a.z = u.y << 16;
+    a.w = u.y & 0xffff0000u;
+    b.x = u.z << 16;
+    b.y = u.z & 0xffff0000u;
+    b.z = u.w << 16;
+    b.w = u.w & 0xffff0000u;
+    return Pack8<0>{a, b};
   }
 };
 
@@ -118,7 +179,7 @@ template <int SK, int DK>
 __device__ __forceinline__ void copy1(const void* s, void* d, int64_t i) {
   if constexpr (SK == DK) {
     if constexpr (SK == 0)
-      static_cast<float*>(d)[i] = static_cast<const float*>(s)[i];
+      static_cast<uint32_t*>(d)[i] = static_cast<const uint32_t*>(s)[i];
     else
       static_cast<uint16_t*>(d)[i] = static_cast<const uint16_t*>(s)[i];
   } else if constexpr (SK == 0) {
@@ -132,33 +193,35 @@ __device__ __forceinline__ bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-constexpr int kUnroll = 4;
+constexpr int kUnroll = RS_UNROLL;
 
 // Convert-copy n elements; the workgroup's lanes stride over 8-element
-// vectors, kUnroll vectors in flight per lane.
-template <int SK, int DK>
+// vectors.  Each pass issues the loads of kUnroll vectors per lane (the
+// last pass predicated) before any of their stores.
+template <int SK, int DK, bool NT>
 __device__ __forceinline__ void copy_run(const void* src, void* dst, int n) {
   const int nv = (aligned16(src) && aligned16(dst)) ? n / 8 : 0;
-  int v = threadIdx.x;
-  for (; v + (kUnroll - 1) * kThreads < nv; v += kUnroll * kThreads) {
+  for (int b = threadIdx.x; b < nv; b += kUnroll * kThreads) {
     Pack8<SK> r[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) r[u] = ld8<SK>(src, int64_t(v + u * kThreads) * 8);
+    for (int u = 0; u < kUnroll; ++u)
+      if (b + u * kThreads < nv) r[u] = ld8<SK, NT>(src, int64_t(b + u * kThreads) * 8);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      st8<DK>(dst, int64_t(v + u * kThreads) * 8, Conv<SK, DK>::run(r[u]));
+      if (b + u * kThreads < nv)
+        st8<DK, NT>(dst, int64_t(b + u * kThreads) * 8, Conv<SK, DK>::run(r[u]));
   }
-  for (; v < nv; v += kThreads) st8<DK>(dst, int64_t(v) * 8, Conv<SK, DK>::run(ld8<SK>(src, int64_t(v) * 8)));
   for (int i = nv * 8 + threadIdx.x; i < n; i += kThreads) copy1<SK, DK>(src, dst, i);
 }
 
-template <int K>
-__device__ __forceinline__ void zero_run(void* dst, int n) {
-  const int nv = aligned16(dst) ? n * esize<K>() / 16 : 0;
-  uint4* d = static_cast<uint4*>(dst);
-  for (int v = threadIdx.x; v < nv; v += kThreads) d[v] = make_uint4(0, 0, 0, 0);
-  const int done = nv * 16 / esize<K>();
-  for (int i = done + threadIdx.x; i < n; i += kThreads) {
+template <int K, bool NT>
+__device__ __forceinline__ void zero_run(void* dst, int64_t n) {
+  const int64_t nv = aligned16(dst) ? n * esize<K>() / 16 : 0;
+  char* d = static_cast<char*>(dst);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t v = threadIdx.x; v < nv; v += kThreads) st16<NT>(d + v * 16, z);
+  const int64_t done = nv * 16 / esize<K>();
+  for (int64_t i = done + threadIdx.x; i < n; i += kThreads) {
     if constexpr (K == 0)
       static_cast<float*>(dst)[i] = 0.0f;
     else
@@ -167,32 +230,39 @@ __device__ __forceinline__ void zero_run(void* dst, int n) {
 }
 
 // ------------------------------------------------------------ pack/unpack
+//
+// Chunk kernels take the chunk range [c0, c0 + nc) and stride over it with
+// the grid, so the grid may be capped below nc (a persistent grid).
 
 template <int SK, int DK>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const ChunkDesc* __restrict__ chunks,
-                                                        int64_t c0,
+                                                        int64_t c0, int64_t nc,
                                                         const void* const* __restrict__ src,
                                                         void* __restrict__ buf) {
-  const ChunkDesc c = chunks[c0 + blockIdx.x];
-  char* d = static_cast<char*>(buf) + c.buf_off * esize<DK>();
-  if (c.tensor < 0) {
-    zero_run<DK>(d, c.len);
-    return;
+  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
+    const ChunkDesc c = chunks[c0 + i];
+    char* d = static_cast<char*>(buf) + c.buf_off * esize<DK>();
+    if (c.tensor < 0) {
+      zero_run<DK, RS_PACK_NT>(d, c.len);
+    } else {
+      const char* s = static_cast<const char*>(src[c.tensor]) + c.ten_off * esize<SK>();
+      copy_run<SK, DK, RS_PACK_NT>(s, d, c.len);
+    }
   }
-  const char* s = static_cast<const char*>(src[c.tensor]) + c.ten_off * esize<SK>();
-  copy_run<SK, DK>(s, d, c.len);
 }
 
 template <int SK, int DK>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const ChunkDesc* __restrict__ chunks,
-                                                          int64_t c0,
+                                                          int64_t c0, int64_t nc,
                                                           const void* __restrict__ buf,
                                                           void* const* __restrict__ dst) {
-  const ChunkDesc c = chunks[c0 + blockIdx.x];
-  if (c.tensor < 0) return;
-  const char* s = static_cast<const char*>(buf) + c.buf_off * esize<SK>();
-  char* d = static_cast<char*>(dst[c.tensor]) + c.ten_off * esize<DK>();
-  copy_run<SK, DK>(s, d, c.len);
+  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
+    const ChunkDesc c = chunks[c0 + i];
+    if (c.tensor < 0) continue;
+    const char* s = static_cast<const char*>(buf) + c.buf_off * esize<SK>();
+    char* d = static_cast<char*>(dst[c.tensor]) + c.ten_off * esize<DK>();
+    copy_run<SK, DK, RS_PACK_NT>(s, d, c.len);
+  }
 }
 
 // -------------------------------------------------------------- scale/add
@@ -204,8 +274,20 @@ __device__ __forceinline__ float axpby(float a, float y, float b, float x) {
   return u + w;
 }
 
-__device__ __forceinline__ bool finite(float v) {
-  return (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u;
+__device__ __forceinline__ bool finite_bits(uint32_t u) {
+  return (u & 0x7f800000u) != 0x7f800000u;
+}
+
+__device__ __forceinline__ bool finite(float v) { return finite_bits(__float_as_uint(v)); }
+
+__device__ __forceinline__ u32x4 axpby4(float a, u32x4 y, float b, u32x4 x, bool& bad) {
+  u32x4 o;
+  o.x = u32(axpby(a, f32(y.x), b, f32(x.x)));
+  o.y = u32(axpby(a, f32(y.y), b, f32(x.y)));
+  o.z = u32(axpby(a, f32(y.z), b, f32(x.z)));
+  o.w = u32(axpby(a, f32(y.w), b, f32(x.w)));
+  bad |= !(finite_bits(o.x) && finite_bits(o.y) && finite_bits(o.z) && finite_bits(o.w));
+  return o;
 }
 
 // Marks found_inf[rank] from lane 0 of every wave that saw a bad value.
@@ -214,60 +296,30 @@ __device__ __forceinline__ void flag_rank(bool bad, uint32_t* found_inf, int ran
 }
 
 template <int XK>
-__global__ __launch_bounds__(kThreads) void scale_add_kernel(
-    const ChunkDesc* __restrict__ chunks, int64_t c0, float* __restrict__ y,
-    const void* __restrict__ x, float alpha, float beta, const uint8_t* __restrict__ mask,
-    uint32_t* __restrict__ found_inf) {
-  const ChunkDesc c = chunks[c0 + blockIdx.x];
-  if (c.tensor < 0) return;
-  if (mask && !mask[c.tensor]) return;
-  float* yp = y + c.buf_off;
-  const char* xp = static_cast<const char*>(x) + c.buf_off * esize<XK>();
-  const int n = c.len;
-  bool bad = false;
+__device__ __forceinline__ void scale_add_run(float* yp, const char* xp, int n, float alpha,
+                                              float beta, bool& bad) {
+  constexpr bool NT = RS_SCALE_NT;
   const int nv = (aligned16(yp) && aligned16(xp)) ? n / 8 : 0;
-  int v = threadIdx.x;
-  for (; v + (kUnroll - 1) * kThreads < nv; v += kUnroll * kThreads) {
+  for (int b = threadIdx.x; b < nv; b += kUnroll * kThreads) {
     Pack8<0> ry[kUnroll];
     Pack8<0> rx[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = int64_t(v + u * kThreads) * 8;
-      ry[u] = ld8<0>(yp, i);
-      rx[u] = Conv<XK, 0>::run(ld8<XK>(xp, i));
+      const int64_t i = int64_t(b + u * kThreads) * 8;
+      if (b + u * kThreads < nv) {
+        ry[u] = ld8<0, NT>(yp, i);
+        rx[u] = Conv<XK, 0>::run(ld8<XK, NT>(xp, i));
+      }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      Pack8<0> o;
-      o.a.x = axpby(alpha, ry[u].a.x, beta, rx[u].a.x);
-      o.a.y = axpby(alpha, ry[u].a.y, beta, rx[u].a.y);
-      o.a.z = axpby(alpha, ry[u].a.z, beta, rx[u].a.z);
-      o.a.w = axpby(alpha, ry[u].a.w, beta, rx[u].a.w);
-      o.b.x = axpby(alpha, ry[u].b.x, beta, rx[u].b.x);
-      o.b.y = axpby(alpha, ry[u].b.y, beta, rx[u].b.y);
-      o.b.z = axpby(alpha, ry[u].b.z, beta, rx[u].b.z);
-      o.b.w = axpby(alpha, ry[u].b.w, beta, rx[u].b.w);
-      bad |= !(finite(o.a.x) && finite(o.a.y) && finite(o.a.z) && finite(o.a.w) &&
-               finite(o.b.x) && finite(o.b.y) && finite(o.b.z) && finite(o.b.w));
-      st8<0>(yp, int64_t(v + u * kThreads) * 8, o);
+      if (b + u * kThreads < nv) {
+        Pack8<0> o;
+        o.a = axpby4(alpha, ry[u].a, beta, rx[u].a, bad);
+        o.b = axpby4(alpha, ry[u].b, beta, rx[u].b, bad);
+        st8<0, NT>(yp, int64_t(b + u * kThreads) * 8, o);
+      }
     }
-  }
-  for (; v < nv; v += kThreads) {
-    const int64_t i = int64_t(v) * 8;
-    const Pack8<0> ry = ld8<0>(yp, i);
-    const Pack8<0> rx = Conv<XK, 0>::run(ld8<XK>(xp, i));
-    Pack8<0> o;
-    o.a.x = axpby(alpha, ry.a.x, beta, rx.a.x);
-    o.a.y = axpby(alpha, ry.a.y, beta, rx.a.y);
-    o.a.z = axpby(alpha, ry.a.z, beta, rx.a.z);
-    o.a.w = axpby(alpha, ry.a.w, beta, rx.a.w);
-    o.b.x = axpby(alpha, ry.b.x, beta, rx.b.x);
-    o.b.y = axpby(alpha, ry.b.y, beta, rx.b.y);
-    o.b.z = axpby(alpha, ry.b.z, beta, rx.b.z);
-    o.b.w = axpby(alpha, ry.b.w, beta, rx.b.w);
-    bad |= !(finite(o.a.x) && finite(o.a.y) && finite(o.a.z) && finite(o.a.w) &&
-             finite(o.b.x) && finite(o.b.y) && finite(o.b.z) && finite(o.b.w));
-    st8<0>(yp, i, o);
   }
   for (int i = nv * 8 + threadIdx.x; i < n; i += kThreads) {
     float xv;
@@ -279,18 +331,48 @@ __global__ __launch_bounds__(kThreads) void scale_add_kernel(
     bad |= !finite(o);
     yp[i] = o;
   }
-  flag_rank(bad, found_inf, c.rank);
+}
+
+template <int XK>
+__global__ __launch_bounds__(kThreads) void scale_add_kernel(
+    const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* __restrict__ y,
+    const void* __restrict__ x, float alpha, float beta, const uint8_t* __restrict__ mask,
+    uint32_t* __restrict__ found_inf) {
+  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
+    const ChunkDesc c = chunks[c0 + i];
+    if (c.tensor < 0) continue;
+    if (mask && !mask[c.tensor]) continue;
+    bool bad = false;
+    scale_add_run<XK>(y + c.buf_off, static_cast<const char*>(x) + c.buf_off * esize<XK>(), c.len,
+                      alpha, beta, bad);
+    flag_rank(bad, found_inf, c.rank);
+  }
 }
 
 // ------------------------------------------------------------------- zero
 
+// Masked zero over chunks (padding skipped).
 template <int K>
 __global__ __launch_bounds__(kThreads) void zero_kernel(const ChunkDesc* __restrict__ chunks,
-                                                        int64_t c0, void* __restrict__ y,
+                                                        int64_t c0, int64_t nc,
+                                                        void* __restrict__ y,
                                                         const uint8_t* __restrict__ mask) {
-  const ChunkDesc c = chunks[c0 + blockIdx.x];
-  if (mask && (c.tensor < 0 || !mask[c.tensor])) return;
-  zero_run<K>(static_cast<char*>(y) + c.buf_off * esize<K>(), c.len);
+  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
+    const ChunkDesc c = chunks[c0 + i];
+    if (mask && (c.tensor < 0 || !mask[c.tensor])) continue;
+    zero_run<K, RS_ZERO_NT>(static_cast<char*>(y) + c.buf_off * esize<K>(), c.len);
+  }
+}
+
+// Unmasked zero of a contiguous, 16-byte aligned byte range: RS_FILL_BYTES
+// per workgroup.
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(char* __restrict__ base,
+                                                             int64_t nbytes) {
+  const int64_t lo = int64_t(blockIdx.x) * RS_FILL_BYTES;
+  const int64_t n16 = (nbytes - lo < RS_FILL_BYTES ? nbytes - lo : RS_FILL_BYTES) / 16;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  char* d = base + lo;
+  for (int64_t v = threadIdx.x; v < n16; v += kThreads) st16<RS_ZERO_NT>(d + v * 16, z);
 }
 
 // ----------------------------------------------------------------- sqnorm
@@ -312,59 +394,56 @@ __device__ __forceinline__ double block_sum(double v, double* lds) {
   return s;
 }
 
-__device__ __forceinline__ double sq(float v) {
-  const double d = double(v);
+__device__ __forceinline__ double sq(uint32_t u) {
+  const double d = double(f32(u));
   return d * d;
 }
 
-// Per chunk: fp64 sum of squares into part[chunk].
+__device__ __forceinline__ void sq4(u32x4 r, double& acc, bool& bad) {
+  acc += sq(r.x);
+  acc += sq(r.y);
+  acc += sq(r.z);
+  acc += sq(r.w);
+  bad |= !(finite_bits(r.x) && finite_bits(r.y) && finite_bits(r.z) && finite_bits(r.w));
+}
+
+// Per (coarse) chunk: fp64 sum of squares into part[chunk].
 __global__ __launch_bounds__(kThreads) void sqnorm_partial_kernel(
-    const ChunkDesc* __restrict__ chunks, int64_t c0, const float* __restrict__ x,
+    const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, const float* __restrict__ x,
     double* __restrict__ part, uint32_t* __restrict__ found_inf) {
   __shared__ double lds[kThreads / kWave];
-  const int64_t ci = c0 + blockIdx.x;
-  const ChunkDesc c = chunks[ci];
-  if (c.tensor < 0) return;
-  const float* xp = x + c.buf_off;
-  const int n = c.len;
-  double acc = 0.0;
-  bool bad = false;
-  const int nv = aligned16(xp) ? n / 4 : 0;
-  const float4* x4 = reinterpret_cast<const float4*>(xp);
-  int v = threadIdx.x;
-  constexpr int U = 8;
-  for (; v + (U - 1) * kThreads < nv; v += U * kThreads) {
-    float4 r[U];
+  for (int64_t ii = blockIdx.x; ii < nc; ii += gridDim.x) {
+    const int64_t ci = c0 + ii;
+    const ChunkDesc c = chunks[ci];
+    if (c.tensor < 0) continue;
+    const float* xp = x + c.buf_off;
+    const int n = c.len;
+    double acc = 0.0;
+    bool bad = false;
+    const int nv = aligned16(xp) ? n / 4 : 0;
+    int v = threadIdx.x;
+    constexpr int U = 2 * kUnroll;
+    for (; v + (U - 1) * kThreads < nv; v += U * kThreads) {
+      u32x4 r[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) r[u] = x4[v + u * kThreads];
+      for (int u = 0; u < U; ++u) r[u] = ld16<RS_SQNORM_NT>(xp + int64_t(v + u * kThreads) * 4);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      acc += sq(r[u].x);
-      acc += sq(r[u].y);
-      acc += sq(r[u].z);
-      acc += sq(r[u].w);
-      bad |= !(finite(r[u].x) && finite(r[u].y) && finite(r[u].z) && finite(r[u].w));
+      for (int u = 0; u < U; ++u) sq4(r[u], acc, bad);
     }
+    for (; v < nv; v += kThreads) sq4(ld16<RS_SQNORM_NT>(xp + int64_t(v) * 4), acc, bad);
+    for (int i = nv * 4 + threadIdx.x; i < n; i += kThreads) {
+      const uint32_t u = __float_as_uint(xp[i]);
+      acc += sq(u);
+      bad |= !finite_bits(u);
+    }
+    flag_rank(bad, found_inf, c.rank);
+    const double s = block_sum(acc, lds);
+    if (threadIdx.x == 0) part[ci] = s;
   }
-  for (; v < nv; v += kThreads) {
-    const float4 r = x4[v];
-    acc += sq(r.x);
-    acc += sq(r.y);
-    acc += sq(r.z);
-    acc += sq(r.w);
-    bad |= !(finite(r.x) && finite(r.y) && finite(r.z) && finite(r.w));
-  }
-  for (int i = nv * 4 + threadIdx.x; i < n; i += kThreads) {
-    acc += sq(xp[i]);
-    bad |= !finite(xp[i]);
-  }
-  flag_rank(bad, found_inf, c.rank);
-  const double s = block_sum(acc, lds);
-  if (threadIdx.x == 0) part[ci] = s;
 }
 
 // Per tensor: fragment sums in rank order, each the fixed-order sum of its
-// chunk partials; writes partial[k*n + t] for every k of the range.
+// coarse-chunk partials; writes partial[k*n + t] for every k of the range.
 __global__ __launch_bounds__(kThreads) void sqnorm_combine_kernel(
     const TensorDesc* __restrict__ tensors, const FragDesc* __restrict__ frags,
     const double* __restrict__ part, int32_t n, int32_t k0, int32_t k1, double* __restrict__ sq_out,
@@ -378,9 +457,17 @@ __global__ __launch_bounds__(kThreads) void sqnorm_combine_kernel(
     double s = 0.0;
     if (has) {  // uniform across the workgroup
       const FragDesc fd = frags[td.frag_begin + (k - td.rank_lo)];
-      double a = 0.0;
-      for (int i = fd.chunk_begin + threadIdx.x; i < fd.chunk_end; i += kThreads) a += part[i];
-      s = block_sum(a, lds);
+      // lanes stride over the partials; four loads in flight per lane
+      double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+      int i = fd.cchunk_begin + threadIdx.x;
+      for (; i + 3 * kThreads < fd.cchunk_end; i += 4 * kThreads) {
+        a0 += part[i];
+        a1 += part[i + kThreads];
+        a2 += part[i + 2 * kThreads];
+        a3 += part[i + 3 * kThreads];
+      }
+      for (; i < fd.cchunk_end; i += kThreads) a0 += part[i];
+      s = block_sum((a0 + a1) + (a2 + a3), lds);
       if (threadIdx.x == 0) total += s;
     }
     if (partial && threadIdx.x == 0) partial[int64_t(k) * n + t] = s;
@@ -389,11 +476,81 @@ __global__ __launch_bounds__(kThreads) void sqnorm_combine_kernel(
 }
 
 // ------------------------------------------------------------------ quant
+//
+// Codes are encode(fl(x / scale)) with IEEE division.  Dividing every
+// element makes the kernel ALU bound on gfx950 (the correctly rounded fp32
+// division is a ~10-instruction sequence), so each element first takes
+// q' = fl(x * fl(1/scale)), which is within 3 ulp of fl(x / scale) when the
+// scale is a normal number.  The code can only differ when a rounding
+// midpoint of the code grid lies within that distance; exactly those
+// elements (window of 8 ulp), and every element of a tile whose scale is
+// zero, subnormal, infinite or NaN, are encoded from the true quotient.
+
+// FP8 E4M3: q' is safe when |q'| >= 2^-6 (plus margin; below that the
+// E4M3 subnormal grid applies) and its 20 dropped mantissa bits are more
+// than 8 ulp from the half-way pattern 0x80000.
+__device__ __forceinline__ bool e4m3_safe(uint32_t u) {
+  const uint32_t a = u & 0x7fffffffu;
+  return a >= 0x3c800010u && ((a & 0xfffffu) - 0x7fff8u) > 16u;
+}
+
+// Encoder for |q| >= 2^-6 and finite (the safe case above): clamp to 448,
+// round the mantissa to 3 bits to nearest even, rebias 127 -> 7.
+__device__ __forceinline__ uint32_t e4m3_encode_normal(uint32_t u) {
+  uint32_t a = min(u & 0x7fffffffu, 0x43e00000u);
+  a += 0x7ffffu + ((a >> 20) & 1u);
+  return ((a >> 20) - (120u << 3)) | ((u >> 24) & 0x80u);
+}
+
+// INT8: q' is safe when more than |q'| * 2^-20 (>= 8 ulp) from a half-integer.
+__device__ __forceinline__ bool int8_safe(float q) {
+  const float a = fabsf(q);
+  const float f = a - floorf(a);
+  return fabsf(f - 0.5f) > a * 0x1p-20f;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t encode(float q) {
+  return FMT == RS_Q_FP8_E4M3 ? e4m3_encode(q) : int8_encode(q);
+}
+
+// Exact code of one element, any tile.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_exact(float x, float scale, bool zero_tile,
+                                                 bool nan_tile) {
+  if (zero_tile) return 0u;
+  if (nan_tile) return FMT == RS_Q_FP8_E4M3 ? 0x7fu : 0u;
+  return encode<FMT>(x / scale);
+}
+
+// Walks the float4 slots f = lane, lane + team, ... of a tile with
+// cols/4 slots per row, as element offsets from the tile's first element.
+struct SlotWalk {
+  int r, c, dq, dr, c4;
+  int64_t ld;
+  __device__ __forceinline__ SlotWalk(int lane, int team, int c4_, int64_t ld_) {
+    c4 = c4_;
+    ld = ld_;
+    r = lane / c4;
+    c = lane - r * c4;
+    dq = team / c4;
+    dr = team - dq * c4;
+  }
+  __device__ __forceinline__ int64_t off() const { return int64_t(r) * ld + c * 4; }
+  __device__ __forceinline__ void next() {
+    r += dq;
+    c += dr;
+    if (c >= c4) {
+      c -= c4;
+      ++r;
+    }
+  }
+};
 
 // Each workgroup takes `count` consecutive tiles; tile j of the item is
-// handled by lanes [j*team, (j+1)*team).  A lane keeps its (at most 64)
-// elements in registers between the absmax and the encode pass, so x is
-// read once.
+// handled by lanes [j*team, (j+1)*team).  On the 16-byte path a lane keeps
+// its (at most 64) elements in registers between the absmax and the encode
+// pass, so x is read once; the other path reads x twice.
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __restrict__ work,
                                                          int64_t w0,
@@ -410,43 +567,31 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
   const int lane = threadIdx.x % team;
   const bool active = slot < w.count;
   const TileDesc td = tiles[w.tile_begin + (active ? slot : 0)];
+  const float* base = x + td.buf_off;
+  uint8_t* cbase = codes + td.buf_off;
   float v[64];
   uint32_t amax = 0;
-  const float* base = x + td.buf_off;
+  const int c4 = td.cols >> 2;
+  const int nf = active ? td.rows * c4 : 0;
+  const int ne = active ? td.rows * td.cols : 0;
   if (vec) {
-    const int c4 = td.cols >> 2;
-    const int nf = active ? td.rows * c4 : 0;
+    SlotWalk sw(lane, team, c4, td.ld);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int f = lane + i * team;
-      float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (f < nf) {
-        const int r = f / c4;
-        const int cc = f - r * c4;
-        q = *reinterpret_cast<const float4*>(base + int64_t(r) * td.ld + cc * 4);
-      }
-      v[4 * i + 0] = q.x;
-      v[4 * i + 1] = q.y;
-      v[4 * i + 2] = q.z;
-      v[4 * i + 3] = q.w;
-      amax = max(amax, __float_as_uint(q.x) & 0x7fffffffu);
-      amax = max(amax, __float_as_uint(q.y) & 0x7fffffffu);
-      amax = max(amax, __float_as_uint(q.z) & 0x7fffffffu);
-      amax = max(amax, __float_as_uint(q.w) & 0x7fffffffu);
+      u32x4 q = {0u, 0u, 0u, 0u};
+      if (lane + i * team < nf) q = ld16<RS_QUANT_NT>(base + sw.off());
+      sw.next();
+      v[4 * i + 0] = f32(q.x);
+      v[4 * i + 1] = f32(q.y);
+      v[4 * i + 2] = f32(q.z);
+      v[4 * i + 3] = f32(q.w);
+      amax = max(amax, max(max(q.x & 0x7fffffffu, q.y & 0x7fffffffu),
+                           max(q.z & 0x7fffffffu, q.w & 0x7fffffffu)));
     }
   } else {
-    const int ne = active ? td.rows * td.cols : 0;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const int e = lane + i * team;
-      float q = 0.f;
-      if (e < ne) {
-        const int r = e / td.cols;
-        const int cc = e - r * td.cols;
-        q = base[int64_t(r) * td.ld + cc];
-      }
-      v[i] = q;
-      amax = max(amax, __float_as_uint(q) & 0x7fffffffu);
+    for (int e = lane; e < ne; e += team) {
+      const int r = e / td.cols;
+      amax = max(amax, __float_as_uint(base[int64_t(r) * td.ld + (e - r * td.cols)]) & 0x7fffffffu);
     }
   }
   // absmax of the tile as the max of |x| bit patterns: NaN patterns sort
@@ -469,37 +614,63 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
   if (nan_tile) scale = __uint_as_float(0x7fc00000u);
   if (lane == 0) scales[td.scale_idx] = scale;
   const bool zero_tile = scale == 0.0f;
-  uint8_t* cbase = codes + td.buf_off;
-  auto enc = [&](float val) -> uint32_t {
-    if (zero_tile) return 0u;
-    if (nan_tile) return FMT == RS_Q_FP8_E4M3 ? 0x7fu : 0u;
-    const float q = val / scale;
-    return FMT == RS_Q_FP8_E4M3 ? e4m3_encode(q) : int8_encode(q);
-  };
-  if (vec) {
-    const int c4 = td.cols >> 2;
-    const int nf = td.rows * c4;
+  const float rcp = 1.0f / scale;
+  // the reciprocal path needs a normal, finite scale (and so a finite rcp)
+  const uint32_t sb = __float_as_uint(scale);
+  const bool fast = sb >= 0x00800000u && sb < 0x7f800000u;
+  if (!vec) {
+    for (int e = lane; e < ne; e += team) {
+      const int r = e / td.cols;
+      const int64_t o = int64_t(r) * td.ld + (e - r * td.cols);
+      cbase[o] = uint8_t(encode_exact<FMT>(base[o], scale, zero_tile, nan_tile));
+    }
+    return;
+  }
+  uint32_t slow = 0;  // bit i: slot i needs the exact path
+  {
+    SlotWalk sw(lane, team, c4, td.ld);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int f = lane + i * team;
-      if (f < nf) {
-        const int r = f / c4;
-        const int cc = f - r * c4;
-        const uint32_t word = enc(v[4 * i]) | (enc(v[4 * i + 1]) << 8) |
-                              (enc(v[4 * i + 2]) << 16) | (enc(v[4 * i + 3]) << 24);
-        *reinterpret_cast<uint32_t*>(cbase + int64_t(r) * td.ld + cc * 4) = word;
-      }
-    }
-  } else {
-    const int ne = td.rows * td.cols;
+      if (lane + i * team < nf) {
+        float q[4];
+        bool safe = fast;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const int e = lane + i * team;
-      if (e < ne) {
-        const int r = e / td.cols;
-        const int cc = e - r * td.cols;
-        cbase[int64_t(r) * td.ld + cc] = uint8_t(enc(v[i]));
+        for (int j = 0; j < 4; ++j) {
+          q[j] = v[4 * i + j] * rcp;
+          if constexpr (FMT == RS_Q_FP8_E4M3)
+            safe = safe && e4m3_safe(u32(q[j]));
+          else
+            safe = safe && int8_safe(q[j]);
+        }
+        if (safe) {
+          uint32_t word;
+          if constexpr (FMT == RS_Q_FP8_E4M3)
+            word = e4m3_encode_normal(u32(q[0])) | (e4m3_encode_normal(u32(q[1])) << 8) |
+                   (e4m3_encode_normal(u32(q[2])) << 16) | (e4m3_encode_normal(u32(q[3])) << 24);
+          else
+            word = int8_encode(q[0]) | (int8_encode(q[1]) << 8) | (int8_encode(q[2]) << 16) |
+                   (int8_encode(q[3]) << 24);
+          *reinterpret_cast<uint32_t*>(cbase + sw.off()) = word;
+        } else {
+          slow |= 1u << i;
+        }
       }
+      sw.next();
+    }
+  }
+  if (slow) {  // rare: re-read the slot (cache resident) and divide
+    SlotWalk sw(lane, team, c4, td.ld);
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+      if (slow & (1u << i)) {
+        const u32x4 q = ld16<false>(base + sw.off());
+        const uint32_t word = encode_exact<FMT>(f32(q.x), scale, zero_tile, nan_tile) |
+                              (encode_exact<FMT>(f32(q.y), scale, zero_tile, nan_tile) << 8) |
+                              (encode_exact<FMT>(f32(q.z), scale, zero_tile, nan_tile) << 16) |
+                              (encode_exact<FMT>(f32(q.w), scale, zero_tile, nan_tile) << 24);
+        *reinterpret_cast<uint32_t*>(cbase + sw.off()) = word;
+      }
+      sw.next();
     }
   }
 }
@@ -525,6 +696,16 @@ rs_status check_ptr(const void* p, size_t align, const char* fn, const char* wha
   if (reinterpret_cast<uintptr_t>(p) % align)
     return fail(RS_ERR_ALIGN, std::string(fn) + ": " + what + " not aligned to its element size");
   return RS_OK;
+}
+
+#ifndef RS_GRID_CAP
+#define RS_GRID_CAP 0
+#endif
+
+// Workgroups for nc chunks: one per chunk, or at most RS_GRID_CAP.
+dim3 chunk_grid(int64_t nc) {
+  const int64_t g = (RS_GRID_CAP > 0 && nc > RS_GRID_CAP) ? RS_GRID_CAP : nc;
+  return dim3(static_cast<unsigned>(g));
 }
 
 rs_status after_launch(const char* fn) {
@@ -559,15 +740,15 @@ extern "C" rs_status rs_pack(const rs_layout* L, const void* const* src, rs_dtyp
   if (nc == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
-  const dim3 g(static_cast<unsigned>(nc)), b(kThreads);
+  const dim3 g = chunk_grid(nc), b(kThreads);
   if (src_dt == RS_F32 && buf_dt == RS_BF16)
-    hipLaunchKernelGGL((pack_kernel<0, 1>), g, b, 0, s, ch, c0, src, buf);
+    hipLaunchKernelGGL((pack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, src, buf);
   else if (src_dt == RS_F32 && buf_dt == RS_F32)
-    hipLaunchKernelGGL((pack_kernel<0, 0>), g, b, 0, s, ch, c0, src, buf);
+    hipLaunchKernelGGL((pack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, src, buf);
   else if (src_dt == RS_BF16 && buf_dt == RS_BF16)
-    hipLaunchKernelGGL((pack_kernel<1, 1>), g, b, 0, s, ch, c0, src, buf);
+    hipLaunchKernelGGL((pack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, src, buf);
   else
-    hipLaunchKernelGGL((pack_kernel<1, 0>), g, b, 0, s, ch, c0, src, buf);
+    hipLaunchKernelGGL((pack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, src, buf);
   return after_launch(fn);
 }
 
@@ -584,15 +765,15 @@ extern "C" rs_status rs_unpack(const rs_layout* L, const void* buf, rs_dtype buf
   if (nc == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
-  const dim3 g(static_cast<unsigned>(nc)), b(kThreads);
+  const dim3 g = chunk_grid(nc), b(kThreads);
   if (buf_dt == RS_BF16 && dst_dt == RS_BF16)
-    hipLaunchKernelGGL((unpack_kernel<1, 1>), g, b, 0, s, ch, c0, buf, dst);
+    hipLaunchKernelGGL((unpack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, buf, dst);
   else if (buf_dt == RS_BF16 && dst_dt == RS_F32)
-    hipLaunchKernelGGL((unpack_kernel<1, 0>), g, b, 0, s, ch, c0, buf, dst);
+    hipLaunchKernelGGL((unpack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, buf, dst);
   else if (buf_dt == RS_F32 && dst_dt == RS_F32)
-    hipLaunchKernelGGL((unpack_kernel<0, 0>), g, b, 0, s, ch, c0, buf, dst);
+    hipLaunchKernelGGL((unpack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, buf, dst);
   else
-    hipLaunchKernelGGL((unpack_kernel<0, 1>), g, b, 0, s, ch, c0, buf, dst);
+    hipLaunchKernelGGL((unpack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, buf, dst);
   return after_launch(fn);
 }
 
@@ -610,12 +791,12 @@ extern "C" rs_status rs_group_scale_add(const rs_layout* L, float* y, const void
   if (nc == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
-  const dim3 g(static_cast<unsigned>(nc)), b(kThreads);
+  const dim3 g = chunk_grid(nc), b(kThreads);
   if (x_dt == RS_F32)
-    hipLaunchKernelGGL((scale_add_kernel<0>), g, b, 0, s, ch, c0, y, x, alpha, beta, tensor_mask,
+    hipLaunchKernelGGL((scale_add_kernel<0>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
                        found_inf);
   else
-    hipLaunchKernelGGL((scale_add_kernel<1>), g, b, 0, s, ch, c0, y, x, alpha, beta, tensor_mask,
+    hipLaunchKernelGGL((scale_add_kernel<1>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
                        found_inf);
   return after_launch(fn);
 }
@@ -627,15 +808,25 @@ extern "C" rs_status rs_group_zero(const rs_layout* L, void* y, rs_dtype dt,
   RS_TRY(check_common(L, k0, k1, fn));
   if (!float_kind(dt)) return fail(RS_ERR_DTYPE, "rs_group_zero: dt must be RS_F32 or RS_BF16");
   RS_TRY(check_ptr(y, dt == RS_F32 ? 4 : 2, fn, "y"));
-  const int64_t c0 = L->rank_chunk[k0], nc = L->rank_chunk[k1] - c0;
-  if (nc == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
-  const dim3 g(static_cast<unsigned>(nc)), b(kThreads);
+  const int64_t es = dt == RS_F32 ? 4 : 2;
+  char* lo = static_cast<char*>(y) + int64_t(k0) * L->S * es;
+  const int64_t nbytes = int64_t(k1 - k0) * L->S * es;
+  if (!tensor_mask && reinterpret_cast<uintptr_t>(lo) % 16 == 0 && nbytes % 16 == 0) {
+    // the whole rank range, padding included: one contiguous fill
+    const int64_t g = (nbytes + RS_FILL_BYTES - 1) / RS_FILL_BYTES;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s, lo,
+                       nbytes);
+    return after_launch(fn);
+  }
+  const int64_t c0 = L->rank_cchunk[k0], nc = L->rank_cchunk[k1] - c0;
+  if (nc == 0) return RS_OK;
+  const ChunkDesc* ch = table<ChunkDesc>(L, L->off_cchunks);
+  const dim3 g = chunk_grid(nc), b(kThreads);
   if (dt == RS_F32)
-    hipLaunchKernelGGL((zero_kernel<0>), g, b, 0, s, ch, c0, y, tensor_mask);
+    hipLaunchKernelGGL((zero_kernel<0>), g, b, 0, s, ch, c0, nc, y, tensor_mask);
   else
-    hipLaunchKernelGGL((zero_kernel<1>), g, b, 0, s, ch, c0, y, tensor_mask);
+    hipLaunchKernelGGL((zero_kernel<1>), g, b, 0, s, ch, c0, nc, y, tensor_mask);
   return after_launch(fn);
 }
 
@@ -650,11 +841,11 @@ extern "C" rs_status rs_ragged_sqnorm(const rs_layout* L, const float* x, double
   if (partial) RS_TRY(check_ptr(partial, 8, fn, "partial"));
   if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t c0 = L->rank_chunk[k0], nc = L->rank_chunk[k1] - c0;
+  const int64_t c0 = L->rank_cchunk[k0], nc = L->rank_cchunk[k1] - c0;
   double* part = static_cast<double*>(ws);
   if (nc > 0)
-    hipLaunchKernelGGL(sqnorm_partial_kernel, dim3(unsigned(nc)), dim3(kThreads), 0, s,
-                       table<ChunkDesc>(L, L->off_chunks), c0, x, part, found_inf);
+    hipLaunchKernelGGL(sqnorm_partial_kernel, chunk_grid(nc), dim3(kThreads), 0, s,
+                       table<ChunkDesc>(L, L->off_cchunks), c0, nc, x, part, found_inf);
   hipLaunchKernelGGL(sqnorm_combine_kernel, dim3(unsigned(L->n)), dim3(kThreads), 0, s,
                      table<TensorDesc>(L, L->off_tensors), table<FragDesc>(L, L->off_frags), part,
                      L->n, k0, k1, sq_out, partial);

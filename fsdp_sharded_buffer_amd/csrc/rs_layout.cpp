@@ -26,21 +26,18 @@ int team_for(int64_t elems) {
   return team;
 }
 
-rs_status build(rs_layout* L) {
+// Splits the buffer into chunks of at most CH positions that never cross a
+// rank, tensor or padding boundary, in buffer order.  Records each rank's
+// first chunk in rank_begin and, when set_frags, creates the fragments;
+// otherwise fills the fragments' coarse chunk ranges.
+void build_chunks(rs_layout* L, int64_t CH, std::vector<ChunkDesc>& out,
+                  std::vector<int64_t>& rank_begin, bool set_frags) {
   const int32_t n = L->n, m = L->m;
-  const int64_t S = L->S, CH = L->chunk_elems;
-  L->tensors.assign(n, TensorDesc{});
-  L->frags.clear();
-  L->chunks.clear();
-  L->tiles.clear();
-  L->work.clear();
-  L->rank_chunk.assign(m + 1, 0);
-  L->rank_frag.assign(m + 1, 0);
-  L->rank_tile.assign(m + 1, 0);
-  L->rank_work.assign(m + 1, 0);
-
-  auto add_chunks = [&](int64_t lo, int64_t hi, int32_t tensor, int64_t ten_lo, int32_t rank,
-                        int32_t frag) {
+  const int64_t S = L->S;
+  out.clear();
+  rank_begin.assign(m + 1, 0);
+  auto add = [&](int64_t lo, int64_t hi, int32_t tensor, int64_t ten_lo, int32_t rank,
+                 int32_t frag) {
     for (int64_t p = lo; p < hi; p += CH) {
       ChunkDesc c;
       c.buf_off = p;
@@ -49,19 +46,17 @@ rs_status build(rs_layout* L) {
       c.tensor = tensor;
       c.rank = rank;
       c.frag = frag;
-      L->chunks.push_back(c);
+      out.push_back(c);
     }
   };
-
-  // Walk ranks in buffer order; inside a rank, tensors in order (offsets are
-  // increasing), padding chunks in the gaps.
-  int32_t t_first = 0;
+  int32_t t_first = 0, f = 0;
   for (int32_t k = 0; k < m; ++k) {
     const int64_t rlo = int64_t(k) * S, rhi = rlo + S;
-    L->rank_chunk[k] = int64_t(L->chunks.size());
-    L->rank_frag[k] = int64_t(L->frags.size());
+    rank_begin[k] = int64_t(out.size());
+    if (set_frags) L->rank_frag[k] = int64_t(L->frags.size());
     int64_t pos = rlo;
-    while (t_first < n && L->offsets[t_first] + L->specs[t_first].rows * L->specs[t_first].cols <= rlo)
+    while (t_first < n &&
+           L->offsets[t_first] + L->specs[t_first].rows * L->specs[t_first].cols <= rlo)
       ++t_first;
     for (int32_t t = t_first; t < n; ++t) {
       const int64_t l = L->offsets[t];
@@ -69,21 +64,42 @@ rs_status build(rs_layout* L) {
       if (l >= rhi) break;
       const int64_t lo = std::max(l, rlo), hi = std::min(r, rhi);
       if (lo >= hi) continue;
-      if (lo > pos) add_chunks(pos, lo, -1, -1, k, -1);
-      const int32_t f = int32_t(L->frags.size());
-      FragDesc fd;
-      fd.tensor = t;
-      fd.rank = k;
-      fd.chunk_begin = int32_t(L->chunks.size());
-      add_chunks(lo, hi, t, lo - l, k, f);
-      fd.chunk_end = int32_t(L->chunks.size());
-      L->frags.push_back(fd);
+      if (lo > pos) add(pos, lo, -1, -1, k, -1);
+      if (set_frags) {
+        FragDesc fd{};
+        fd.tensor = t;
+        fd.rank = k;
+        fd.chunk_begin = int32_t(out.size());
+        add(lo, hi, t, lo - l, k, f);
+        fd.chunk_end = int32_t(out.size());
+        L->frags.push_back(fd);
+      } else {
+        L->frags[f].cchunk_begin = int32_t(out.size());
+        add(lo, hi, t, lo - l, k, f);
+        L->frags[f].cchunk_end = int32_t(out.size());
+      }
+      ++f;
       pos = hi;
     }
-    if (pos < rhi) add_chunks(pos, rhi, -1, -1, k, -1);
+    if (pos < rhi) add(pos, rhi, -1, -1, k, -1);
   }
-  L->rank_chunk[m] = int64_t(L->chunks.size());
-  L->rank_frag[m] = int64_t(L->frags.size());
+  rank_begin[m] = int64_t(out.size());
+  if (set_frags) L->rank_frag[m] = int64_t(L->frags.size());
+}
+
+rs_status build(rs_layout* L) {
+  const int32_t n = L->n, m = L->m;
+  const int64_t S = L->S;
+  L->tensors.assign(n, TensorDesc{});
+  L->frags.clear();
+  L->tiles.clear();
+  L->work.clear();
+  L->rank_frag.assign(m + 1, 0);
+  L->rank_tile.assign(m + 1, 0);
+  L->rank_work.assign(m + 1, 0);
+
+  build_chunks(L, L->chunk_elems, L->chunks, L->rank_chunk, true);
+  build_chunks(L, L->chunk_elems * kCoarseFactor, L->cchunks, L->rank_cchunk, false);
   if (L->chunks.size() > size_t(INT32_MAX) || L->frags.size() > size_t(INT32_MAX))
     return fail(RS_ERR_INVALID_ARG, "rs_layout_create: too many chunks; raise chunk_elems");
 
@@ -159,14 +175,15 @@ rs_status build(rs_layout* L) {
   off = align256(off + sizeof(FragDesc) * L->frags.size());
   L->off_chunks = off;
   off = align256(off + sizeof(ChunkDesc) * L->chunks.size());
+  L->off_cchunks = off;
+  off = align256(off + sizeof(ChunkDesc) * L->cchunks.size());
   L->off_tiles = off;
   off = align256(off + sizeof(TileDesc) * L->tiles.size());
   L->off_work = off;
   off = align256(off + sizeof(QuantWork) * L->work.size());
   L->device_bytes = std::max<size_t>(off, 256);
-  // sqnorm scratch: one fp64 partial per chunk plus one per fragment
-  L->workspace_bytes = align256(sizeof(double) * L->chunks.size()) +
-                       align256(sizeof(double) * L->frags.size());
+  // sqnorm scratch: one fp64 partial per coarse chunk
+  L->workspace_bytes = align256(sizeof(double) * std::max<size_t>(L->cchunks.size(), 1));
   return RS_OK;
 }
 
@@ -178,7 +195,7 @@ extern "C" rs_status rs_layout_create(const rs_tensor_spec* specs, int32_t n, in
   if (!specs || !offsets || !out || n <= 0 || m <= 0 || S <= 0)
     return fail(RS_ERR_INVALID_ARG, "rs_layout_create: null pointer or non-positive n/m/S");
   if (chunk_elems == 0) chunk_elems = kDefaultChunk;
-  if (chunk_elems < 64 || chunk_elems % 64 || chunk_elems > (int64_t(1) << 30))
+  if (chunk_elems < 64 || chunk_elems % 64 || chunk_elems > (int64_t(1) << 22))
     return fail(RS_ERR_INVALID_ARG, "rs_layout_create: chunk_elems must be a multiple of 64");
   int64_t prev_end = 0;
   for (int32_t t = 0; t < n; ++t) {
@@ -225,6 +242,7 @@ extern "C" rs_status rs_layout_get_info(const rs_layout* L, rs_layout_info* info
   info->S = L->S;
   info->total = L->S * L->m;
   info->num_chunks = int64_t(L->chunks.size());
+  info->num_coarse_chunks = int64_t(L->cchunks.size());
   info->num_frags = int64_t(L->frags.size());
   info->num_tiles = int64_t(L->tiles.size());
   info->chunk_elems = L->chunk_elems;
@@ -244,6 +262,7 @@ extern "C" rs_status rs_layout_upload(rs_layout* L, void* dev_table, void* strea
   put(L->off_tensors, L->tensors.data(), sizeof(TensorDesc) * L->tensors.size());
   put(L->off_frags, L->frags.data(), sizeof(FragDesc) * L->frags.size());
   put(L->off_chunks, L->chunks.data(), sizeof(ChunkDesc) * L->chunks.size());
+  put(L->off_cchunks, L->cchunks.data(), sizeof(ChunkDesc) * L->cchunks.size());
   put(L->off_tiles, L->tiles.data(), sizeof(TileDesc) * L->tiles.size());
   put(L->off_work, L->work.data(), sizeof(QuantWork) * L->work.size());
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -112,6 +112,7 @@ typedef struct {
   int32_t n, m;
   int64_t S, total;
   int64_t num_chunks;   /* work chunks over the whole buffer */
+  int64_t num_coarse_chunks; /* chunks of 32*chunk_elems (norms, masked zero) */
   int64_t num_frags;    /* tensor-rank intersections */
   int64_t num_tiles;    /* quantisation tiles of all quantised tensors */
   int64_t chunk_elems;  /* maximum chunk length */
@@ -121,7 +122,9 @@ typedef struct {
 
 /* rs_layout_create - validate a layout and build its tables (host only).
  *   specs, n, m, S, offsets  as from rs_plan (any valid layout is accepted)
- *   chunk_elems  maximum elements per work chunk, a multiple of 64; 0 = 16384
+ *   chunk_elems  maximum elements per work chunk, a multiple of 64, at most
+ *                2^22; 0 = 2048.  A second table of 32x larger chunks is
+ *                built for the norms and the masked zero.
  *   out          receives the handle
  * RS_ERR_INVALID_ARG if a tensor overlaps the next, leaves the buffer, has a
  * granule cut by a shard boundary, or a quantisation tile crosses a shard
