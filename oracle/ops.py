@@ -58,15 +58,16 @@ def _range_of(l: int, n: int, S: int, k0: int, k1: int) -> Tuple[int, int]:
 
 
 def pack(tensors: Sequence[np.ndarray], offsets: Sequence[int], S: int, m: int,
-         buf: np.ndarray, buf_dtype: str, k0: int, k1: int) -> np.ndarray:
+         buf: np.ndarray, buf_dtype: str, k0: int, k1: int, inplace: bool = False) -> np.ndarray:
     """buf[l_t + i] = cast(tensor_t.flat[i]) for positions in ranks [k0, k1);
     every other position of those ranks (the padding between tensors) = 0.
 
     buf holds fp32 values (buf_dtype "f32") or bf16 bit patterns ("bf16",
     uint16 array).  Sources are fp32 arrays or bf16 bit patterns (uint16).
-    Returns a new array; positions outside [k0*S, k1*S) are kept.
+    Returns a new array (buf itself when inplace); positions outside
+    [k0*S, k1*S) are kept.
     """
-    out = buf.copy()
+    out = buf if inplace else buf.copy()
     out[k0 * S:k1 * S] = 0
     for t, l in zip(tensors, offsets):
         flat = np.asarray(t).reshape(-1)
@@ -104,15 +105,16 @@ def unpack(buf: np.ndarray, shapes: Sequence[Tuple[int, int]], offsets: Sequence
 
 def scale_add(y: np.ndarray, x: np.ndarray, alpha: float, beta: float,
               items: Sequence[Item], offsets: Sequence[int], S: int, m: int,
-              k0: int, k1: int, mask: Optional[Sequence[int]] = None
+              k0: int, k1: int, mask: Optional[Sequence[int]] = None, inplace: bool = False
               ) -> Tuple[np.ndarray, np.ndarray]:
     """y <- fl(fl(alpha*y) + fl(beta*x)) in fp32 over the tensor elements of
     ranks [k0, k1) (padding untouched; tensors with mask[t] == 0 skipped).
 
     x is fp32 or bf16 bit patterns (uint16).  found_inf[k] = 1 when any value
-    written in rank k is not finite.  Returns (new y, found_inf[m] uint32).
+    written in rank k is not finite.  Returns (new y, found_inf[m] uint32);
+    with inplace the new y is y itself.
     """
-    out = y.copy()
+    out = y if inplace else y.copy()
     found = np.zeros(m, dtype=np.uint32)
     a, b = F32(alpha), F32(beta)
     for tid, k, lo, hi in fragments(items, offsets, S, m):
@@ -211,6 +213,19 @@ def quant_tile(tile: np.ndarray, fmt: str) -> Tuple[np.float32, np.ndarray]:
     return scale, codes
 
 
+def tile_counts(spec) -> Tuple[int, int]:
+    """(tile rows, tile cols) of a quantised tensor."""
+    return -(-spec.rows // spec.q_rows), -(-spec.cols // spec.q_cols)
+
+
+def tile_bounds(spec, local: int) -> Tuple[int, int, int, int]:
+    """Tile number `local` of a tensor in row-major tile order -> (r0, r1, c0, c1)."""
+    _, ntc = tile_counts(spec)
+    ti, tj = divmod(local, ntc)
+    r0, c0 = ti * spec.q_rows, tj * spec.q_cols
+    return r0, min(spec.rows, r0 + spec.q_rows), c0, min(spec.cols, c0 + spec.q_cols)
+
+
 def block_quant(x: np.ndarray, specs, offsets: Sequence[int], S: int, m: int, fmt: str,
                 k0: int, k1: int, codes: np.ndarray, scales: np.ndarray,
                 only_tiles=None) -> Tuple[np.ndarray, np.ndarray]:
@@ -221,16 +236,24 @@ def block_quant(x: np.ndarray, specs, offsets: Sequence[int], S: int, m: int, fm
     (quantised tensors only, in group order), row-major inside a tensor.
     Positions and scales of other tiles are kept.  Every tile must lie inside
     one rank; an exception is raised otherwise.  only_tiles, when given, is a
-    set of global tile indices to compute (a sample of a large group).
+    collection of global tile indices to compute (a sample of a large group).
     """
     codes = codes.copy()
     scales = scales.copy()
+    wanted = None if only_tiles is None else set(int(i) for i in only_tiles)
     base = 0
     for spec, l in zip(specs, offsets):
         if spec.q_rows <= 0:
             continue
+        ntr, ntc = tile_counts(spec)
+        count = ntr * ntc
+        if wanted is None:
+            locals_ = range(count)
+        else:
+            locals_ = sorted(i - base for i in wanted if base <= i < base + count)
         C = spec.cols
-        for idx, (r0, r1, c0, c1) in enumerate(tile_grid(spec.rows, C, spec.q_rows, spec.q_cols)):
+        for idx in locals_:
+            r0, r1, c0, c1 = tile_bounds(spec, idx)
             first = l + r0 * C + c0
             last = l + (r1 - 1) * C + (c1 - 1)
             k = first // S
@@ -238,15 +261,13 @@ def block_quant(x: np.ndarray, specs, offsets: Sequence[int], S: int, m: int, fm
                 raise ValueError(f"tile {base + idx} of {spec.name} straddles a shard boundary")
             if not (k0 <= k < k1):
                 continue
-            if only_tiles is not None and (base + idx) not in only_tiles:
-                continue
             pos = l + (np.arange(r0, r1)[:, None] * C + np.arange(c0, c1)[None, :])
             sc, cd = quant_tile(x[pos], fmt)
             scales[base + idx] = sc
             codes[pos] = cd
-        base += len(tile_grid(spec.rows, C, spec.q_rows, spec.q_cols))
+        base += count
     return codes, scales
 
 
 def num_tiles(specs) -> int:
-    return sum(len(tile_grid(s.rows, s.cols, s.q_rows, s.q_cols)) for s in specs if s.q_rows > 0)
+    return sum(tile_counts(s)[0] * tile_counts(s)[1] for s in specs if s.q_rows > 0)

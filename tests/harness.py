@@ -130,6 +130,14 @@ def assert_f32_equal_nan_class(got: np.ndarray, exp: np.ndarray, what: str, max_
     """Equal bits for non-NaN values (or within max_ulp), NaN where NaN."""
     gn, en = np.isnan(got), np.isnan(exp)
     assert np.array_equal(gn, en), f"{what}: NaN positions differ"
+    if max_ulp == 0:
+        ok = got.view(np.uint32) == exp.astype(np.float32).view(np.uint32)
+        ok |= gn
+        if not ok.all():
+            i = int(np.flatnonzero(~ok)[0])
+            raise AssertionError(f"{what}: {int((~ok).sum())} values differ; first at {i}: "
+                                 f"got {got[i]!r} expected {exp[i]!r}")
+        return
     g = got[~gn].view(np.int32).astype(np.int64)
     e = exp[~en].astype(np.float32).view(np.int32).astype(np.int64)
     # map sign-magnitude to a monotone integer line
