@@ -56,6 +56,22 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "native", "e4m3_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "native", "libe4m3_probe.so")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """Test-only probe of the FP8 conversion instruction (tests/native)."""
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.run([hipcc(), "-x", "hip"] + DEVICE + [PROBE_SRC, "-shared", "-fPIC", "-o", tmp]
+                   + COMMON, check=True)
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build()
+    build_probe()
     sys.exit(0)

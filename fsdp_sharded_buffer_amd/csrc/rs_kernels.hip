@@ -231,8 +231,10 @@ __device__ __forceinline__ void zero_run(void* dst, int64_t n) {
 
 // ------------------------------------------------------------ pack/unpack
 //
-// Chunk kernels take the chunk range [c0, c0 + nc) and stride over it with
-// the grid, so the grid may be capped below nc (a persistent grid).
+// Chunk kernels take the chunk range [c0, c0 + nc); workgroup b handles
+// chunk b (one workgroup per chunk measured fastest on MI355X: fewer,
+// longer-lived workgroups or consecutive chunk runs per workgroup were
+// slower), striding by the grid if the grid is ever smaller than nc.
 
 template <int SK, int DK>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const ChunkDesc* __restrict__ chunks,
@@ -486,27 +488,34 @@ __global__ __launch_bounds__(kThreads) void sqnorm_combine_kernel(
 // elements (window of 8 ulp), and every element of a tile whose scale is
 // zero, subnormal, infinite or NaN, are encoded from the true quotient.
 
-// FP8 E4M3: q' is safe when |q'| >= 2^-6 (plus margin; below that the
-// E4M3 subnormal grid applies) and its 20 dropped mantissa bits are more
-// than 8 ulp from the half-way pattern 0x80000.
+// FP8 E4M3: q' is safe when 2^-6 (plus margin) <= |q'| < 464 - below, the
+// E4M3 subnormal grid applies; 464 is the first midpoint past 448 - and its
+// 20 dropped mantissa bits are more than 8 ulp from the half-way pattern
+// 0x80000.
 __device__ __forceinline__ bool e4m3_safe(uint32_t u) {
   const uint32_t a = u & 0x7fffffffu;
-  return a >= 0x3c800010u && ((a & 0xfffffu) - 0x7fff8u) > 16u;
+  return a - 0x3c800010u < 0x43e80000u - 0x3c800010u && ((a & 0xfffffu) - 0x7fff8u) > 16u;
 }
 
-// Encoder for |q| >= 2^-6 and finite (the safe case above): clamp to 448,
-// round the mantissa to 3 bits to nearest even, rebias 127 -> 7.
-__device__ __forceinline__ uint32_t e4m3_encode_normal(uint32_t u) {
-  uint32_t a = min(u & 0x7fffffffu, 0x43e00000u);
-  a += 0x7ffffu + ((a >> 20) & 1u);
-  return ((a >> 20) - (120u << 3)) | ((u >> 24) & 0x80u);
+// Four safe values -> four E4M3 codes, little-endian in one word, with
+// gfx950's conversion instruction (OCP E4M3, round to nearest even).  For
+// finite inputs with 2^-6 <= |q| < 464 it equals the saturating encoder
+// above; a test checks that on every such fp32 input.
+__device__ __forceinline__ uint32_t e4m3_pack4_normal(float q0, float q1, float q2, float q3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
+  return uint32_t(w);
 }
 
-// INT8: q' is safe when more than |q'| * 2^-20 (>= 8 ulp) from a half-integer.
-__device__ __forceinline__ bool int8_safe(float q) {
-  const float a = fabsf(q);
-  const float f = a - floorf(a);
-  return fabsf(f - 0.5f) > a * 0x1p-20f;
+// INT8: q' is safe when its distance to the nearest integer is below
+// 0.5 - |q'| * 2^-20, i.e. more than |q'| * 2^-20 (>= 8 ulp) from a
+// half-integer; r = rint(q') is then also the rounded true quotient.
+__device__ __forceinline__ bool int8_safe(float q, float r) {
+  return fabsf(q - r) < 0.5f - fabsf(q) * 0x1p-20f;
+}
+
+__device__ __forceinline__ uint32_t int8_from_rint(float r) {
+  return uint32_t(int32_t(fminf(fmaxf(r, -127.0f), 127.0f))) & 0xffu;
 }
 
 template <int FMT>
@@ -523,26 +532,27 @@ __device__ __forceinline__ uint32_t encode_exact(float x, float scale, bool zero
   return encode<FMT>(x / scale);
 }
 
-// Walks the float4 slots f = lane, lane + team, ... of a tile with
-// cols/4 slots per row, as element offsets from the tile's first element.
+// Walks the float4 slots f = lane, lane + team, ... of a tile with c4
+// slots per row, as element offsets from the tile's first element (tiles
+// span less than 2^31 elements; the layout checks it).
 struct SlotWalk {
-  int r, c, dq, dr, c4;
-  int64_t ld;
-  __device__ __forceinline__ SlotWalk(int lane, int team, int c4_, int64_t ld_) {
+  int off, c, dr, c4, step, wrap;
+  __device__ __forceinline__ SlotWalk(int lane, int team, int c4_, int ld) {
     c4 = c4_;
-    ld = ld_;
-    r = lane / c4;
+    const int r = lane / c4;
     c = lane - r * c4;
-    dq = team / c4;
+    const int dq = team / c4;
     dr = team - dq * c4;
+    off = r * ld + c * 4;
+    step = dq * ld + dr * 4;      // advance by team slots
+    wrap = ld - c4 * 4;           // extra when the column wraps to the next row
   }
-  __device__ __forceinline__ int64_t off() const { return int64_t(r) * ld + c * 4; }
   __device__ __forceinline__ void next() {
-    r += dq;
+    off += step;
     c += dr;
     if (c >= c4) {
       c -= c4;
-      ++r;
+      off += wrap;
     }
   }
 };
@@ -575,11 +585,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
   const int nf = active ? td.rows * c4 : 0;
   const int ne = active ? td.rows * td.cols : 0;
   if (vec) {
-    SlotWalk sw(lane, team, c4, td.ld);
+    SlotWalk sw(lane, team, c4, int(td.ld));
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       u32x4 q = {0u, 0u, 0u, 0u};
-      if (lane + i * team < nf) q = ld16<RS_QUANT_NT>(base + sw.off());
+      if (lane + i * team < nf) q = ld16<RS_QUANT_NT>(base + sw.off);
       sw.next();
       v[4 * i + 0] = f32(q.x);
       v[4 * i + 1] = f32(q.y);
@@ -628,47 +638,48 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
   }
   uint32_t slow = 0;  // bit i: slot i needs the exact path
   {
-    SlotWalk sw(lane, team, c4, td.ld);
+    SlotWalk sw(lane, team, c4, int(td.ld));
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (lane + i * team < nf) {
         float q[4];
-        bool safe = fast;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          q[j] = v[4 * i + j] * rcp;
-          if constexpr (FMT == RS_Q_FP8_E4M3)
-            safe = safe && e4m3_safe(u32(q[j]));
-          else
-            safe = safe && int8_safe(q[j]);
-        }
-        if (safe) {
-          uint32_t word;
-          if constexpr (FMT == RS_Q_FP8_E4M3)
-            word = e4m3_encode_normal(u32(q[0])) | (e4m3_encode_normal(u32(q[1])) << 8) |
-                   (e4m3_encode_normal(u32(q[2])) << 16) | (e4m3_encode_normal(u32(q[3])) << 24);
-          else
-            word = int8_encode(q[0]) | (int8_encode(q[1]) << 8) | (int8_encode(q[2]) << 16) |
-                   (int8_encode(q[3]) << 24);
-          *reinterpret_cast<uint32_t*>(cbase + sw.off()) = word;
+        for (int j = 0; j < 4; ++j) q[j] = v[4 * i + j] * rcp;
+        bool safe = fast;
+        uint32_t word;
+        if constexpr (FMT == RS_Q_FP8_E4M3) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) safe = safe && e4m3_safe(u32(q[j]));
+          word = e4m3_pack4_normal(q[0], q[1], q[2], q[3]);
         } else {
-          slow |= 1u << i;
+          float r[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            r[j] = __builtin_rintf(q[j]);
+            safe = safe && int8_safe(q[j], r[j]);
+          }
+          word = int8_from_rint(r[0]) | (int8_from_rint(r[1]) << 8) | (int8_from_rint(r[2]) << 16) |
+                 (int8_from_rint(r[3]) << 24);
         }
+        if (safe)
+          *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
+        else
+          slow |= 1u << i;
       }
       sw.next();
     }
   }
   if (slow) {  // rare: re-read the slot (cache resident) and divide
-    SlotWalk sw(lane, team, c4, td.ld);
+    SlotWalk sw(lane, team, c4, int(td.ld));
 #pragma unroll 1
     for (int i = 0; i < 16; ++i) {
       if (slow & (1u << i)) {
-        const u32x4 q = ld16<false>(base + sw.off());
+        const u32x4 q = ld16<false>(base + sw.off);
         const uint32_t word = encode_exact<FMT>(f32(q.x), scale, zero_tile, nan_tile) |
                               (encode_exact<FMT>(f32(q.y), scale, zero_tile, nan_tile) << 8) |
                               (encode_exact<FMT>(f32(q.z), scale, zero_tile, nan_tile) << 16) |
                               (encode_exact<FMT>(f32(q.w), scale, zero_tile, nan_tile) << 24);
-        *reinterpret_cast<uint32_t*>(cbase + sw.off()) = word;
+        *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
       }
       sw.next();
     }
@@ -698,15 +709,8 @@ rs_status check_ptr(const void* p, size_t align, const char* fn, const char* wha
   return RS_OK;
 }
 
-#ifndef RS_GRID_CAP
-#define RS_GRID_CAP 0
-#endif
-
-// Workgroups for nc chunks: one per chunk, or at most RS_GRID_CAP.
-dim3 chunk_grid(int64_t nc) {
-  const int64_t g = (RS_GRID_CAP > 0 && nc > RS_GRID_CAP) ? RS_GRID_CAP : nc;
-  return dim3(static_cast<unsigned>(g));
-}
+// Workgroups for nc chunks: one per chunk.
+dim3 chunk_grid(int64_t nc) { return dim3(static_cast<unsigned>(nc)); }
 
 rs_status after_launch(const char* fn) {
   const hipError_t e = hipGetLastError();

@@ -204,9 +204,10 @@ extern "C" rs_status rs_layout_create(const rs_tensor_spec* specs, int32_t n, in
     if (s.rows <= 0 || s.cols <= 0 || s.gran_rows < 0)
       return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name + " has a bad shape");
     if ((s.q_rows > 0) != (s.q_cols > 0) || s.q_rows < 0 || s.q_cols < 0 ||
-        int64_t(s.q_rows) * s.q_cols > kMaxTileElems)
+        int64_t(s.q_rows) * s.q_cols > kMaxTileElems ||
+        int64_t(s.q_rows) * s.cols > int64_t(INT32_MAX))
       return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name +
-                                          " has a bad quantisation tile (at most 16384 elements)");
+                                          " has a bad quantisation tile (at most 16384 elements, q_rows * cols < 2^31)");
     const int64_t l = offsets[t], E = s.rows * s.cols, g = granule_of(s);
     if (l < prev_end)
       return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name + " overlaps the previous tensor");

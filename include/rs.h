@@ -62,7 +62,8 @@ enum { RS_Q_FP8_E4M3 = 0, RS_Q_INT8 = 1 };
  *   granularity); 0 means element granularity (granule = 1 element),
  *   otherwise the granule is gran_rows*cols elements.
  * q_rows, q_cols: block-quantisation tile (veScale-FSDP, section 6.3); 0,0
- *   means the tensor is not quantised.  q_rows*q_cols <= 16384. */
+ *   means the tensor is not quantised.  q_rows*q_cols <= 16384 and
+ *   q_rows*cols < 2^31. */
 typedef struct {
   int64_t rows;
   int64_t cols;

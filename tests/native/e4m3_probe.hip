@@ -1,0 +1,36 @@
+// Test-only probe: applies gfx950's packed fp32 -> OCP E4M3 conversion
+// (the instruction the block quantisation fast path uses) to consecutive
+// fp32 bit patterns, four at a time exactly as the kernel packs a word, so
+// a test can compare every input of the fast path's domain with the CPU
+// oracle.  Not part of librs.so.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+__global__ void probe_kernel(uint32_t first, int64_t n, uint32_t sign, uint8_t* out) {
+  const int64_t i = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  float q[4];
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k = i + j < n ? i + j : n - 1;
+    q[j] = __uint_as_float((first + uint32_t(k)) | sign);
+  }
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+  for (int j = 0; j < 4; ++j)
+    if (i + j < n) out[i + j] = uint8_t(uint32_t(w) >> (8 * j));
+}
+
+}  // namespace
+
+// out[k] = E4M3 code of the fp32 with bits (first + k) | sign, k < n.
+extern "C" int probe_e4m3_hw(uint32_t first, int64_t n, uint32_t sign, uint8_t* out, void* stream) {
+  if (n <= 0 || !out) return -1;
+  const int64_t threads = (n + 3) / 4;
+  const unsigned grid = unsigned((threads + 255) / 256);
+  hipLaunchKernelGGL(probe_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), first,
+                     n, sign, out);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
