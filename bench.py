@@ -53,6 +53,17 @@ def op_bytes(w, S, n_tiles):
     }
 
 
+def extra_bytes(w, S, n_tiles):
+    """Algorithmic bytes of the operations measured beside the step."""
+    Eq = sum(t.numel for t in w.tensors if t.q_rows)
+    E = w.numel
+    return {
+        "block_dequant": Eq + 4 * n_tiles + 4 * Eq,   # codes + scales in, fp32 out
+        "adamw_step": 28 * E,    # p, g, m, v in; p, m, v out (fp32)
+        "sgd_step": 20 * E,      # p, g, buf in; p, buf out (fp32)
+    }
+
+
 def read_counters(workload: str):
     """HBM traffic of the scale-add kernel from the committed rocprofv3
     counter summary, if it was taken on the current kernel source."""
@@ -173,6 +184,17 @@ def main():
         "zero": lambda: R.rs_group_zero(h, grad, R.RS_F32, None, 0, m, sp),
     }
     nbytes = op_bytes(w, S, lay.info["num_tiles"])
+    deq = torch.empty(total, dtype=torch.float32, device=dev)
+    mom = torch.zeros(total, dtype=torch.float32, device=dev)
+    var = torch.zeros(total, dtype=torch.float32, device=dev)
+    extra = {
+        "block_dequant": lambda: R.rs_block_dequant(h, codes, qfmt, scales, deq, R.RS_F32, 0, m, sp),
+        "adamw_step": lambda: R.rs_adamw_step(h, deq, acc, mom, var, 1e-4, 0.9, 0.95, 1e-8, 0.1,
+                                              0.5, 0.1, 1.0, None, None, 0, m, sp),
+        "sgd_step": lambda: R.rs_sgd_step(h, deq, acc, mom, 1e-4, 0.9, 0.0, False, 1.0, None, None,
+                                          0, m, sp),
+    }
+    xbytes = extra_bytes(w, S, lay.info["num_tiles"])
 
     def step():
         for f in ops.values():
@@ -203,10 +225,12 @@ def main():
         del a, b
 
     # per-operation launch time with HIP events on the launch stream
-    only = [o for o in args.only.split(",") if o] or list(ops)
-    per_op = {}
+    only = [o for o in args.only.split(",") if o] or (list(ops) + list(extra))
+    per_op, per_extra = {}, {}
+    allops = dict(ops, **extra)
+    allbytes = dict(nbytes, **xbytes)
     for name in only:
-        f = ops[name]
+        f = allops[name]
         for _ in range(3):
             f()
         torch.cuda.synchronize()
@@ -226,17 +250,20 @@ def main():
             e1.synchronize()
             samples.append(e0.elapsed_time(e1) / reps)
         med = float(np.median(samples))
-        gbs = nbytes[name] / (med * 1e-3) / 1e9
-        per_op[name] = {"us": round(med * 1e3, 2), "min_us": round(min(samples) * 1e3, 2),
-                        "bytes": nbytes[name], "GB/s": round(gbs, 1),
-                        "frac_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps}
+        gbs = allbytes[name] / (med * 1e-3) / 1e9
+        (per_op if name in ops else per_extra)[name] = {
+            "us": round(med * 1e3, 2), "min_us": round(min(samples) * 1e3, 2),
+            "bytes": allbytes[name], "GB/s": round(gbs, 1),
+            "frac_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps}
         log(f"{name:12s} {med*1e3:9.1f} us  {gbs:8.1f} GB/s  {gbs/HBM_PEAK_GBS*100:5.1f}% of peak")
 
-    dom = "scale_add" if "scale_add" in per_op else next(iter(per_op))
+    timed = dict(per_op, **per_extra)
+    dom = "scale_add" if "scale_add" in timed else next(iter(timed))
     roof = {"kernel": "scale_add_kernel<fp32>" if dom == "scale_add" else dom,
-            "bound": "hbm", "achieved": per_op[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": per_op[dom]["frac_peak"], "traffic": read_counters(w.name),
-            "bytes_per_launch": nbytes[dom], "avg_launch_us": per_op[dom]["us"]}
+            "bound": "hbm", "achieved": timed[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": timed[dom]["frac_peak"],
+            "traffic": read_counters(w.name) if dom == "scale_add" else None,
+            "bytes_per_launch": allbytes[dom], "avg_launch_us": timed[dom]["us"]}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -256,6 +283,7 @@ def main():
                    "pad_frac": round(pinfo["pad_frac"], 5)},
         "frac_peak": round(value / HBM_PEAK_GBS, 4),
         "ops": per_op,
+        "next_ops": per_extra,
         "roofline": roof,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),

@@ -15,7 +15,7 @@ from ctypes import POINTER, byref, c_double, c_float, c_int32, c_int64, c_void_p
 from typing import Dict, List, Optional, Sequence, Tuple
 
 from ._lib import lib, RsError, check  # noqa: F401
-from ._lib import rs_tensor_spec, rs_plan_info, rs_layout_info
+from ._lib import rs_tensor_spec, rs_plan_info, rs_layout_info, rs_adamw_params, rs_sgd_params
 
 RS_F32, RS_BF16, RS_U8 = 0, 1, 2
 RS_Q_FP8_E4M3, RS_Q_INT8 = 0, 1
@@ -24,7 +24,8 @@ __all__ = [
     "RS_F32", "RS_BF16", "RS_U8", "RS_Q_FP8_E4M3", "RS_Q_INT8", "RsError",
     "rs_plan", "rs_layout_create", "rs_layout_get_info", "rs_layout_upload",
     "rs_layout_destroy", "rs_pack", "rs_unpack", "rs_group_scale_add", "rs_group_zero",
-    "rs_ragged_sqnorm", "rs_block_quant", "rs_status_str", "rs_last_error",
+    "rs_ragged_sqnorm", "rs_block_quant", "rs_block_dequant", "rs_adamw_step", "rs_sgd_step",
+    "rs_status_str", "rs_last_error",
     "Layout", "ptr_table", "dtype_code", "specs_array",
 ]
 
@@ -114,9 +115,34 @@ def rs_ragged_sqnorm(layout, x, sq, partial=None, found_inf=None, ws=None, k0: i
                                  k0, k1, _stream(stream)))
 
 
-def rs_block_quant(layout, x, fmt: int, codes, scales, k0: int, k1: int, stream=None) -> None:
-    check(lib().rs_block_quant(layout, _ptr(x), fmt, _ptr(codes), _ptr(scales), k0, k1,
-                               _stream(stream)))
+def rs_block_quant(layout, x, fmt: int, codes, scales, k0: int, k1: int, stream=None,
+                   found_inf=None) -> None:
+    check(lib().rs_block_quant(layout, _ptr(x), fmt, _ptr(codes), _ptr(scales), _ptr(found_inf),
+                               k0, k1, _stream(stream)))
+
+
+def rs_block_dequant(layout, codes, fmt: int, scales, y, y_dt: int, k0: int, k1: int,
+                     stream=None) -> None:
+    check(lib().rs_block_dequant(layout, _ptr(codes), fmt, _ptr(scales), _ptr(y), y_dt, k0, k1,
+                                 _stream(stream)))
+
+
+def rs_adamw_step(layout, p, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
+                  weight_decay: float, bias_correction1: float, bias_correction2: float,
+                  grad_scale: float = 1.0, tensor_mask=None, found_inf=None, k0: int = 0,
+                  k1: int = 1, stream=None) -> None:
+    hp = rs_adamw_params(lr, beta1, beta2, eps, weight_decay, bias_correction1, bias_correction2,
+                         grad_scale)
+    check(lib().rs_adamw_step(layout, _ptr(p), _ptr(g), _ptr(m), _ptr(v), byref(hp),
+                              _ptr(tensor_mask), _ptr(found_inf), k0, k1, _stream(stream)))
+
+
+def rs_sgd_step(layout, p, g, buf, lr: float, momentum: float, weight_decay: float,
+                nesterov: bool = False, grad_scale: float = 1.0, tensor_mask=None, found_inf=None,
+                k0: int = 0, k1: int = 1, stream=None) -> None:
+    hp = rs_sgd_params(lr, momentum, weight_decay, grad_scale, 1 if nesterov else 0)
+    check(lib().rs_sgd_step(layout, _ptr(p), _ptr(g), _ptr(buf), byref(hp), _ptr(tensor_mask),
+                            _ptr(found_inf), k0, k1, _stream(stream)))
 
 
 def rs_status_str(status: int) -> str:

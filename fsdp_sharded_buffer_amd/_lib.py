@@ -27,6 +27,17 @@ class rs_layout_info(ctypes.Structure):
                 ("chunk_elems", c_int64), ("device_bytes", c_int64), ("workspace_bytes", c_int64)]
 
 
+class rs_adamw_params(ctypes.Structure):
+    _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
+                ("weight_decay", c_float), ("bias_correction1", c_float),
+                ("bias_correction2", c_float), ("grad_scale", c_float)]
+
+
+class rs_sgd_params(ctypes.Structure):
+    _fields_ = [("lr", c_float), ("momentum", c_float), ("weight_decay", c_float),
+                ("grad_scale", c_float), ("nesterov", c_int32)]
+
+
 class RsError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"rs status {status}: {msg}")
@@ -52,8 +63,15 @@ SIGNATURES = {
                                 c_void_p]),
     "rs_ragged_sqnorm": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_int32, c_int32, c_void_p]),
-    "rs_block_quant": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
-                                 c_int32, c_void_p]),
+    "rs_block_quant": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                 c_int32, c_int32, c_void_p]),
+    "rs_block_dequant": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                   c_int32, c_int32, c_void_p]),
+    "rs_adamw_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                POINTER(rs_adamw_params), c_void_p, c_void_p, c_int32, c_int32,
+                                c_void_p]),
+    "rs_sgd_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(rs_sgd_params),
+                              c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
     "rs_status_str": (c_char_p, [c_int32]),
     "rs_last_error": (c_char_p, []),
 }

@@ -11,6 +11,7 @@
 // both sides of a run are 16-byte aligned, element accesses otherwise.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <string>
 
@@ -89,6 +90,10 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #ifndef RS_FILL_BYTES
 #define RS_FILL_BYTES 262144
 #endif
+#ifndef RS_DEQ_LDS
+#define RS_DEQ_LDS 1
+#endif
+
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -568,6 +573,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
                                                          const float* __restrict__ x,
                                                          uint8_t* __restrict__ codes,
                                                          float* __restrict__ scales,
+                                                         uint32_t* __restrict__ found_inf,
                                                          int vec_ok) {
   __shared__ uint32_t lds[kThreads / kWave];
   const QuantWork w = work[w0 + blockIdx.x];
@@ -622,7 +628,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
   float scale = famax / Q;
   const bool nan_tile = amax > 0x7f800000u;
   if (nan_tile) scale = __uint_as_float(0x7fc00000u);
-  if (lane == 0) scales[td.scale_idx] = scale;
+  if (lane == 0) {
+    scales[td.scale_idx] = scale;
+    // an Inf or NaN |x| pattern is >= the +Inf pattern
+    if (found_inf && amax >= 0x7f800000u) found_inf[td.rank] = 1u;
+  }
   const bool zero_tile = scale == 0.0f;
   const float rcp = 1.0f / scale;
   // the reciprocal path needs a normal, finite scale (and so a finite rcp)
@@ -682,6 +692,247 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
         *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
       }
       sw.next();
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dequant
+//
+// y = fl(decode(code) * scale) per element of every tile in the range; the
+// decode is exact (E4M3 with gfx950's widening conversion, INT8 as an
+// integer), so the product is the only rounding (plus the bf16 cast).
+
+template <int FMT>
+__device__ __forceinline__ void decode4(uint32_t word, float d[4]) {
+  if constexpr (FMT == RS_Q_FP8_E4M3) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(word), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(word), true);
+    d[0] = lo[0];
+    d[1] = lo[1];
+    d[2] = hi[0];
+    d[3] = hi[1];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = float(int8_t(uint8_t(word >> (8 * j))));
+  }
+}
+
+template <int YK>
+__device__ __forceinline__ void store4(char* yb, int64_t elem, const float d[4], float scale) {
+  if constexpr (YK == 0) {
+    u32x4 o;
+    o.x = u32(d[0] * scale);
+    o.y = u32(d[1] * scale);
+    o.z = u32(d[2] * scale);
+    o.w = u32(d[3] * scale);
+    st16<false>(yb + elem * 4, o);
+  } else {
+    uint2 o;
+    o.x = bf16_rne(d[0] * scale) | (bf16_rne(d[1] * scale) << 16);
+    o.y = bf16_rne(d[2] * scale) | (bf16_rne(d[3] * scale) << 16);
+    *reinterpret_cast<uint2*>(yb + elem * 2) = o;
+  }
+}
+
+// Lanes take 4 codes (one 32-bit load, one 16-byte fp32 store) per slot,
+// all loads of a lane issued before its stores; unaligned tiles one code
+// per lane.  (16 codes per lane - 16-byte loads, lane-strided stores - was
+// several times slower.)
+template <int FMT, int YK>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const QuantWork* __restrict__ work,
+                                                           int64_t w0,
+                                                           const TileDesc* __restrict__ tiles,
+                                                           const uint8_t* __restrict__ codes,
+                                                           const float* __restrict__ scales,
+                                                           void* __restrict__ y, int vec_ok) {
+  const QuantWork w = work[w0 + blockIdx.x];
+  const int team = w.team;
+  const int slot = threadIdx.x / team;
+  const int lane = threadIdx.x % team;
+  const bool active = slot < w.count;
+  const TileDesc td = tiles[w.tile_begin + (active ? slot : 0)];
+  const float scale = scales[td.scale_idx];
+  const uint8_t* cb = codes + td.buf_off;
+  char* yb = static_cast<char*>(y) + td.buf_off * esize<YK>();
+#if RS_DEQ_LDS
+  // stage each team's tile codes in LDS with coalesced 16-byte loads, then
+  // decode 4 codes per lane with lane-contiguous 16-byte stores
+  __shared__ uint32_t stage[kThreads * 16];  // 16 KB: team * 64 codes per tile
+  const bool g16 = vec_ok == 2 && td.cols % 16 == 0 && td.ld % 16 == 0 && td.buf_off % 16 == 0;
+  if (__syncthreads_and(g16 || !active)) {  // uniform: every active tile qualifies
+    uint32_t* tl = stage + slot * team * 16;
+    const int c16 = td.cols >> 4;
+    const int n16 = active ? td.rows * c16 : 0;
+    for (int f = lane; f < n16; f += team) {
+      const int r = f / c16;
+      const int c = f - r * c16;
+      const u32x4 q = ld16<RS_PACK_NT>(cb + int64_t(r) * td.ld + c * 16);
+      uint32_t* dst = tl + (r * td.cols + c * 16) / 4;
+      dst[0] = q.x;
+      dst[1] = q.y;
+      dst[2] = q.z;
+      dst[3] = q.w;
+    }
+    __syncthreads();
+    const int c4 = td.cols >> 2;
+    const int nf = active ? td.rows * c4 : 0;
+    for (int f = lane; f < nf; f += team) {
+      const int r = f / c4;
+      const int c = f - r * c4;
+      float d[4];
+      decode4<FMT>(tl[(r * td.cols) / 4 + c], d);
+      store4<YK>(yb, int64_t(r) * td.ld + c * 4, d, scale);
+    }
+    return;
+  }
+#endif
+  if (!active) return;
+  if (w.vec && vec_ok) {
+    const int c4 = td.cols >> 2;
+    const int nf = td.rows * c4;
+    SlotWalk sw(lane, team, c4, int(td.ld));
+    uint32_t q[16];
+    int off[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      off[i] = sw.off;
+      if (lane + i * team < nf) q[i] = *reinterpret_cast<const uint32_t*>(cb + off[i]);
+      sw.next();
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (lane + i * team < nf) {
+        float d[4];
+        decode4<FMT>(q[i], d);
+        store4<YK>(yb, off[i], d, scale);
+      }
+    }
+  } else {
+    const int ne = td.rows * td.cols;
+    for (int e = lane; e < ne; e += team) {
+      const int r = e / td.cols;
+      const int64_t o = int64_t(r) * td.ld + (e - r * td.cols);
+      float d[4];
+      decode4<FMT>(cb[o], d);
+      const float v = d[0] * scale;
+      if constexpr (YK == 0)
+        reinterpret_cast<float*>(yb)[o] = v;
+      else
+        reinterpret_cast<uint16_t*>(yb)[o] = uint16_t(bf16_rne(v));
+    }
+  }
+}
+
+// -------------------------------------------------------------- optimizers
+//
+// Fused optimizer steps over the fragments of a rank range, one launch for
+// the whole group, fp32 with every operation rounded once (contraction is
+// off in this file; sqrt and division are IEEE).
+
+struct AdamConst {
+  float beta1, beta2, omb1, omb2, eps, decay, step, bc2s, inv;
+};
+
+// True (uniformly) when any of the m found-inf flags is set: the step is
+// skipped, as the sharded gradient scaler does.
+__device__ __forceinline__ bool skip_step(const uint32_t* found_inf, int m) {
+  int hit = 0;
+  if (found_inf)
+    for (int i = threadIdx.x; i < m; i += kThreads) hit |= found_inf[i] != 0u;
+  return __syncthreads_or(hit) != 0;
+}
+
+__device__ __forceinline__ void adamw1(float& p, float g, float& m, float& v, const AdamConst& k) {
+  const float gg = g * k.inv;
+  const float m2 = k.beta1 * m + k.omb1 * gg;
+  const float v2 = k.beta2 * v + k.omb2 * (gg * gg);
+  const float den = sqrtf(v2) / k.bc2s + k.eps;
+  const float upd = m2 / den;
+  p = p * k.decay - k.step * upd;
+  m = m2;
+  v = v2;
+}
+
+__global__ __launch_bounds__(kThreads) void adamw_kernel(
+    const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* __restrict__ p,
+    const float* __restrict__ g, float* __restrict__ m, float* __restrict__ v, AdamConst k,
+    const uint8_t* __restrict__ mask, const uint32_t* __restrict__ found_inf, int m_ranks) {
+  if (skip_step(found_inf, m_ranks)) return;
+  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
+    const ChunkDesc c = chunks[c0 + i];
+    if (c.tensor < 0 || (mask && !mask[c.tensor])) continue;
+    float* pp = p + c.buf_off;
+    const float* gp = g + c.buf_off;
+    float* mp = m + c.buf_off;
+    float* vp = v + c.buf_off;
+    const int n = c.len;
+    const bool vec = aligned16(pp) && aligned16(gp) && aligned16(mp) && aligned16(vp);
+    const int nv = vec ? n / 4 : 0;
+    for (int q = threadIdx.x; q < nv; q += kThreads) {
+      u32x4 P = ld16<false>(pp + 4 * q), G = ld16<false>(gp + 4 * q);
+      u32x4 M = ld16<false>(mp + 4 * q), V = ld16<false>(vp + 4 * q);
+      float a[4] = {f32(P.x), f32(P.y), f32(P.z), f32(P.w)};
+      float b[4] = {f32(M.x), f32(M.y), f32(M.z), f32(M.w)};
+      float d[4] = {f32(V.x), f32(V.y), f32(V.z), f32(V.w)};
+      const float e[4] = {f32(G.x), f32(G.y), f32(G.z), f32(G.w)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) adamw1(a[j], e[j], b[j], d[j], k);
+      st16<false>(pp + 4 * q, u32x4{u32(a[0]), u32(a[1]), u32(a[2]), u32(a[3])});
+      st16<false>(mp + 4 * q, u32x4{u32(b[0]), u32(b[1]), u32(b[2]), u32(b[3])});
+      st16<false>(vp + 4 * q, u32x4{u32(d[0]), u32(d[1]), u32(d[2]), u32(d[3])});
+    }
+    for (int e = nv * 4 + threadIdx.x; e < n; e += kThreads) {
+      float a = pp[e], b = mp[e], d = vp[e];
+      adamw1(a, gp[e], b, d, k);
+      pp[e] = a;
+      mp[e] = b;
+      vp[e] = d;
+    }
+  }
+}
+
+struct SgdConst {
+  float lr, mu, wd, inv;
+  int nesterov;
+};
+
+__device__ __forceinline__ void sgd1(float& p, float g, float& b, const SgdConst& k) {
+  const float gg = g * k.inv + k.wd * p;
+  const float b2 = k.mu * b + gg;
+  const float d = k.nesterov ? gg + k.mu * b2 : b2;
+  p = p - k.lr * d;
+  b = b2;
+}
+
+__global__ __launch_bounds__(kThreads) void sgd_kernel(
+    const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* __restrict__ p,
+    const float* __restrict__ g, float* __restrict__ buf, SgdConst k,
+    const uint8_t* __restrict__ mask, const uint32_t* __restrict__ found_inf, int m_ranks) {
+  if (skip_step(found_inf, m_ranks)) return;
+  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
+    const ChunkDesc c = chunks[c0 + i];
+    if (c.tensor < 0 || (mask && !mask[c.tensor])) continue;
+    float* pp = p + c.buf_off;
+    const float* gp = g + c.buf_off;
+    float* bp = buf + c.buf_off;
+    const int n = c.len;
+    const bool vec = aligned16(pp) && aligned16(gp) && aligned16(bp);
+    const int nv = vec ? n / 4 : 0;
+    for (int q = threadIdx.x; q < nv; q += kThreads) {
+      u32x4 P = ld16<false>(pp + 4 * q), G = ld16<false>(gp + 4 * q), B = ld16<false>(bp + 4 * q);
+      float a[4] = {f32(P.x), f32(P.y), f32(P.z), f32(P.w)};
+      float b[4] = {f32(B.x), f32(B.y), f32(B.z), f32(B.w)};
+      const float e[4] = {f32(G.x), f32(G.y), f32(G.z), f32(G.w)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sgd1(a[j], e[j], b[j], k);
+      st16<false>(pp + 4 * q, u32x4{u32(a[0]), u32(a[1]), u32(a[2]), u32(a[3])});
+      st16<false>(bp + 4 * q, u32x4{u32(b[0]), u32(b[1]), u32(b[2]), u32(b[3])});
+    }
+    for (int e = nv * 4 + threadIdx.x; e < n; e += kThreads) {
+      float a = pp[e], b = bp[e];
+      sgd1(a, gp[e], b, k);
+      pp[e] = a;
+      bp[e] = b;
     }
   }
 }
@@ -857,8 +1108,8 @@ extern "C" rs_status rs_ragged_sqnorm(const rs_layout* L, const float* x, double
 }
 
 extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt fmt,
-                                    uint8_t* codes, float* scales, int32_t k0, int32_t k1,
-                                    void* stream) {
+                                    uint8_t* codes, float* scales, uint32_t* found_inf, int32_t k0,
+                                    int32_t k1, void* stream) {
   const char* fn = "rs_block_quant";
   RS_TRY(check_common(L, k0, k1, fn));
   if (fmt != RS_Q_FP8_E4M3 && fmt != RS_Q_INT8)
@@ -866,6 +1117,7 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
   RS_TRY(check_ptr(x, 4, fn, "x"));
   RS_TRY(check_ptr(codes, 1, fn, "codes"));
   RS_TRY(check_ptr(scales, 4, fn, "scales"));
+  if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
   // the 16-byte path needs x 16-byte aligned and codes 4-byte aligned
   const int vec_ok = (reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(codes) % 4 == 0) ? 1 : 0;
@@ -876,9 +1128,98 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
   if (fmt == RS_Q_FP8_E4M3)
     hipLaunchKernelGGL((quant_kernel<RS_Q_FP8_E4M3>), g, b, 0, s,
                        table<QuantWork>(L, L->off_work), w0, table<TileDesc>(L, L->off_tiles), x,
-                       codes, scales, vec_ok);
+                       codes, scales, found_inf, vec_ok);
   else
     hipLaunchKernelGGL((quant_kernel<RS_Q_INT8>), g, b, 0, s, table<QuantWork>(L, L->off_work),
-                       w0, table<TileDesc>(L, L->off_tiles), x, codes, scales, vec_ok);
+                       w0, table<TileDesc>(L, L->off_tiles), x, codes, scales, found_inf, vec_ok);
+  return after_launch(fn);
+}
+
+extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, rs_qfmt fmt,
+                                      const float* scales, void* y, rs_dtype y_dt, int32_t k0,
+                                      int32_t k1, void* stream) {
+  const char* fn = "rs_block_dequant";
+  RS_TRY(check_common(L, k0, k1, fn));
+  if (fmt != RS_Q_FP8_E4M3 && fmt != RS_Q_INT8)
+    return fail(RS_ERR_DTYPE, "rs_block_dequant: fmt must be RS_Q_FP8_E4M3 or RS_Q_INT8");
+  if (!float_kind(y_dt)) return fail(RS_ERR_DTYPE, "rs_block_dequant: y must be RS_F32 or RS_BF16");
+  RS_TRY(check_ptr(codes, 1, fn, "codes"));
+  RS_TRY(check_ptr(scales, 4, fn, "scales"));
+  RS_TRY(check_ptr(y, y_dt == RS_F32 ? 4 : 2, fn, "y"));
+  const uintptr_t ca = reinterpret_cast<uintptr_t>(codes), ya = reinterpret_cast<uintptr_t>(y);
+  int vec_ok = (ca % 4 == 0 && ya % (y_dt == RS_F32 ? 16 : 8) == 0) ? 1 : 0;
+  if (vec_ok && ca % 16 == 0) vec_ok = 2;
+  const int64_t w0 = L->rank_work[k0], nw = L->rank_work[k1] - w0;
+  if (nw == 0) return RS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 g(static_cast<unsigned>(nw)), b(kThreads);
+  const QuantWork* wk = table<QuantWork>(L, L->off_work);
+  const TileDesc* tl = table<TileDesc>(L, L->off_tiles);
+  if (fmt == RS_Q_FP8_E4M3 && y_dt == RS_F32)
+    hipLaunchKernelGGL((dequant_kernel<RS_Q_FP8_E4M3, 0>), g, b, 0, s, wk, w0, tl, codes, scales, y, vec_ok);
+  else if (fmt == RS_Q_FP8_E4M3)
+    hipLaunchKernelGGL((dequant_kernel<RS_Q_FP8_E4M3, 1>), g, b, 0, s, wk, w0, tl, codes, scales, y, vec_ok);
+  else if (y_dt == RS_F32)
+    hipLaunchKernelGGL((dequant_kernel<RS_Q_INT8, 0>), g, b, 0, s, wk, w0, tl, codes, scales, y, vec_ok);
+  else
+    hipLaunchKernelGGL((dequant_kernel<RS_Q_INT8, 1>), g, b, 0, s, wk, w0, tl, codes, scales, y, vec_ok);
+  return after_launch(fn);
+}
+
+extern "C" rs_status rs_adamw_step(const rs_layout* L, float* p, const float* g, float* m, float* v,
+                                   const rs_adamw_params* hp, const uint8_t* tensor_mask,
+                                   const uint32_t* found_inf, int32_t k0, int32_t k1,
+                                   void* stream) {
+  const char* fn = "rs_adamw_step";
+  RS_TRY(check_common(L, k0, k1, fn));
+  if (!hp) return fail(RS_ERR_INVALID_ARG, "rs_adamw_step: null hyperparameters");
+  RS_TRY(check_ptr(p, 4, fn, "p"));
+  RS_TRY(check_ptr(g, 4, fn, "g"));
+  RS_TRY(check_ptr(m, 4, fn, "m"));
+  RS_TRY(check_ptr(v, 4, fn, "v"));
+  if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
+  if (!(hp->bias_correction1 > 0.0f) || !(hp->bias_correction2 > 0.0f) || !(hp->grad_scale != 0.0f))
+    return fail(RS_ERR_INVALID_ARG, "rs_adamw_step: bias corrections must be > 0, grad_scale != 0");
+  AdamConst k;
+  k.beta1 = hp->beta1;
+  k.beta2 = hp->beta2;
+  k.omb1 = 1.0f - hp->beta1;
+  k.omb2 = 1.0f - hp->beta2;
+  k.eps = hp->eps;
+  const float lrwd = hp->lr * hp->weight_decay;
+  k.decay = 1.0f - lrwd;
+  k.step = hp->lr / hp->bias_correction1;
+  k.bc2s = std::sqrt(hp->bias_correction2);
+  k.inv = 1.0f / hp->grad_scale;
+  const int64_t c0 = L->rank_chunk[k0], nc = L->rank_chunk[k1] - c0;
+  if (nc == 0) return RS_OK;
+  hipLaunchKernelGGL(adamw_kernel, chunk_grid(nc), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), table<ChunkDesc>(L, L->off_chunks), c0, nc,
+                     p, g, m, v, k, tensor_mask, found_inf, L->m);
+  return after_launch(fn);
+}
+
+extern "C" rs_status rs_sgd_step(const rs_layout* L, float* p, const float* g, float* buf,
+                                 const rs_sgd_params* hp, const uint8_t* tensor_mask,
+                                 const uint32_t* found_inf, int32_t k0, int32_t k1, void* stream) {
+  const char* fn = "rs_sgd_step";
+  RS_TRY(check_common(L, k0, k1, fn));
+  if (!hp) return fail(RS_ERR_INVALID_ARG, "rs_sgd_step: null hyperparameters");
+  RS_TRY(check_ptr(p, 4, fn, "p"));
+  RS_TRY(check_ptr(g, 4, fn, "g"));
+  RS_TRY(check_ptr(buf, 4, fn, "buf"));
+  if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
+  if (!(hp->grad_scale != 0.0f)) return fail(RS_ERR_INVALID_ARG, "rs_sgd_step: grad_scale == 0");
+  SgdConst k;
+  k.lr = hp->lr;
+  k.mu = hp->momentum;
+  k.wd = hp->weight_decay;
+  k.inv = 1.0f / hp->grad_scale;
+  k.nesterov = hp->nesterov ? 1 : 0;
+  const int64_t c0 = L->rank_chunk[k0], nc = L->rank_chunk[k1] - c0;
+  if (nc == 0) return RS_OK;
+  hipLaunchKernelGGL(sgd_kernel, chunk_grid(nc), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), table<ChunkDesc>(L, L->off_chunks), c0, nc,
+                     p, g, buf, k, tensor_mask, found_inf, L->m);
   return after_launch(fn);
 }

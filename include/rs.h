@@ -228,9 +228,69 @@ rs_status rs_ragged_sqnorm(const rs_layout* layout, const float* x, double* sq, 
  *           padding and of tensors that are not quantised are not written
  *   scales  device fp32 [info.num_tiles]: tiles numbered tensor by tensor
  *           (quantised tensors only, in group order), row-major inside a
- *           tensor; only tiles in the range are written */
+ *           tensor; only tiles in the range are written
+ *   found_inf device uint32 [m] or NULL: found_inf[k] is set to 1 when a
+ *           quantised value read in rank k is not finite (the non-finite
+ *           check of the sharded gradient scaler, for grads quantised
+ *           before communication); never cleared by the call */
 rs_status rs_block_quant(const rs_layout* layout, const float* x, rs_qfmt fmt, uint8_t* codes,
-                         float* scales, int32_t k0, int32_t k1, void* stream);
+                         float* scales, uint32_t* found_inf, int32_t k0, int32_t k1, void* stream);
+
+/* rs_block_dequant - the inverse: y[p] = fl(decode(codes[p]) * scale) for
+ * every element of every tile in [k0*S, k1*S) (the dequantisation step of
+ * an 8-bit optimizer state; veScale-FSDP, section 6.3).  decode is exact:
+ * E4M3FN per OCP (codes 0x7F/0xFF give NaN), INT8 as a signed integer; the
+ * fp32 product is the one rounding (bf16 output: then rounded to nearest
+ * even).  Positions of padding and of tensors that are not quantised are not
+ * written.
+ *   codes   device uint8, m*S bytes (as written by rs_block_quant)
+ *   scales  device fp32 [info.num_tiles]
+ *   y       device, m*S elements of y_dt (RS_F32 or RS_BF16) */
+rs_status rs_block_dequant(const rs_layout* layout, const uint8_t* codes, rs_qfmt fmt,
+                           const float* scales, void* y, rs_dtype y_dt, int32_t k0, int32_t k1,
+                           void* stream);
+
+/* AdamW hyperparameters for one step (fp32).  bias_correction1/2 are
+ * 1 - beta1^t and 1 - beta2^t for step t, computed by the caller. */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  float bias_correction1, bias_correction2;
+  float grad_scale; /* grads are divided by it (1 = unscaled) */
+} rs_adamw_params;
+
+/* rs_adamw_step - one fused AdamW step over every fragment of the range, in
+ * place (the fused optimizer the pages run on the local shard; veScale
+ * 深度技术分析, OpDispatcher: fused AdamW/SGD handler).  Per element, fp32,
+ * each operation rounded once, IEEE sqrt and division:
+ *   g = grad / grad_scale   (as grad * fl(1/grad_scale))
+ *   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g)
+ *   p = p*(1 - lr*wd) - (lr/bc1) * (m / (sqrt(v)/sqrt(bc2) + eps))
+ * with 1-b1, 1-b2, 1-lr*wd, lr/bc1, sqrt(bc2), 1/grad_scale formed once in
+ * fp32.  Only tensor elements in [k0*S, k1*S) with tensor_mask[t] != 0 (all
+ * when NULL) change.  found_inf: device uint32 [m] or NULL; when any entry
+ * is non-zero nothing is written (the step is skipped).
+ *   p, g, m, v   device fp32, m*S elements each (buffer layout)
+ *   hp           host */
+rs_status rs_adamw_step(const rs_layout* layout, float* p, const float* g, float* m, float* v,
+                        const rs_adamw_params* hp, const uint8_t* tensor_mask,
+                        const uint32_t* found_inf, int32_t k0, int32_t k1, void* stream);
+
+/* SGD hyperparameters (fp32). */
+typedef struct {
+  float lr, momentum, weight_decay;
+  float grad_scale;
+  int32_t nesterov;
+} rs_sgd_params;
+
+/* rs_sgd_step - one fused SGD-with-momentum step, in place:
+ *   g = grad/grad_scale + wd*p;  b = mu*b + g;  d = nesterov ? g + mu*b : b;
+ *   p = p - lr*d
+ * (fp32, each operation rounded once; no dampening - a zeroed b makes the
+ * first step b = g).  Masks, rank range and found_inf as in rs_adamw_step.
+ *   p, g, buf    device fp32, m*S elements each */
+rs_status rs_sgd_step(const rs_layout* layout, float* p, const float* g, float* buf,
+                      const rs_sgd_params* hp, const uint8_t* tensor_mask,
+                      const uint32_t* found_inf, int32_t k0, int32_t k1, void* stream);
 
 /* Static description of a status code. */
 const char* rs_status_str(rs_status status);

@@ -9,3 +9,4 @@ import it.  It shares no code with the HIP path; both take inputs from the
 seeded generators in workloads.py.
 """
 from . import casts, ops, plan  # noqa: F401
+from . import optim  # noqa: F401,E402

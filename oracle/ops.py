@@ -271,3 +271,63 @@ def block_quant(x: np.ndarray, specs, offsets: Sequence[int], S: int, m: int, fm
 
 def num_tiles(specs) -> int:
     return sum(tile_counts(s)[0] * tile_counts(s)[1] for s in specs if s.q_rows > 0)
+
+
+def decode_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """Code -> fp32 value (exact): E4M3FN per the OCP definition (0x7F/0xFF
+    are NaN), INT8 as a signed integer."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if fmt == "fp8_e4m3":
+        return casts.e4m3fn_to_f64(c).astype(F32)
+    return c.view(np.int8).astype(F32)
+
+
+def block_dequant(codes: np.ndarray, scales: np.ndarray, specs, offsets: Sequence[int], S: int,
+                  m: int, fmt: str, k0: int, k1: int, y: np.ndarray, y_dtype: str,
+                  only_tiles=None) -> np.ndarray:
+    """Inverse of block_quant: y[p] = fl32(decode(codes[p]) * scale) for every
+    element of every quantised tile in ranks [k0, k1); y holds fp32 values
+    ("f32") or bf16 bit patterns ("bf16", the fp32 product rounded to
+    nearest even).  Other positions of y are kept.
+
+    This is the dequantisation step of an 8-bit optimizer's state
+    (veScale-FSDP: Flexible and High-Performance FSDP at Scale, section 6.3).
+    """
+    y = y.copy()
+    wanted = None if only_tiles is None else set(int(i) for i in only_tiles)
+    base = 0
+    for spec, l in zip(specs, offsets):
+        if spec.q_rows <= 0:
+            continue
+        ntr, ntc = tile_counts(spec)
+        count = ntr * ntc
+        locals_ = range(count) if wanted is None else sorted(i - base for i in wanted
+                                                                if base <= i < base + count)
+        for idx in locals_:
+            r0, r1, c0, c1 = tile_bounds(spec, idx)
+            first = l + r0 * spec.cols + c0
+            if not (k0 <= first // S < k1):
+                continue
+            pos = l + (np.arange(r0, r1)[:, None] * spec.cols + np.arange(c0, c1)[None, :])
+            with np.errstate(all="ignore"):
+                val = (decode_codes(codes[pos], fmt) * F32(scales[base + idx])).astype(F32)
+            y[pos] = casts.bf16_bits_from_f32(val) if y_dtype == "bf16" else val
+        base += count
+    return y
+
+
+def quant_found_inf(x: np.ndarray, specs, offsets: Sequence[int], S: int, m: int,
+                    k0: int, k1: int) -> np.ndarray:
+    """found_inf[k] = 1 when a quantised element read in rank k (k0 <= k < k1)
+    is not finite - the non-finite check of the sharded gradient scaler
+    applied to the values being quantised ("PyTorch FSDP", native mixed
+    precision section)."""
+    found = np.zeros(m, dtype=np.uint32)
+    for spec, l in zip(specs, offsets):
+        if spec.q_rows <= 0:
+            continue
+        for k in range(max(k0, l // S), min(k1, (l + spec.numel - 1) // S + 1)):
+            lo, hi = max(l, k * S), min(l + spec.numel, (k + 1) * S)
+            if lo < hi and not np.all(np.isfinite(x[lo:hi])):
+                found[k] = 1
+    return found

@@ -148,3 +148,42 @@ def assert_f32_equal_nan_class(got: np.ndarray, exp: np.ndarray, what: str, max_
         i = int(np.argmax(d))
         raise AssertionError(f"{what}: {int((d > max_ulp).sum())} values off by more than {max_ulp} ulp; "
                              f"worst {int(d[i])} ulp")
+
+
+# ------------------------------------------------------------ small cases
+
+def _moe_small():
+    w = W.moe_experts()
+    ts = list(w.tensors[:12]) + [w.tensors[-1]]
+    return W.scaled_workload(W.Workload("moe4", tuple(ts), m=16, qfmt="fp8_e4m3", block=128,
+                                        grad_dist="student_t3"), 8, 8)
+
+
+def _mixed_small():
+    w = W.ragged_mixed()
+    return W.scaled_workload(W.Workload("mixed2", w.tensors[:19], m=32, qfmt="int8", block=128,
+                                        nonfinite_frac=1e-3), 32, 16)
+
+
+SMALL = {
+    "toy": lambda: (W.toy_unit(), 16, 0),
+    "toy_a1_c64": lambda: (W.toy_unit(), 1, 64),
+    "ragged_a1_c64": lambda: (W.ragged_small(), 1, 64),
+    "ragged_a16_c256": lambda: (W.ragged_small(), 16, 256),
+    "llama8b_div16": lambda: (W.scaled_workload(W.llama8b_layer(), 16, 16), 16, 320),
+    "llama8b_div16_a1": lambda: (W.scaled_workload(W.llama8b_layer(), 16, 16), 1, 1024),
+    "mixed_div": lambda: (_mixed_small(), 16, 512),
+    "moe_div8": lambda: (_moe_small(), 16, 2048),
+    "llama70b_div32": lambda: (W.scaled_workload(W.llama70b_layer(), 32, 32), 16, 0),
+}
+
+_cases = {}
+
+
+def case(name) -> Case:
+    if name not in _cases:
+        w, A, ch = SMALL[name]()
+        _cases[name] = Case(w, A, ch)
+    return _cases[name]
+
+

@@ -141,7 +141,7 @@ def test_hot_calls_reject_before_launch():
     lib = _lib.lib()
     st = lib.rs_pack(h, 16, 0, 16, 1, 0, 1, None)
     assert st == -7 and "not uploaded" in R.rs_last_error()
-    st = lib.rs_block_quant(None, 16, 0, 16, 16, 0, 1, None)
+    st = lib.rs_block_quant(None, 16, 0, 16, 16, None, 0, 1, None)
     assert st == -1
     R.rs_layout_destroy(h)
     assert R.rs_status_str(-5) == "rank range out of bounds"

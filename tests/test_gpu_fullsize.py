@@ -152,6 +152,34 @@ def test_full_sqnorm(fx):
         del x
 
 
+@pytest.mark.timeout(600)
+def test_full_adamw(fx):
+    import torch
+    from oracle import optim as OP
+    R = fx.R
+    log(f"full adamw {fx.w.name}")
+    rng = np.random.default_rng(29)
+    m0 = (rng.standard_normal(fx.total) * 1e-4).astype(np.float32)
+    v0 = np.abs(rng.standard_normal(fx.total) * 1e-6).astype(np.float32)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1, bc1=1 - 0.9 ** 5,
+              bc2=1 - 0.95 ** 5, grad_scale=1.0)
+    p = torch.from_numpy(fx.param_host).cuda()
+    g = torch.from_numpy(fx.grad_host).cuda()
+    m = torch.from_numpy(m0).cuda()
+    v = torch.from_numpy(v0).cuda()
+    R.rs_adamw_step(fx.lay.handle, p, g, m, v, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["wd"],
+                    hp["bc1"], hp["bc2"], 1.0, None, None, 0, fx.m)
+    _sync()
+    ep, em, ev = fx.param_host.copy(), m0, v0
+    for k in range(fx.m):
+        OP.adamw_step(ep, fx.grad_host, em, ev, fx.items, fx.offsets, fx.S, fx.m, k, k + 1, hp,
+                      inplace=True)
+    assert_f32_equal_nan_class(to_np(p), ep, f"full adamw {fx.w.name} p")
+    assert_f32_equal_nan_class(to_np(m), em, f"full adamw {fx.w.name} m")
+    assert_f32_equal_nan_class(to_np(v), ev, f"full adamw {fx.w.name} v")
+    del p, g, m, v
+
+
 def _tile_sample(fx, rng, n_random):
     specs = fx.w.tensors
     nt = O.num_tiles(specs)
@@ -228,4 +256,12 @@ def test_full_block_quant(fx):
             if s.q_rows:
                 quantised[l:l + s.numel] = True
         assert np.all(gc_[~quantised] == 0xAB)
-        del x, codes
+        # dequantise the device codes back to fp32 and check the same tiles
+        y = torch.full((fx.total,), float("nan"), dtype=torch.float32, device="cuda")
+        R.rs_block_dequant(fx.lay.handle, codes, R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8,
+                           scales, y, R.RS_F32, 0, fx.m)
+        _sync()
+        ey = O.block_dequant(gc_, gs, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, 0, fx.m,
+                             np.zeros(fx.total, np.float32), "f32", only_tiles=tiles)
+        assert_f32_equal_nan_class(to_np(y)[pos], ey[pos], f"full dequant {fx.w.name} {src}")
+        del x, codes, y

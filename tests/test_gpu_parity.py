@@ -16,8 +16,8 @@ from oracle import casts as OC
 from oracle import ops as O
 from oracle import plan as P
 
-from harness import (GUARD, Case, assert_bits_equal, assert_f32_equal_nan_class, check_guards,
-                     from_np, guarded, log, to_np)
+from harness import (GUARD, SMALL, Case, assert_bits_equal, assert_f32_equal_nan_class, case,
+                     check_guards, from_np, guarded, log, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,41 +34,6 @@ def _gpu():
         pytest.skip("no GPU")
     import fsdp_sharded_buffer_amd  # noqa: F401  (fails loudly if librs.so is missing)
     yield
-
-
-def _moe_small():
-    w = W.moe_experts()
-    ts = list(w.tensors[:12]) + [w.tensors[-1]]
-    return W.scaled_workload(W.Workload("moe4", tuple(ts), m=16, qfmt="fp8_e4m3", block=128,
-                                        grad_dist="student_t3"), 8, 8)
-
-
-def _mixed_small():
-    w = W.ragged_mixed()
-    return W.scaled_workload(W.Workload("mixed2", w.tensors[:19], m=32, qfmt="int8", block=128,
-                                        nonfinite_frac=1e-3), 32, 16)
-
-
-SMALL = {
-    "toy": lambda: (W.toy_unit(), 16, 0),
-    "toy_a1_c64": lambda: (W.toy_unit(), 1, 64),
-    "ragged_a1_c64": lambda: (W.ragged_small(), 1, 64),
-    "ragged_a16_c256": lambda: (W.ragged_small(), 16, 256),
-    "llama8b_div16": lambda: (W.scaled_workload(W.llama8b_layer(), 16, 16), 16, 320),
-    "llama8b_div16_a1": lambda: (W.scaled_workload(W.llama8b_layer(), 16, 16), 1, 1024),
-    "mixed_div": lambda: (_mixed_small(), 16, 512),
-    "moe_div8": lambda: (_moe_small(), 16, 2048),
-    "llama70b_div32": lambda: (W.scaled_workload(W.llama70b_layer(), 32, 32), 16, 0),
-}
-
-_cases = {}
-
-
-def case(name) -> Case:
-    if name not in _cases:
-        w, A, ch = SMALL[name]()
-        _cases[name] = Case(w, A, ch)
-    return _cases[name]
 
 
 def _sync():
@@ -426,3 +391,79 @@ def test_rank_range_errors():
     with pytest.raises(R.RsError) as e:   # fp32 data at an odd byte address
         R.rs_group_zero(c.lay.handle, x.view(torch.uint8)[1:].data_ptr(), R.RS_F32, None, 0, 1)
     assert e.value.status == -3
+
+
+# --------------------------------------------------------------- dequant
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "int8"])
+def test_block_dequant(name, fmt):
+    import torch
+    c = case(name)
+    R = c.R
+    nt = c.lay.info["num_tiles"]
+    x0 = c.flat(c.inputs().grads, fill=np.float32(np.nan))
+    codes0, scales0 = O.block_quant(x0, c.w.tensors, c.offsets, c.S, c.m, fmt, 0, c.m,
+                                    np.zeros(c.total, np.uint8), np.zeros(max(nt, 1), np.float32))
+    dc, ds = from_np(codes0), from_np(scales0)
+    qf = R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8
+    for yk in ("f32", "bf16"):
+        ydt = torch.bfloat16 if yk == "bf16" else torch.float32
+        canary = BF16_CANARY if yk == "bf16" else F32_CANARY
+        for k0, k1 in c.ranges():
+            log(f"dequant {name} {fmt} {yk} [{k0},{k1})")
+            yw, y = guarded(c.total, ydt, canary)
+            R.rs_block_dequant(c.lay.handle, dc, qf, ds, y, R.RS_BF16 if yk == "bf16" else R.RS_F32, k0, k1)
+            _sync()
+            init = np.full(c.total, canary, dtype=np.uint16 if yk == "bf16" else np.uint32)
+            if yk == "f32":
+                init = init.view(np.float32)
+            exp = O.block_dequant(codes0, scales0, c.w.tensors, c.offsets, c.S, c.m, fmt, k0, k1,
+                                  init, yk)
+            got = to_np(y)
+            what = f"dequant {name} {fmt} {yk} [{k0},{k1})"
+            if yk == "f32":
+                assert_f32_equal_nan_class(got, exp, what)
+            else:
+                gn = (got & 0x7FFF) > 0x7F80
+                en = (exp & 0x7FFF) > 0x7F80
+                assert np.array_equal(gn, en), what + " NaN"
+                assert_bits_equal(np.where(gn, 0, got), np.where(en, 0, exp), what)
+            check_guards(yw, canary, what)
+
+
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "int8"])
+def test_block_dequant_all_codes(fmt):
+    import torch
+    c = case("toy")
+    R = c.R
+    nt = c.lay.info["num_tiles"]
+    rng = np.random.default_rng(41)
+    codes = rng.integers(0, 256, size=c.total).astype(np.uint8)
+    codes[c.offsets[0]:c.offsets[0] + 256] = np.arange(256, dtype=np.uint8)
+    scales = (2.0 ** rng.uniform(-20, 20, size=nt)).astype(np.float32)
+    scales[0] = 1.0
+    y = torch.empty(c.total, dtype=torch.float32, device="cuda")
+    R.rs_block_dequant(c.lay.handle, from_np(codes), R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8,
+                       from_np(scales), y, R.RS_F32, 0, c.m)
+    _sync()
+    exp = O.block_dequant(codes, scales, c.w.tensors, c.offsets, c.S, c.m, fmt, 0, c.m,
+                          np.zeros(c.total, np.float32), "f32")
+    assert_f32_equal_nan_class(to_np(y), exp, f"dequant all codes {fmt}")
+
+
+def test_block_quant_found_inf():
+    import torch
+    c = case("mixed_div")
+    R = c.R
+    nt = c.lay.info["num_tiles"]
+    x0 = c.flat(c.inputs().grads)
+    ef = O.quant_found_inf(x0, c.w.tensors, c.offsets, c.S, c.m, 0, c.m)
+    assert ef.any()
+    fi = torch.zeros(c.m, dtype=torch.int32, device="cuda")
+    codes = torch.empty(c.total, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(nt, dtype=torch.float32, device="cuda")
+    R.rs_block_quant(c.lay.handle, from_np(x0), R.RS_Q_INT8, codes, scales, 0, c.m, found_inf=fi)
+    _sync()
+    assert np.array_equal(to_np(fi).astype(np.uint32), ef)

@@ -271,3 +271,74 @@ def test_block_quant_straddle_rejected():
     with pytest.raises(ValueError):
         O.block_quant(x, ts, p.offsets, p.S, 3, "int8", 0, 3,
                       np.zeros(p.total, np.uint8), np.zeros(2, np.float32))
+
+
+def test_decode_codes_against_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    dec = O.decode_codes(codes, "fp8_e4m3")
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(dec), nan)
+    assert np.array_equal(dec[~nan], ref[~nan])
+    dec = O.decode_codes(codes, "int8")
+    assert np.array_equal(dec, codes.view(np.int8).astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "int8"])
+def test_dequant_roundtrip_error_bound(fmt):
+    """|dequant(quant(x)) - x| <= scale * (half a code step at q + half an fp32
+    ulp of q) + half an fp32 ulp of the result."""
+    w = _ragged_group()
+    items, p = _setup(w, 1)
+    x = (np.random.default_rng(31).standard_normal(p.total) * 0.02).astype(np.float32)
+    nt = O.num_tiles(w.tensors)
+    codes, scales = O.block_quant(x, w.tensors, p.offsets, p.S, w.m, fmt, 0, w.m,
+                                  np.zeros(p.total, np.uint8), np.zeros(nt, np.float32))
+    y = O.block_dequant(codes, scales, w.tensors, p.offsets, p.S, w.m, fmt, 0, w.m,
+                        np.full(p.total, np.nan, np.float32), "f32")
+    base = 0
+    for s, l in zip(w.tensors, p.offsets):
+        if not s.q_rows:
+            continue
+        for (r0, r1, c0, c1) in O.tile_grid(s.rows, s.cols, s.q_rows, s.q_cols):
+            pos = l + (np.arange(r0, r1)[:, None] * s.cols + np.arange(c0, c1)[None, :])
+            sc = np.float64(scales[base])
+            q = np.abs(x[pos].astype(np.float64)) / sc
+            if fmt == "fp8_e4m3":
+                step = np.where(q < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(q, 2.0 ** -6))) - 3))
+            else:
+                step = np.ones_like(q)
+            ulp32 = np.spacing(np.abs(x[pos]).astype(np.float32)).astype(np.float64)
+            bound = sc * (step / 2 + np.spacing(q.astype(np.float32)).astype(np.float64) / 2) + ulp32
+            assert np.all(np.abs(y[pos].astype(np.float64) - x[pos]) <= bound * 1.000001)
+            base += 1
+    # positions outside quantised tiles untouched
+    v = p.offsets[1]
+    assert np.all(np.isnan(y[v:v + 37]))
+
+
+def test_dequant_bf16_and_special_scales():
+    codes = np.array([0x38, 0xB8, 0x7F, 0x00, 0x80, 0x01], np.uint8)  # 1, -1, NaN, 0, -0, 2^-9
+    ts = (W.TensorSpec("a", 2, 3, 2, 2, 3),)
+    items = P.items_from_specs(ts)
+    p = P.plan(items, 1, 1)
+    y = O.block_dequant(codes, np.array([3.0], np.float32), ts, p.offsets, p.S, 1, "fp8_e4m3",
+                        0, 1, np.zeros(6, np.float32), "f32")
+    assert y[0] == 3.0 and y[1] == -3.0 and np.isnan(y[2]) and y[3] == 0.0
+    assert np.signbit(y[4]) and y[5] == np.float32(3.0 * 2.0 ** -9)
+    yb = O.block_dequant(codes, np.array([1.0 / 3.0], np.float32), ts, p.offsets, p.S, 1,
+                         "fp8_e4m3", 0, 1, np.zeros(6, np.uint16), "bf16")
+    ref = torch.tensor([1 / 3, -1 / 3], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(yb[:2], ref)
+
+
+def test_quant_found_inf():
+    w = _ragged_group()
+    items, p = _setup(w, 1)
+    x = np.ones(p.total, np.float32)
+    l = p.offsets[3]        # row-granular tensor "e"
+    x[l + 7] = np.inf
+    v = p.offsets[1]        # the vector is not quantised: ignored
+    x[v + 2] = np.nan
+    f = O.quant_found_inf(x, w.tensors, p.offsets, p.S, w.m, 0, w.m)
+    assert f.tolist() == [1 if k == (l + 7) // p.S else 0 for k in range(w.m)]
