@@ -61,6 +61,8 @@ def extra_bytes(w, S, n_tiles):
         "block_dequant": Eq + 4 * n_tiles + 4 * Eq,   # codes + scales in, fp32 out
         "adamw_step": 28 * E,    # p, g, m, v in; p, m, v out (fp32)
         "sgd_step": 20 * E,      # p, g, buf in; p, buf out (fp32)
+        "adamw8_step": 8 * Eq + 2 * Eq + 4 * Eq + 2 * Eq + 16 * n_tiles,  # p,g in; 2 codes in;
+                                                                          # p out; 2 codes out
     }
 
 
@@ -186,6 +188,8 @@ def main():
     nbytes = op_bytes(w, S, lay.info["num_tiles"])
     deq = torch.empty(total, dtype=torch.float32, device=dev)
     mom = torch.zeros(total, dtype=torch.float32, device=dev)
+    codes2 = torch.zeros(total, dtype=torch.uint8, device=dev)
+    scales2 = torch.ones(lay.info["num_tiles"], dtype=torch.float32, device=dev)
     var = torch.zeros(total, dtype=torch.float32, device=dev)
     extra = {
         "block_dequant": lambda: R.rs_block_dequant(h, codes, qfmt, scales, deq, R.RS_F32, 0, m, sp),
@@ -193,6 +197,9 @@ def main():
                                               0.5, 0.1, 1.0, None, None, 0, m, sp),
         "sgd_step": lambda: R.rs_sgd_step(h, deq, acc, mom, 1e-4, 0.9, 0.0, False, 1.0, None, None,
                                           0, m, sp),
+        "adamw8_step": lambda: R.rs_adamw8_step(h, deq, acc, codes, scales, codes2, scales2, qfmt,
+                                                1e-4, 0.9, 0.95, 1e-8, 0.1, 0.5, 0.1, 1.0, None, 0,
+                                                m, sp),
     }
     xbytes = extra_bytes(w, S, lay.info["num_tiles"])
 

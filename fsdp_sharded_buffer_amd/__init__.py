@@ -24,7 +24,8 @@ __all__ = [
     "RS_F32", "RS_BF16", "RS_U8", "RS_Q_FP8_E4M3", "RS_Q_INT8", "RsError",
     "rs_plan", "rs_layout_create", "rs_layout_get_info", "rs_layout_upload",
     "rs_layout_destroy", "rs_pack", "rs_unpack", "rs_group_scale_add", "rs_group_zero",
-    "rs_ragged_sqnorm", "rs_block_quant", "rs_block_dequant", "rs_adamw_step", "rs_sgd_step",
+    "rs_ragged_sqnorm", "rs_block_quant", "rs_block_dequant", "rs_adamw_step", "rs_adamw8_step",
+    "rs_sgd_step",
     "rs_status_str", "rs_last_error",
     "Layout", "ptr_table", "dtype_code", "specs_array",
 ]
@@ -135,6 +136,17 @@ def rs_adamw_step(layout, p, g, m, v, lr: float, beta1: float, beta2: float, eps
                          grad_scale)
     check(lib().rs_adamw_step(layout, _ptr(p), _ptr(g), _ptr(m), _ptr(v), byref(hp),
                               _ptr(tensor_mask), _ptr(found_inf), k0, k1, _stream(stream)))
+
+
+def rs_adamw8_step(layout, p, g, m_codes, m_scales, v_codes, v_scales, fmt: int, lr: float,
+                   beta1: float, beta2: float, eps: float, weight_decay: float,
+                   bias_correction1: float, bias_correction2: float, grad_scale: float = 1.0,
+                   found_inf=None, k0: int = 0, k1: int = 1, stream=None) -> None:
+    hp = rs_adamw_params(lr, beta1, beta2, eps, weight_decay, bias_correction1, bias_correction2,
+                         grad_scale)
+    check(lib().rs_adamw8_step(layout, _ptr(p), _ptr(g), _ptr(m_codes), _ptr(m_scales),
+                               _ptr(v_codes), _ptr(v_scales), fmt, byref(hp), _ptr(found_inf),
+                               k0, k1, _stream(stream)))
 
 
 def rs_sgd_step(layout, p, g, buf, lr: float, momentum: float, weight_decay: float,

@@ -70,6 +70,9 @@ SIGNATURES = {
     "rs_adamw_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 POINTER(rs_adamw_params), c_void_p, c_void_p, c_int32, c_int32,
                                 c_void_p]),
+    "rs_adamw8_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_int32, POINTER(rs_adamw_params), c_void_p, c_int32,
+                                 c_int32, c_void_p]),
     "rs_sgd_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(rs_sgd_params),
                               c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
     "rs_status_str": (c_char_p, [c_int32]),

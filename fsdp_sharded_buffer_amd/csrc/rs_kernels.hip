@@ -93,6 +93,12 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #ifndef RS_DEQ_LDS
 #define RS_DEQ_LDS 1
 #endif
+#ifndef RS_ADAM8_LOADS
+#define RS_ADAM8_LOADS 1
+#endif
+#ifndef RS_ADAM8_BATCH
+#define RS_ADAM8_BATCH 2
+#endif
 
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -868,18 +874,33 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(
     const int n = c.len;
     const bool vec = aligned16(pp) && aligned16(gp) && aligned16(mp) && aligned16(vp);
     const int nv = vec ? n / 4 : 0;
-    for (int q = threadIdx.x; q < nv; q += kThreads) {
-      u32x4 P = ld16<false>(pp + 4 * q), G = ld16<false>(gp + 4 * q);
-      u32x4 M = ld16<false>(mp + 4 * q), V = ld16<false>(vp + 4 * q);
-      float a[4] = {f32(P.x), f32(P.y), f32(P.z), f32(P.w)};
-      float b[4] = {f32(M.x), f32(M.y), f32(M.z), f32(M.w)};
-      float d[4] = {f32(V.x), f32(V.y), f32(V.z), f32(V.w)};
-      const float e[4] = {f32(G.x), f32(G.y), f32(G.z), f32(G.w)};
+    for (int q0 = threadIdx.x; q0 < nv; q0 += kUnroll * kThreads) {
+      u32x4 P[kUnroll], G[kUnroll], M[kUnroll], V[kUnroll];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) adamw1(a[j], e[j], b[j], d[j], k);
-      st16<false>(pp + 4 * q, u32x4{u32(a[0]), u32(a[1]), u32(a[2]), u32(a[3])});
-      st16<false>(mp + 4 * q, u32x4{u32(b[0]), u32(b[1]), u32(b[2]), u32(b[3])});
-      st16<false>(vp + 4 * q, u32x4{u32(d[0]), u32(d[1]), u32(d[2]), u32(d[3])});
+      for (int u = 0; u < kUnroll; ++u) {
+        const int q = q0 + u * kThreads;
+        if (q < nv) {
+          P[u] = ld16<false>(pp + 4 * q);
+          G[u] = ld16<false>(gp + 4 * q);
+          M[u] = ld16<false>(mp + 4 * q);
+          V[u] = ld16<false>(vp + 4 * q);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int q = q0 + u * kThreads;
+        if (q < nv) {
+          float a[4] = {f32(P[u].x), f32(P[u].y), f32(P[u].z), f32(P[u].w)};
+          float b[4] = {f32(M[u].x), f32(M[u].y), f32(M[u].z), f32(M[u].w)};
+          float d[4] = {f32(V[u].x), f32(V[u].y), f32(V[u].z), f32(V[u].w)};
+          const float e[4] = {f32(G[u].x), f32(G[u].y), f32(G[u].z), f32(G[u].w)};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) adamw1(a[j], e[j], b[j], d[j], k);
+          st16<false>(pp + 4 * q, u32x4{u32(a[0]), u32(a[1]), u32(a[2]), u32(a[3])});
+          st16<false>(mp + 4 * q, u32x4{u32(b[0]), u32(b[1]), u32(b[2]), u32(b[3])});
+          st16<false>(vp + 4 * q, u32x4{u32(d[0]), u32(d[1]), u32(d[2]), u32(d[3])});
+        }
+      }
     }
     for (int e = nv * 4 + threadIdx.x; e < n; e += kThreads) {
       float a = pp[e], b = mp[e], d = vp[e];
@@ -918,21 +939,283 @@ __global__ __launch_bounds__(kThreads) void sgd_kernel(
     const int n = c.len;
     const bool vec = aligned16(pp) && aligned16(gp) && aligned16(bp);
     const int nv = vec ? n / 4 : 0;
-    for (int q = threadIdx.x; q < nv; q += kThreads) {
-      u32x4 P = ld16<false>(pp + 4 * q), G = ld16<false>(gp + 4 * q), B = ld16<false>(bp + 4 * q);
-      float a[4] = {f32(P.x), f32(P.y), f32(P.z), f32(P.w)};
-      float b[4] = {f32(B.x), f32(B.y), f32(B.z), f32(B.w)};
-      const float e[4] = {f32(G.x), f32(G.y), f32(G.z), f32(G.w)};
+    for (int q0 = threadIdx.x; q0 < nv; q0 += kUnroll * kThreads) {
+      u32x4 P[kUnroll], G[kUnroll], B[kUnroll];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sgd1(a[j], e[j], b[j], k);
-      st16<false>(pp + 4 * q, u32x4{u32(a[0]), u32(a[1]), u32(a[2]), u32(a[3])});
-      st16<false>(bp + 4 * q, u32x4{u32(b[0]), u32(b[1]), u32(b[2]), u32(b[3])});
+      for (int u = 0; u < kUnroll; ++u) {
+        const int q = q0 + u * kThreads;
+        if (q < nv) {
+          P[u] = ld16<false>(pp + 4 * q);
+          G[u] = ld16<false>(gp + 4 * q);
+          B[u] = ld16<false>(bp + 4 * q);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int q = q0 + u * kThreads;
+        if (q < nv) {
+          float a[4] = {f32(P[u].x), f32(P[u].y), f32(P[u].z), f32(P[u].w)};
+          float b[4] = {f32(B[u].x), f32(B[u].y), f32(B[u].z), f32(B[u].w)};
+          const float e[4] = {f32(G[u].x), f32(G[u].y), f32(G[u].z), f32(G[u].w)};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sgd1(a[j], e[j], b[j], k);
+          st16<false>(pp + 4 * q, u32x4{u32(a[0]), u32(a[1]), u32(a[2]), u32(a[3])});
+          st16<false>(bp + 4 * q, u32x4{u32(b[0]), u32(b[1]), u32(b[2]), u32(b[3])});
+        }
+      }
     }
     for (int e = nv * 4 + threadIdx.x; e < n; e += kThreads) {
       float a = pp[e], b = bp[e];
       sgd1(a, gp[e], b, k);
       pp[e] = a;
       bp[e] = b;
+    }
+  }
+}
+
+// 8-bit AdamW: the moments of every quantised tensor are block-quantised
+// (codes + one fp32 scale per tile, the layout's tile table).  Per tile:
+// dequantise m and v, the AdamW update in fp32, requantise m' and v' with
+// their new absmax scales.  Phase 1 computes m' and v' only for their
+// absmax; phase 2 re-reads g and the old codes (cache resident), recomputes
+// m' and v' bit-identically, updates p and encodes with the reciprocal fast
+// path; slots that need the exact quotient are redone in phase 3 from the
+// codes, which are still the old ones there.  Keeping m' and v' out of
+// registers between the phases keeps occupancy up.
+
+template <int FMT>
+__device__ __forceinline__ void moments4(u32x4 G, uint32_t cm, uint32_t cv, float sm, float sv,
+                                         const AdamConst& k, float* M, float* V) {
+  float dm[4], dv[4];
+  decode4<FMT>(cm, dm);
+  decode4<FMT>(cv, dv);
+  const float gs[4] = {f32(G.x), f32(G.y), f32(G.z), f32(G.w)};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float mo = dm[j] * sm;
+    const float vo = dv[j] * sv;
+    const float gg = gs[j] * k.inv;
+    M[j] = k.beta1 * mo + k.omb1 * gg;
+    V[j] = k.beta2 * vo + k.omb2 * (gg * gg);
+  }
+}
+
+__device__ __forceinline__ uint32_t absmax4(const float* a, uint32_t acc) {
+  return max(acc, max(max(u32(a[0]) & 0x7fffffffu, u32(a[1]) & 0x7fffffffu),
+                      max(u32(a[2]) & 0x7fffffffu, u32(a[3]) & 0x7fffffffu)));
+}
+
+// Fast encode of four values with a normal, finite scale; safe = false when
+// any of them needs the exact quotient.
+template <int FMT>
+__device__ __forceinline__ uint32_t fast_encode4(const float* a, float rcp, bool& safe) {
+  float q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = a[j] * rcp;
+  if constexpr (FMT == RS_Q_FP8_E4M3) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) safe = safe && e4m3_safe(u32(q[j]));
+    return e4m3_pack4_normal(q[0], q[1], q[2], q[3]);
+  } else {
+    float r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r[j] = __builtin_rintf(q[j]);
+      safe = safe && int8_safe(q[j], r[j]);
+    }
+    return int8_from_rint(r[0]) | (int8_from_rint(r[1]) << 8) | (int8_from_rint(r[2]) << 16) |
+           (int8_from_rint(r[3]) << 24);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t exact_encode4(const float* a, float scale, bool zero_tile,
+                                                  bool nan_tile) {
+  return encode_exact<FMT>(a[0], scale, zero_tile, nan_tile) |
+         (encode_exact<FMT>(a[1], scale, zero_tile, nan_tile) << 8) |
+         (encode_exact<FMT>(a[2], scale, zero_tile, nan_tile) << 16) |
+         (encode_exact<FMT>(a[3], scale, zero_tile, nan_tile) << 24);
+}
+
+struct TileScale {
+  float scale, rcp;
+  bool fast, zero_tile, nan_tile;
+  __device__ __forceinline__ TileScale(uint32_t amax, float Q) {
+    scale = __uint_as_float(amax) / Q;
+    nan_tile = amax > 0x7f800000u;
+    if (nan_tile) scale = __uint_as_float(0x7fc00000u);
+    zero_tile = scale == 0.0f;
+    rcp = 1.0f / scale;
+    const uint32_t sb = __float_as_uint(scale);
+    fast = sb >= 0x00800000u && sb < 0x7f800000u;
+  }
+};
+
+__device__ __forceinline__ float adam_p(float p, float m2, float v2, const AdamConst& k) {
+  const float den = sqrtf(v2) / k.bc2s + k.eps;
+  return p * k.decay - k.step * (m2 / den);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void adamw8_kernel(
+    const QuantWork* __restrict__ work, int64_t w0, const TileDesc* __restrict__ tiles,
+    float* __restrict__ p, const float* __restrict__ g, uint8_t* __restrict__ mc,
+    float* __restrict__ ms, uint8_t* __restrict__ vc, float* __restrict__ vs, AdamConst k,
+    const uint32_t* __restrict__ found_inf, int m_ranks, int vec_ok) {
+  __shared__ uint32_t lds[2][kThreads / kWave];
+  if (skip_step(found_inf, m_ranks)) return;
+  const QuantWork w = work[w0 + blockIdx.x];
+  const bool vec = w.vec && vec_ok;
+  const int team = w.team;
+  const int slot = threadIdx.x / team;
+  const int lane = threadIdx.x % team;
+  const bool active = slot < w.count;
+  const TileDesc td = tiles[w.tile_begin + (active ? slot : 0)];
+  const int64_t o0 = td.buf_off;
+  const float sm_old = ms[td.scale_idx], sv_old = vs[td.scale_idx];
+  const int c4 = td.cols >> 2;
+  const int nf = active ? td.rows * c4 : 0;
+  const int ne = active ? td.rows * td.cols : 0;
+  uint32_t am = 0, av = 0;
+  if (vec) {
+    // RS_ADAM8_LOADS slots' g and codes are loaded before their moments
+    constexpr int NL = RS_ADAM8_LOADS;
+    SlotWalk sw(lane, team, c4, int(td.ld));
+#pragma unroll
+    for (int b = 0; b < 16; b += NL) {
+      u32x4 G[NL];
+      uint32_t CM[NL], CV[NL];
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        if (lane + (b + u) * team < nf) {
+          const int64_t o = o0 + sw.off;
+          G[u] = ld16<false>(g + o);
+          CM[u] = *reinterpret_cast<const uint32_t*>(mc + o);
+          CV[u] = *reinterpret_cast<const uint32_t*>(vc + o);
+        }
+        sw.next();
+      }
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        if (lane + (b + u) * team < nf) {
+          float M[4], V[4];
+          moments4<FMT>(G[u], CM[u], CV[u], sm_old, sv_old, k, M, V);
+          am = absmax4(M, am);
+          av = absmax4(V, av);
+        }
+      }
+    }
+  } else {
+    for (int e = lane; e < ne; e += team) {
+      const int r = e / td.cols;
+      const int64_t o = o0 + int64_t(r) * td.ld + (e - r * td.cols);
+      float m1[4], v1[4];
+      moments4<FMT>(u32x4{u32(g[o]), 0u, 0u, 0u}, mc[o], vc[o], sm_old, sv_old, k, m1, v1);
+      am = max(am, u32(m1[0]) & 0x7fffffffu);
+      av = max(av, u32(v1[0]) & 0x7fffffffu);
+    }
+  }
+  const int red = team < kWave ? team : kWave;
+  for (int o = red / 2; o >= 1; o >>= 1) {
+    am = max(am, uint32_t(__shfl_xor(int(am), o)));
+    av = max(av, uint32_t(__shfl_xor(int(av), o)));
+  }
+  if (team > kWave) {  // uniform
+    if (threadIdx.x % kWave == 0) {
+      lds[0][threadIdx.x / kWave] = am;
+      lds[1][threadIdx.x / kWave] = av;
+    }
+    __syncthreads();
+    const int first = (threadIdx.x / team) * (team / kWave);
+    uint32_t a = lds[0][first], b = lds[1][first];
+    for (int i = 1; i < team / kWave; ++i) {
+      a = max(a, lds[0][first + i]);
+      b = max(b, lds[1][first + i]);
+    }
+    am = a;
+    av = b;
+  }
+  if (!active) return;
+  constexpr float Q = FMT == RS_Q_FP8_E4M3 ? 448.0f : 127.0f;
+  const TileScale tm(am, Q), tv(av, Q);
+  if (lane == 0) {
+    ms[td.scale_idx] = tm.scale;
+    vs[td.scale_idx] = tv.scale;
+  }
+  if (!vec) {
+    for (int e = lane; e < ne; e += team) {
+      const int r = e / td.cols;
+      const int64_t o = o0 + int64_t(r) * td.ld + (e - r * td.cols);
+      float m1[4], v1[4];
+      moments4<FMT>(u32x4{u32(g[o]), 0u, 0u, 0u}, mc[o], vc[o], sm_old, sv_old, k, m1, v1);
+      p[o] = adam_p(p[o], m1[0], v1[0], k);
+      mc[o] = uint8_t(encode_exact<FMT>(m1[0], tm.scale, tm.zero_tile, tm.nan_tile));
+      vc[o] = uint8_t(encode_exact<FMT>(v1[0], tv.scale, tv.zero_tile, tv.nan_tile));
+    }
+    return;
+  }
+  uint32_t slow = 0;
+  {
+    // g, the old codes and p of RS_ADAM8_BATCH slots are loaded ahead of
+    // that batch's stores (p and the codes are rewritten in place)
+    constexpr int NB = RS_ADAM8_BATCH;
+    SlotWalk sw(lane, team, c4, int(td.ld));
+#pragma unroll
+    for (int b = 0; b < 16; b += NB) {
+      u32x4 P[NB], G[NB];
+      uint32_t CM[NB], CV[NB];
+      int o[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        o[u] = sw.off;
+        if (lane + (b + u) * team < nf) {
+          const int64_t q = o0 + o[u];
+          P[u] = ld16<false>(p + q);
+          G[u] = ld16<false>(g + q);
+          CM[u] = *reinterpret_cast<const uint32_t*>(mc + q);
+          CV[u] = *reinterpret_cast<const uint32_t*>(vc + q);
+        }
+        sw.next();
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int i = b + u;
+        if (lane + i * team < nf) {
+          const int64_t q = o0 + o[u];
+          float M[4], V[4];
+          moments4<FMT>(G[u], CM[u], CV[u], sm_old, sv_old, k, M, V);
+          u32x4 out;
+          out.x = u32(adam_p(f32(P[u].x), M[0], V[0], k));
+          out.y = u32(adam_p(f32(P[u].y), M[1], V[1], k));
+          out.z = u32(adam_p(f32(P[u].z), M[2], V[2], k));
+          out.w = u32(adam_p(f32(P[u].w), M[3], V[3], k));
+          st16<false>(p + q, out);
+          bool safe = tm.fast && tv.fast;
+          const uint32_t wm = fast_encode4<FMT>(M, tm.rcp, safe);
+          const uint32_t wv = fast_encode4<FMT>(V, tv.rcp, safe);
+          if (safe) {
+            *reinterpret_cast<uint32_t*>(mc + q) = wm;
+            *reinterpret_cast<uint32_t*>(vc + q) = wv;
+          } else {
+            slow |= 1u << i;
+          }
+        }
+      }
+    }
+  }
+  if (slow) {  // rare: recompute the slot's moments from the old codes and divide
+    SlotWalk sw(lane, team, c4, int(td.ld));
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+      if (slow & (1u << i)) {
+        const int64_t o = o0 + sw.off;
+        float m4[4], v4[4];
+        moments4<FMT>(ld16<false>(g + o), *reinterpret_cast<const uint32_t*>(mc + o),
+                      *reinterpret_cast<const uint32_t*>(vc + o), sm_old, sv_old, k, m4, v4);
+        *reinterpret_cast<uint32_t*>(mc + o) = exact_encode4<FMT>(m4, tm.scale, tm.zero_tile, tm.nan_tile);
+        *reinterpret_cast<uint32_t*>(vc + o) = exact_encode4<FMT>(v4, tv.scale, tv.zero_tile, tv.nan_tile);
+      }
+      sw.next();
     }
   }
 }
@@ -1221,5 +1504,54 @@ extern "C" rs_status rs_sgd_step(const rs_layout* L, float* p, const float* g, f
   hipLaunchKernelGGL(sgd_kernel, chunk_grid(nc), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), table<ChunkDesc>(L, L->off_chunks), c0, nc,
                      p, g, buf, k, tensor_mask, found_inf, L->m);
+  return after_launch(fn);
+}
+
+extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g, uint8_t* m_codes,
+                                    float* m_scales, uint8_t* v_codes, float* v_scales,
+                                    rs_qfmt fmt, const rs_adamw_params* hp,
+                                    const uint32_t* found_inf, int32_t k0, int32_t k1,
+                                    void* stream) {
+  const char* fn = "rs_adamw8_step";
+  RS_TRY(check_common(L, k0, k1, fn));
+  if (!hp) return fail(RS_ERR_INVALID_ARG, "rs_adamw8_step: null hyperparameters");
+  if (fmt != RS_Q_FP8_E4M3 && fmt != RS_Q_INT8)
+    return fail(RS_ERR_DTYPE, "rs_adamw8_step: fmt must be RS_Q_FP8_E4M3 or RS_Q_INT8");
+  RS_TRY(check_ptr(p, 4, fn, "p"));
+  RS_TRY(check_ptr(g, 4, fn, "g"));
+  RS_TRY(check_ptr(m_codes, 1, fn, "m_codes"));
+  RS_TRY(check_ptr(v_codes, 1, fn, "v_codes"));
+  RS_TRY(check_ptr(m_scales, 4, fn, "m_scales"));
+  RS_TRY(check_ptr(v_scales, 4, fn, "v_scales"));
+  if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
+  if (!(hp->bias_correction1 > 0.0f) || !(hp->bias_correction2 > 0.0f) || !(hp->grad_scale != 0.0f))
+    return fail(RS_ERR_INVALID_ARG, "rs_adamw8_step: bias corrections must be > 0, grad_scale != 0");
+  AdamConst k;
+  k.beta1 = hp->beta1;
+  k.beta2 = hp->beta2;
+  k.omb1 = 1.0f - hp->beta1;
+  k.omb2 = 1.0f - hp->beta2;
+  k.eps = hp->eps;
+  const float lrwd = hp->lr * hp->weight_decay;
+  k.decay = 1.0f - lrwd;
+  k.step = hp->lr / hp->bias_correction1;
+  k.bc2s = std::sqrt(hp->bias_correction2);
+  k.inv = 1.0f / hp->grad_scale;
+  const int vec_ok = (reinterpret_cast<uintptr_t>(p) % 16 == 0 &&
+                      reinterpret_cast<uintptr_t>(g) % 16 == 0 &&
+                      reinterpret_cast<uintptr_t>(m_codes) % 4 == 0 &&
+                      reinterpret_cast<uintptr_t>(v_codes) % 4 == 0) ? 1 : 0;
+  const int64_t w0 = L->rank_work[k0], nw = L->rank_work[k1] - w0;
+  if (nw == 0) return RS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 gr(static_cast<unsigned>(nw)), b(kThreads);
+  const QuantWork* wk = table<QuantWork>(L, L->off_work);
+  const TileDesc* tl = table<TileDesc>(L, L->off_tiles);
+  if (fmt == RS_Q_FP8_E4M3)
+    hipLaunchKernelGGL((adamw8_kernel<RS_Q_FP8_E4M3>), gr, b, 0, s, wk, w0, tl, p, g, m_codes,
+                       m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
+  else
+    hipLaunchKernelGGL((adamw8_kernel<RS_Q_INT8>), gr, b, 0, s, wk, w0, tl, p, g, m_codes,
+                       m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
   return after_launch(fn);
 }

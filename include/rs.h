@@ -275,6 +275,24 @@ rs_status rs_adamw_step(const rs_layout* layout, float* p, const float* g, float
                         const rs_adamw_params* hp, const uint8_t* tensor_mask,
                         const uint32_t* found_inf, int32_t k0, int32_t k1, void* stream);
 
+/* rs_adamw8_step - AdamW with block-quantised moments (8-bit Adam;
+ * veScale-FSDP, section 6.3: block-wise INT8 optimizer states, quantised
+ * per shard without communication).  For every tile of every quantised
+ * tensor in [k0*S, k1*S):
+ *   m = fl(decode(m code) * m scale), v likewise (as rs_block_dequant);
+ *   the AdamW update of rs_adamw_step on (p, g, m, v);
+ *   m', v' re-quantised with new absmax scales (as rs_block_quant).
+ * Tensors that are not quantised are not touched (step their fp32 moments
+ * with rs_adamw_step and a tensor mask).  found_inf as in rs_adamw_step.
+ *   p, g               device fp32, m*S elements (buffer layout)
+ *   m_codes, v_codes   device uint8, m*S bytes, in place
+ *   m_scales, v_scales device fp32 [info.num_tiles], in place
+ *   fmt                RS_Q_INT8 or RS_Q_FP8_E4M3 */
+rs_status rs_adamw8_step(const rs_layout* layout, float* p, const float* g, uint8_t* m_codes,
+                         float* m_scales, uint8_t* v_codes, float* v_scales, rs_qfmt fmt,
+                         const rs_adamw_params* hp, const uint32_t* found_inf, int32_t k0,
+                         int32_t k1, void* stream);
+
 /* SGD hyperparameters (fp32). */
 typedef struct {
   float lr, momentum, weight_decay;

@@ -102,3 +102,49 @@ def sgd_step(p, g, b, items: Sequence[Item], offsets, S, m_ranks, k0, k1, lr, mo
             p[lo:hi] = (p[lo:hi] - F32(lr * d)).astype(F32)
             b[lo:hi] = b2
     return p, b
+
+
+def adamw8_step(p, g, m_codes, m_scales, v_codes, v_scales, specs, offsets, S, m_ranks, k0, k1,
+                fmt: str, hp: dict, found_inf=None, only_tiles=None):
+    """AdamW with block-quantised moments (8-bit Adam, veScale-FSDP section
+    6.3): for every tile of every quantised tensor in ranks [k0, k1):
+
+        m = dequant(m codes, m scale);  v = dequant(v codes, v scale)
+        (p, m', v') = the AdamW update above, in fp32
+        m codes, m scale = block_quant(m');  v codes, v scale = block_quant(v')
+
+    Non-quantised tensors are not touched (their fp32 moments are stepped
+    with adamw_step).  Returns new (p, m_codes, m_scales, v_codes, v_scales).
+    """
+    from . import ops as O
+
+    p = p.copy()
+    m_codes, v_codes = m_codes.copy(), v_codes.copy()
+    m_scales, v_scales = m_scales.copy(), v_scales.copy()
+    if _skip(found_inf):
+        return p, m_codes, m_scales, v_codes, v_scales
+    k = adamw_constants(**hp)
+    wanted = None if only_tiles is None else set(int(i) for i in only_tiles)
+    base = 0
+    for spec, l in zip(specs, offsets):
+        if spec.q_rows <= 0:
+            continue
+        ntr, ntc = O.tile_counts(spec)
+        count = ntr * ntc
+        locals_ = range(count) if wanted is None else sorted(i - base for i in wanted
+                                                                if base <= i < base + count)
+        for idx in locals_:
+            r0, r1, c0, c1 = O.tile_bounds(spec, idx)
+            if not (k0 <= (l + r0 * spec.cols + c0) // S < k1):
+                continue
+            pos = l + (np.arange(r0, r1)[:, None] * spec.cols + np.arange(c0, c1)[None, :])
+            t = base + idx
+            with np.errstate(all="ignore"):
+                mo = (O.decode_codes(m_codes[pos], fmt) * F32(m_scales[t])).astype(F32)
+                vo = (O.decode_codes(v_codes[pos], fmt) * F32(v_scales[t])).astype(F32)
+            p2, m2, v2 = adamw_elem(p[pos], g[pos], mo, vo, k)
+            p[pos] = p2
+            m_scales[t], m_codes[pos] = O.quant_tile(m2, fmt)
+            v_scales[t], v_codes[pos] = O.quant_tile(v2, fmt)
+        base += count
+    return p, m_codes, m_scales, v_codes, v_scales

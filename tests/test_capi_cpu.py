@@ -22,7 +22,7 @@ from fsdp_sharded_buffer_amd import _lib  # noqa: E402
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(rs_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(rs_[a-z_0-9]+)\s*\(", txt)))
 
 
 def test_library_exports_every_declared_symbol():

@@ -118,3 +118,42 @@ def test_sgd(name, nesterov):
         assert_f32_equal_nan_class(to_np(b), eb, what + " buf")
         for wh in (pw, gw, bw):
             check_guards(wh, F32_CANARY, what)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("fmt", ["int8", "fp8_e4m3"])
+def test_adamw8(name, fmt):
+    import torch
+    from oracle import ops as O
+    c = case(name)
+    R = c.R
+    nt = c.lay.info["num_tiles"]
+    p0, g0, m0, v0 = _state(c, 6)
+    mc0, ms0 = O.block_quant(m0, c.w.tensors, c.offsets, c.S, c.m, fmt, 0, c.m,
+                             np.zeros(c.total, np.uint8), np.zeros(max(nt, 1), np.float32))
+    vc0, vs0 = O.block_quant(v0, c.w.tensors, c.offsets, c.S, c.m, fmt, 0, c.m,
+                             np.zeros(c.total, np.uint8), np.zeros(max(nt, 1), np.float32))
+    hp = HP[0]
+    qf = R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8
+    for step in range(2):          # two steps in a row: the second reads requantised states
+        for k0, k1 in c.ranges()[:3]:
+            if step == 1 and (k0, k1) != (0, c.m):
+                continue
+            log(f"adamw8 {name} {fmt} step{step} [{k0},{k1})")
+            p, g = from_np(p0), from_np(g0)
+            mc, ms, vc, vs = from_np(mc0), from_np(ms0), from_np(vc0), from_np(vs0)
+            for _ in range(step + 1):
+                R.rs_adamw8_step(c.lay.handle, p, g, mc, ms, vc, vs, qf, hp["lr"], hp["beta1"],
+                                 hp["beta2"], hp["eps"], hp["wd"], hp["bc1"], hp["bc2"], hp["grad_scale"],
+                                 None, k0, k1)
+            _sync()
+            e = (p0, mc0, ms0, vc0, vs0)
+            for _ in range(step + 1):
+                e = OP.adamw8_step(e[0], g0, e[1], e[2], e[3], e[4], c.w.tensors, c.offsets, c.S, c.m,
+                                   k0, k1, fmt, hp)
+            what = f"adamw8 {name} {fmt} step{step} [{k0},{k1})"
+            assert_f32_equal_nan_class(to_np(p), e[0], what + " p")
+            assert np.array_equal(to_np(mc), e[1]), what + " m codes"
+            assert np.array_equal(to_np(ms).view(np.uint32), e[2].view(np.uint32)), what + " m scales"
+            assert np.array_equal(to_np(vc), e[3]), what + " v codes"
+            assert np.array_equal(to_np(vs).view(np.uint32), e[4].view(np.uint32)), what + " v scales"

@@ -122,3 +122,41 @@ def test_sgd_matches_torch(nesterov):
         opt.step()
         np.testing.assert_allclose(p2[sl], tp.detach().numpy(), rtol=1e-6, atol=1e-10)
         np.testing.assert_allclose(b2[sl], opt.state[tp]["momentum_buffer"].numpy(), rtol=1e-6, atol=1e-10)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8_e4m3"])
+def test_adamw8_composes_pinned_parts(fmt):
+    """8-bit Adam = dequantise, the fp32 AdamW update, requantise: each part
+    is pinned on its own; check the composition, the untouched vector and
+    the found_inf skip."""
+    from oracle import ops as O
+    w, items, pl = _setup()
+    p, g, m, v = _bufs(pl.total, 11)
+    nt = O.num_tiles(w.tensors)
+    mc, ms = O.block_quant(m, w.tensors, pl.offsets, pl.S, w.m, fmt, 0, w.m,
+                           np.zeros(pl.total, np.uint8), np.zeros(nt, np.float32))
+    vc, vs = O.block_quant(v, w.tensors, pl.offsets, pl.S, w.m, fmt, 0, w.m,
+                           np.zeros(pl.total, np.uint8), np.zeros(nt, np.float32))
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1, bc1=0.5, bc2=0.2, grad_scale=1.0)
+    p2, mc2, ms2, vc2, vs2 = OP.adamw8_step(p, g, mc, ms, vc, vs, w.tensors, pl.offsets, pl.S, w.m,
+                                            0, w.m, fmt, hp)
+    md = O.block_dequant(mc, ms, w.tensors, pl.offsets, pl.S, w.m, fmt, 0, w.m, m.copy(), "f32")
+    vd = O.block_dequant(vc, vs, w.tensors, pl.offsets, pl.S, w.m, fmt, 0, w.m, v.copy(), "f32")
+    ep, em, ev = OP.adamw_step(p, g, md, vd, items, pl.offsets, pl.S, w.m, 0, w.m, hp)
+    quantised = np.zeros(pl.total, bool)
+    for s, l in zip(w.tensors, pl.offsets):
+        if s.q_rows:
+            quantised[l:l + s.numel] = True
+    assert np.array_equal(p2[quantised], ep[quantised])
+    assert np.array_equal(p2[~quantised], p[~quantised])        # vector untouched
+    emc, ems = O.block_quant(em, w.tensors, pl.offsets, pl.S, w.m, fmt, 0, w.m,
+                             np.zeros(pl.total, np.uint8), np.zeros(nt, np.float32))
+    assert np.array_equal(mc2[quantised], emc[quantised]) and np.array_equal(ms2, ems)
+    evc, evs = O.block_quant(ev, w.tensors, pl.offsets, pl.S, w.m, fmt, 0, w.m,
+                             np.zeros(pl.total, np.uint8), np.zeros(nt, np.float32))
+    assert np.array_equal(vc2[quantised], evc[quantised]) and np.array_equal(vs2, evs)
+    # found_inf skips everything
+    out = OP.adamw8_step(p, g, mc, ms, vc, vs, w.tensors, pl.offsets, pl.S, w.m, 0, w.m, fmt, hp,
+                         found_inf=np.ones(w.m, np.uint32))
+    for a, b in zip(out, (p, mc, ms, vc, vs)):
+        assert np.array_equal(a, b)
