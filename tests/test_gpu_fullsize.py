@@ -236,19 +236,7 @@ def test_full_block_quant(fx):
                                         only_tiles=tiles)
         gc_, gs = to_np(codes), to_np(scales)
         assert_bits_equal(gs[tiles], escales[tiles], f"full quant {fx.w.name} {src} scales")
-        # positions of the sampled tiles
-        pos = []
-        base = 0
-        want = set(tiles)
-        for s, l in zip(fx.w.tensors, fx.offsets):
-            if not s.q_rows:
-                continue
-            ntr, ntc = O.tile_counts(s)
-            for i in [t - base for t in tiles if base <= t < base + ntr * ntc]:
-                r0, r1, c0, c1 = O.tile_bounds(s, i)
-                pos.append((l + np.arange(r0, r1)[:, None] * s.cols + np.arange(c0, c1)[None, :]).reshape(-1))
-            base += ntr * ntc
-        pos = np.concatenate(pos)
+        pos = _tile_positions(fx, tiles)
         assert_bits_equal(gc_[pos], ecodes[pos], f"full quant {fx.w.name} {src} codes")
         # padding and non-quantised positions keep the canary
         quantised = np.zeros(fx.total, bool)
@@ -265,3 +253,76 @@ def test_full_block_quant(fx):
                              np.zeros(fx.total, np.float32), "f32", only_tiles=tiles)
         assert_f32_equal_nan_class(to_np(y)[pos], ey[pos], f"full dequant {fx.w.name} {src}")
         del x, codes, y
+
+
+def _tile_positions(fx, tiles):
+    pos = []
+    base = 0
+    for s, l in zip(fx.w.tensors, fx.offsets):
+        if not s.q_rows:
+            continue
+        ntr, ntc = O.tile_counts(s)
+        for i in [t - base for t in tiles if base <= t < base + ntr * ntc]:
+            r0, r1, c0, c1 = O.tile_bounds(s, i)
+            pos.append((l + np.arange(r0, r1)[:, None] * s.cols + np.arange(c0, c1)[None, :]).reshape(-1))
+        base += ntr * ntc
+    return np.concatenate(pos)
+
+
+def _random_codes(rng, n, fmt, signed):
+    """Seeded valid codes: INT8 in [-127, 127] (or [0, 127]); E4M3FN without
+    the NaN codes (and without the sign bit when unsigned)."""
+    if fmt == "int8":
+        lo = -127 if signed else 0
+        return rng.integers(lo, 128, size=n, dtype=np.int16).astype(np.int8).view(np.uint8)
+    c = rng.integers(0, 0x7F, size=n, dtype=np.uint8)          # 0x00..0x7E
+    if signed:
+        c |= (rng.integers(0, 2, size=n, dtype=np.uint8) << 7)
+    return c
+
+
+@pytest.mark.timeout(900)
+def test_full_adamw8(fx):
+    """8-bit AdamW over the whole buffer in one launch; compared on sampled
+    tiles (every tile of the 8B layer), non-quantised elements untouched."""
+    import torch
+    from oracle import optim as OP
+    R = fx.R
+    log(f"full adamw8 {fx.w.name}")
+    rng = np.random.default_rng(31)
+    fmt = fx.w.qfmt
+    nt = fx.lay.info["num_tiles"]
+    qmax = 448.0 if fmt == "fp8_e4m3" else 127.0
+    mc0 = _random_codes(rng, fx.total, fmt, True)
+    vc0 = _random_codes(rng, fx.total, fmt, False)
+    ms0 = (np.abs(rng.standard_normal(nt)) * 1e-4 / qmax).astype(np.float32)
+    vs0 = (np.abs(rng.standard_normal(nt)) * 1e-6 / qmax).astype(np.float32)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1, bc1=1 - 0.9 ** 5,
+              bc2=1 - 0.95 ** 5, grad_scale=1.0)
+    p = torch.from_numpy(fx.param_host).cuda()
+    g = torch.from_numpy(fx.grad_host).cuda()
+    mc, vc = torch.from_numpy(mc0).cuda(), torch.from_numpy(vc0).cuda()
+    ms, vs = torch.from_numpy(ms0).cuda(), torch.from_numpy(vs0).cuda()
+    qf = R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8
+    R.rs_adamw8_step(fx.lay.handle, p, g, mc, ms, vc, vs, qf, hp["lr"], hp["beta1"], hp["beta2"],
+                     hp["eps"], hp["wd"], hp["bc1"], hp["bc2"], hp["grad_scale"], None, 0, fx.m)
+    _sync()
+    tiles = list(range(nt)) if nt <= 20000 else _tile_sample(fx, rng, 2000)
+    ep, emc, ems, evc, evs = OP.adamw8_step(fx.param_host, fx.grad_host, mc0, ms0, vc0, vs0,
+                                            fx.w.tensors, fx.offsets, fx.S, fx.m, 0, fx.m, fmt, hp,
+                                            only_tiles=tiles)
+    pos = _tile_positions(fx, tiles)
+    what = f"full adamw8 {fx.w.name}"
+    gp = to_np(p)
+    assert_f32_equal_nan_class(gp[pos], ep[pos], what + " p")
+    assert_bits_equal(to_np(mc)[pos], emc[pos], what + " m codes")
+    assert_bits_equal(to_np(vc)[pos], evc[pos], what + " v codes")
+    assert_bits_equal(to_np(ms)[tiles], ems[tiles], what + " m scales")
+    assert_bits_equal(to_np(vs)[tiles], evs[tiles], what + " v scales")
+    quantised = np.zeros(fx.total, bool)
+    for s, l in zip(fx.w.tensors, fx.offsets):
+        if s.q_rows:
+            quantised[l:l + s.numel] = True
+    assert np.array_equal(gp[~quantised].view(np.uint32), fx.param_host[~quantised].view(np.uint32))
+    assert np.array_equal(to_np(mc)[~quantised], mc0[~quantised])
+    del p, g, mc, vc, ms, vs
