@@ -93,11 +93,19 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #ifndef RS_DEQ_LDS
 #define RS_DEQ_LDS 1
 #endif
-#ifndef RS_ADAM8_LOADS
-#define RS_ADAM8_LOADS 1
+#ifndef RS_ADAM8_F
+#define RS_ADAM8_F 2
 #endif
 #ifndef RS_ADAM8_BATCH
-#define RS_ADAM8_BATCH 2
+#define RS_ADAM8_BATCH 1
+#endif
+#ifndef RS_ADAM8_NT
+#define RS_ADAM8_NT 1
+#endif
+#ifdef RS_ADAM8_WPE
+#define RS_ADAM8_ATTR __attribute__((amdgpu_waves_per_eu(RS_ADAM8_WPE)))
+#else
+#define RS_ADAM8_ATTR
 #endif
 
 
@@ -844,7 +852,7 @@ struct AdamConst {
 __device__ __forceinline__ bool skip_step(const uint32_t* found_inf, int m) {
   int hit = 0;
   if (found_inf)
-    for (int i = threadIdx.x; i < m; i += kThreads) hit |= found_inf[i] != 0u;
+    for (int i = threadIdx.x; i < m; i += blockDim.x) hit |= found_inf[i] != 0u;
   return __syncthreads_or(hit) != 0;
 }
 
@@ -976,12 +984,14 @@ __global__ __launch_bounds__(kThreads) void sgd_kernel(
 // 8-bit AdamW: the moments of every quantised tensor are block-quantised
 // (codes + one fp32 scale per tile, the layout's tile table).  Per tile:
 // dequantise m and v, the AdamW update in fp32, requantise m' and v' with
-// their new absmax scales.  Phase 1 computes m' and v' only for their
-// absmax; phase 2 re-reads g and the old codes (cache resident), recomputes
-// m' and v' bit-identically, updates p and encodes with the reciprocal fast
-// path; slots that need the exact quotient are redone in phase 3 from the
-// codes, which are still the old ones there.  Keeping m' and v' out of
-// registers between the phases keeps occupancy up.
+// their new absmax scales.  A work item (the quantisation kernel's: `count`
+// tiles of `team` lanes, at most 16 four-element slots per lane) is spread
+// over F sub-blocks of kThreads threads, each taking 16/F of the slots, so a
+// lane keeps its m' and v' in registers between the absmax pass and the
+// encode pass (every input is read once) at a modest register count.  The
+// first pass also writes p', which does not depend on the new scales, so
+// the pass after the absmax reduction only encodes and stores codes.  Slots
+// whose encode needs the exact quotient are redone from the same registers.
 
 template <int FMT>
 __device__ __forceinline__ void moments4(u32x4 G, uint32_t cm, uint32_t cv, float sm, float sv,
@@ -1056,19 +1066,23 @@ __device__ __forceinline__ float adam_p(float p, float m2, float v2, const AdamC
   return p * k.decay - k.step * (m2 / den);
 }
 
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void adamw8_kernel(
+template <int FMT, int F>
+__global__ __launch_bounds__(kThreads* F) RS_ADAM8_ATTR void adamw8_kernel(
     const QuantWork* __restrict__ work, int64_t w0, const TileDesc* __restrict__ tiles,
     float* __restrict__ p, const float* __restrict__ g, uint8_t* __restrict__ mc,
     float* __restrict__ ms, uint8_t* __restrict__ vc, float* __restrict__ vs, AdamConst k,
     const uint32_t* __restrict__ found_inf, int m_ranks, int vec_ok) {
-  __shared__ uint32_t lds[2][kThreads / kWave];
+  constexpr int NS = 16 / F;  // slots per lane
+  __shared__ uint32_t ldw[2][kThreads * F / kWave];
+  __shared__ uint32_t ldt[2][F][kThreads];
   if (skip_step(found_inf, m_ranks)) return;
   const QuantWork w = work[w0 + blockIdx.x];
   const bool vec = w.vec && vec_ok;
   const int team = w.team;
-  const int slot = threadIdx.x / team;
-  const int lane = threadIdx.x % team;
+  const int sub = threadIdx.x / kThreads;
+  const int tt = threadIdx.x % kThreads;
+  const int slot = tt / team;
+  const int lane = tt % team;
   const bool active = slot < w.count;
   const TileDesc td = tiles[w.tile_begin + (active ? slot : 0)];
   const int64_t o0 = td.buf_off;
@@ -1076,102 +1090,26 @@ __global__ __launch_bounds__(kThreads) void adamw8_kernel(
   const int c4 = td.cols >> 2;
   const int nf = active ? td.rows * c4 : 0;
   const int ne = active ? td.rows * td.cols : 0;
+  const int s0 = sub * NS;  // first slot of this sub-block
   uint32_t am = 0, av = 0;
+  float M[NS][4], V[NS][4];
   if (vec) {
-    // RS_ADAM8_LOADS slots' g and codes are loaded before their moments
-    constexpr int NL = RS_ADAM8_LOADS;
-    SlotWalk sw(lane, team, c4, int(td.ld));
+    // p' needs m' and v' only, not the new scales: it is written here, so
+    // the encode pass after the absmax reduction touches no input
+    constexpr int NB = RS_ADAM8_BATCH < NS ? RS_ADAM8_BATCH : NS;
+    SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
 #pragma unroll
-    for (int b = 0; b < 16; b += NL) {
-      u32x4 G[NL];
-      uint32_t CM[NL], CV[NL];
-#pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        if (lane + (b + u) * team < nf) {
-          const int64_t o = o0 + sw.off;
-          G[u] = ld16<false>(g + o);
-          CM[u] = *reinterpret_cast<const uint32_t*>(mc + o);
-          CV[u] = *reinterpret_cast<const uint32_t*>(vc + o);
-        }
-        sw.next();
-      }
-#pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        if (lane + (b + u) * team < nf) {
-          float M[4], V[4];
-          moments4<FMT>(G[u], CM[u], CV[u], sm_old, sv_old, k, M, V);
-          am = absmax4(M, am);
-          av = absmax4(V, av);
-        }
-      }
-    }
-  } else {
-    for (int e = lane; e < ne; e += team) {
-      const int r = e / td.cols;
-      const int64_t o = o0 + int64_t(r) * td.ld + (e - r * td.cols);
-      float m1[4], v1[4];
-      moments4<FMT>(u32x4{u32(g[o]), 0u, 0u, 0u}, mc[o], vc[o], sm_old, sv_old, k, m1, v1);
-      am = max(am, u32(m1[0]) & 0x7fffffffu);
-      av = max(av, u32(v1[0]) & 0x7fffffffu);
-    }
-  }
-  const int red = team < kWave ? team : kWave;
-  for (int o = red / 2; o >= 1; o >>= 1) {
-    am = max(am, uint32_t(__shfl_xor(int(am), o)));
-    av = max(av, uint32_t(__shfl_xor(int(av), o)));
-  }
-  if (team > kWave) {  // uniform
-    if (threadIdx.x % kWave == 0) {
-      lds[0][threadIdx.x / kWave] = am;
-      lds[1][threadIdx.x / kWave] = av;
-    }
-    __syncthreads();
-    const int first = (threadIdx.x / team) * (team / kWave);
-    uint32_t a = lds[0][first], b = lds[1][first];
-    for (int i = 1; i < team / kWave; ++i) {
-      a = max(a, lds[0][first + i]);
-      b = max(b, lds[1][first + i]);
-    }
-    am = a;
-    av = b;
-  }
-  if (!active) return;
-  constexpr float Q = FMT == RS_Q_FP8_E4M3 ? 448.0f : 127.0f;
-  const TileScale tm(am, Q), tv(av, Q);
-  if (lane == 0) {
-    ms[td.scale_idx] = tm.scale;
-    vs[td.scale_idx] = tv.scale;
-  }
-  if (!vec) {
-    for (int e = lane; e < ne; e += team) {
-      const int r = e / td.cols;
-      const int64_t o = o0 + int64_t(r) * td.ld + (e - r * td.cols);
-      float m1[4], v1[4];
-      moments4<FMT>(u32x4{u32(g[o]), 0u, 0u, 0u}, mc[o], vc[o], sm_old, sv_old, k, m1, v1);
-      p[o] = adam_p(p[o], m1[0], v1[0], k);
-      mc[o] = uint8_t(encode_exact<FMT>(m1[0], tm.scale, tm.zero_tile, tm.nan_tile));
-      vc[o] = uint8_t(encode_exact<FMT>(v1[0], tv.scale, tv.zero_tile, tv.nan_tile));
-    }
-    return;
-  }
-  uint32_t slow = 0;
-  {
-    // g, the old codes and p of RS_ADAM8_BATCH slots are loaded ahead of
-    // that batch's stores (p and the codes are rewritten in place)
-    constexpr int NB = RS_ADAM8_BATCH;
-    SlotWalk sw(lane, team, c4, int(td.ld));
-#pragma unroll
-    for (int b = 0; b < 16; b += NB) {
+    for (int b = 0; b < NS; b += NB) {
       u32x4 P[NB], G[NB];
       uint32_t CM[NB], CV[NB];
       int o[NB];
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         o[u] = sw.off;
-        if (lane + (b + u) * team < nf) {
+        if (lane + (s0 + b + u) * team < nf) {
           const int64_t q = o0 + o[u];
-          P[u] = ld16<false>(p + q);
-          G[u] = ld16<false>(g + q);
+          G[u] = ld16<RS_ADAM8_NT>(g + q);
+          P[u] = ld16<RS_ADAM8_NT>(p + q);
           CM[u] = *reinterpret_cast<const uint32_t*>(mc + q);
           CV[u] = *reinterpret_cast<const uint32_t*>(vc + q);
         }
@@ -1180,40 +1118,109 @@ __global__ __launch_bounds__(kThreads) void adamw8_kernel(
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const int i = b + u;
-        if (lane + i * team < nf) {
-          const int64_t q = o0 + o[u];
-          float M[4], V[4];
-          moments4<FMT>(G[u], CM[u], CV[u], sm_old, sv_old, k, M, V);
+        if (lane + (s0 + i) * team < nf) {
+          moments4<FMT>(G[u], CM[u], CV[u], sm_old, sv_old, k, M[i], V[i]);
+          am = absmax4(M[i], am);
+          av = absmax4(V[i], av);
           u32x4 out;
-          out.x = u32(adam_p(f32(P[u].x), M[0], V[0], k));
-          out.y = u32(adam_p(f32(P[u].y), M[1], V[1], k));
-          out.z = u32(adam_p(f32(P[u].z), M[2], V[2], k));
-          out.w = u32(adam_p(f32(P[u].w), M[3], V[3], k));
-          st16<false>(p + q, out);
-          bool safe = tm.fast && tv.fast;
-          const uint32_t wm = fast_encode4<FMT>(M, tm.rcp, safe);
-          const uint32_t wv = fast_encode4<FMT>(V, tv.rcp, safe);
-          if (safe) {
-            *reinterpret_cast<uint32_t*>(mc + q) = wm;
-            *reinterpret_cast<uint32_t*>(vc + q) = wv;
-          } else {
-            slow |= 1u << i;
-          }
+          out.x = u32(adam_p(f32(P[u].x), M[i][0], V[i][0], k));
+          out.y = u32(adam_p(f32(P[u].y), M[i][1], V[i][1], k));
+          out.z = u32(adam_p(f32(P[u].z), M[i][2], V[i][2], k));
+          out.w = u32(adam_p(f32(P[u].w), M[i][3], V[i][3], k));
+          st16<RS_ADAM8_NT>(p + o0 + o[u], out);
         }
       }
     }
+  } else {
+    for (int e = lane + sub * team; e < ne; e += team * F) {
+      const int r = e / td.cols;
+      const int64_t o = o0 + int64_t(r) * td.ld + (e - r * td.cols);
+      float m1[4], v1[4];
+      moments4<FMT>(u32x4{u32(g[o]), 0u, 0u, 0u}, mc[o], vc[o], sm_old, sv_old, k, m1, v1);
+      am = max(am, u32(m1[0]) & 0x7fffffffu);
+      av = max(av, u32(v1[0]) & 0x7fffffffu);
+      p[o] = adam_p(p[o], m1[0], v1[0], k);
+    }
   }
-  if (slow) {  // rare: recompute the slot's moments from the old codes and divide
-    SlotWalk sw(lane, team, c4, int(td.ld));
-#pragma unroll 1
-    for (int i = 0; i < 16; ++i) {
+  const int red = team < kWave ? team : kWave;
+  for (int o = red / 2; o >= 1; o >>= 1) {
+    am = max(am, uint32_t(__shfl_xor(int(am), o)));
+    av = max(av, uint32_t(__shfl_xor(int(av), o)));
+  }
+  if (team > kWave) {  // uniform: combine the waves of a tile within a sub-block
+    if (threadIdx.x % kWave == 0) {
+      ldw[0][threadIdx.x / kWave] = am;
+      ldw[1][threadIdx.x / kWave] = av;
+    }
+    __syncthreads();
+    const int first = sub * (kThreads / kWave) + (tt / team) * (team / kWave);
+    uint32_t a = ldw[0][first], b = ldw[1][first];
+    for (int i = 1; i < team / kWave; ++i) {
+      a = max(a, ldw[0][first + i]);
+      b = max(b, ldw[1][first + i]);
+    }
+    am = a;
+    av = b;
+  }
+  if constexpr (F > 1) {  // combine the sub-blocks
+    ldt[0][sub][tt] = am;
+    ldt[1][sub][tt] = av;
+    __syncthreads();
+    am = ldt[0][0][tt];
+    av = ldt[1][0][tt];
+#pragma unroll
+    for (int j = 1; j < F; ++j) {
+      am = max(am, ldt[0][j][tt]);
+      av = max(av, ldt[1][j][tt]);
+    }
+  }
+  if (!active) return;
+  constexpr float Q = FMT == RS_Q_FP8_E4M3 ? 448.0f : 127.0f;
+  const TileScale tm(am, Q), tv(av, Q);
+  if (lane == 0 && sub == 0) {
+    ms[td.scale_idx] = tm.scale;
+    vs[td.scale_idx] = tv.scale;
+  }
+  if (!vec) {
+    // every element's old codes are read and rewritten by one thread only
+    for (int e = lane + sub * team; e < ne; e += team * F) {
+      const int r = e / td.cols;
+      const int64_t o = o0 + int64_t(r) * td.ld + (e - r * td.cols);
+      float m1[4], v1[4];
+      moments4<FMT>(u32x4{u32(g[o]), 0u, 0u, 0u}, mc[o], vc[o], sm_old, sv_old, k, m1, v1);
+      mc[o] = uint8_t(encode_exact<FMT>(m1[0], tm.scale, tm.zero_tile, tm.nan_tile));
+      vc[o] = uint8_t(encode_exact<FMT>(v1[0], tv.scale, tv.zero_tile, tv.nan_tile));
+    }
+    return;
+  }
+  uint32_t slow = 0;
+  {
+    SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (lane + (s0 + i) * team < nf) {
+        const int64_t q = o0 + sw.off;
+        bool safe = tm.fast && tv.fast;
+        const uint32_t wm = fast_encode4<FMT>(M[i], tm.rcp, safe);
+        const uint32_t wv = fast_encode4<FMT>(V[i], tv.rcp, safe);
+        if (safe) {
+          *reinterpret_cast<uint32_t*>(mc + q) = wm;
+          *reinterpret_cast<uint32_t*>(vc + q) = wv;
+        } else {
+          slow |= 1u << i;
+        }
+      }
+      sw.next();
+    }
+  }
+  if (slow) {  // rare: exact division for the slots that need it
+    SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
       if (slow & (1u << i)) {
         const int64_t o = o0 + sw.off;
-        float m4[4], v4[4];
-        moments4<FMT>(ld16<false>(g + o), *reinterpret_cast<const uint32_t*>(mc + o),
-                      *reinterpret_cast<const uint32_t*>(vc + o), sm_old, sv_old, k, m4, v4);
-        *reinterpret_cast<uint32_t*>(mc + o) = exact_encode4<FMT>(m4, tm.scale, tm.zero_tile, tm.nan_tile);
-        *reinterpret_cast<uint32_t*>(vc + o) = exact_encode4<FMT>(v4, tv.scale, tv.zero_tile, tv.nan_tile);
+        *reinterpret_cast<uint32_t*>(mc + o) = exact_encode4<FMT>(M[i], tm.scale, tm.zero_tile, tm.nan_tile);
+        *reinterpret_cast<uint32_t*>(vc + o) = exact_encode4<FMT>(V[i], tv.scale, tv.zero_tile, tv.nan_tile);
       }
       sw.next();
     }
@@ -1544,14 +1551,14 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
   const int64_t w0 = L->rank_work[k0], nw = L->rank_work[k1] - w0;
   if (nw == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 gr(static_cast<unsigned>(nw)), b(kThreads);
+  const dim3 gr(static_cast<unsigned>(nw)), b(kThreads * RS_ADAM8_F);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
   const TileDesc* tl = table<TileDesc>(L, L->off_tiles);
   if (fmt == RS_Q_FP8_E4M3)
-    hipLaunchKernelGGL((adamw8_kernel<RS_Q_FP8_E4M3>), gr, b, 0, s, wk, w0, tl, p, g, m_codes,
-                       m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
+    hipLaunchKernelGGL((adamw8_kernel<RS_Q_FP8_E4M3, RS_ADAM8_F>), gr, b, 0, s, wk, w0, tl, p, g,
+                       m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
   else
-    hipLaunchKernelGGL((adamw8_kernel<RS_Q_INT8>), gr, b, 0, s, wk, w0, tl, p, g, m_codes,
-                       m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
+    hipLaunchKernelGGL((adamw8_kernel<RS_Q_INT8, RS_ADAM8_F>), gr, b, 0, s, wk, w0, tl, p, g,
+                       m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
   return after_launch(fn);
 }
