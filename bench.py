@@ -121,6 +121,58 @@ def cpu_baseline(w, offs, S, inp, k1, min_seconds=10.0):
                       f"six operations in {dt:.1f} s, numpy on one host core"}
 
 
+STUDY_MS = (8, 16, 32, 64, 128, 256, 512, 1024)
+STUDY_ROWS = (1, 16, 128)
+
+
+def padding_study(align: int, out_path: str = "") -> None:
+    """Planner-only study (host, no GPU): padding % = (m*S - E)/E of each
+    group with every matrix at 1-, 16- and 128-row granules over FSDP sizes
+    m, for the given tensor order and the best of the three orders, with
+    the planner's wall time (the pages' study: veScale-FSDP, section 6.4 and
+    "Planning Algorithm").  Prints a markdown table per group; with out_path
+    also writes one JSON line per plan."""
+    import fsdp_sharded_buffer_amd as R
+    import workloads as W
+
+    groups = {n: W.WORKLOADS[n].tensors
+              for n in ("llama3_8b_layer", "llama70b_layer", "ragged_mixed", "moe_experts")}
+    groups["moe_experts_fused"] = W.fused_experts(W.WORKLOADS["moe_experts"]).tensors
+    recs = []
+    for name, specs in groups.items():
+        E = sum(s.numel for s in specs)
+        print(f"\n{name} (E = {E}, A = {align}): padding % given order / best order "
+              f"[planner ms, all orders]\n")
+        print("| rows | " + " | ".join(f"m={m}" for m in STUDY_MS) + " |")
+        print("|---|" + "---|" * len(STUDY_MS))
+        for rows in STUDY_ROWS:
+            sp = W.regranulated(specs, rows)
+            gmax = max(s.gran_rows * s.cols for s in sp if s.gran_rows)
+            cells = []
+            for m in STUDY_MS:
+                res = {}
+                t0 = time.perf_counter()
+                for k in ("given", "block", "shape"):
+                    perm, _, info = R.rs_plan_ordered(sp, m, align, k)
+                    res[k] = info
+                    recs.append({"group": name, "rows": rows, "m": m, "align": align, "order": k,
+                                 "S": info["S"], "pad_frac": info["pad_frac"],
+                                 "lower_bound": info["lower_bound"], "seconds": info["seconds"],
+                                 "max_granule": gmax})
+                ms = (time.perf_counter() - t0) * 1e3
+                g = res["given"]["pad_frac"] * 100
+                b = min(r["pad_frac"] for r in res.values()) * 100
+                mark = "" if -(-E // m) >= gmax else "*"
+                cells.append(f"{g:.2f}/{b:.2f}{mark} [{ms:.0f}]")
+            print(f"| {rows} | " + " | ".join(cells) + " |", flush=True)
+    print("\n* E/m is below the largest granule: some rank holds less than one granule of "
+          "data, so S >= granule forces padding.")
+    if out_path:
+        with open(out_path, "w") as f:
+            for r in recs:
+                f.write(json.dumps(r) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,7 +187,13 @@ def main():
     ap.add_argument("--only", default="", help="comma list of ops to time per op (default all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) to scale HBM counters")
+    ap.add_argument("--padding-study", action="store_true",
+                    help="planner-only padding study over granularity and FSDP size (no GPU)")
+    ap.add_argument("--study-out", default="", help="JSON lines of the padding study")
     args = ap.parse_args()
+    if args.padding_study:
+        padding_study(args.align if "--align" in sys.argv else 1, args.study_out)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the m virtual ranks are slices of one device buffer "
               "and this build has no multi-GPU path; run with --gpus 1", file=sys.stderr)

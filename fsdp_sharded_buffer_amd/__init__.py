@@ -19,10 +19,14 @@ from ._lib import rs_tensor_spec, rs_plan_info, rs_layout_info, rs_adamw_params,
 
 RS_F32, RS_BF16, RS_U8 = 0, 1, 2
 RS_Q_FP8_E4M3, RS_Q_INT8 = 0, 1
+RS_ORDER_GIVEN, RS_ORDER_BLOCK, RS_ORDER_SHAPE, RS_ORDER_BEST = 0, 1, 2, 3
+ORDERS = {"given": RS_ORDER_GIVEN, "block": RS_ORDER_BLOCK, "shape": RS_ORDER_SHAPE,
+          "best": RS_ORDER_BEST}
 
 __all__ = [
     "RS_F32", "RS_BF16", "RS_U8", "RS_Q_FP8_E4M3", "RS_Q_INT8", "RsError",
-    "rs_plan", "rs_layout_create", "rs_layout_get_info", "rs_layout_upload",
+    "RS_ORDER_GIVEN", "RS_ORDER_BLOCK", "RS_ORDER_SHAPE", "RS_ORDER_BEST", "ORDERS",
+    "rs_plan", "rs_plan_order", "rs_plan_ordered", "rs_layout_create", "rs_layout_get_info", "rs_layout_upload",
     "rs_layout_destroy", "rs_pack", "rs_unpack", "rs_group_scale_add", "rs_group_zero",
     "rs_ragged_sqnorm", "rs_block_quant", "rs_block_dequant", "rs_adamw_step", "rs_adamw8_step",
     "rs_sgd_step",
@@ -68,6 +72,29 @@ def rs_plan(specs, m: int, align: int = 1, S_cap: int = 0) -> Tuple[List[int], D
     info = rs_plan_info()
     check(lib().rs_plan(arr, len(specs), m, align, S_cap, offs, byref(info)))
     return list(offs), {f: getattr(info, f) for f, _ in rs_plan_info._fields_}
+
+
+def _order_kind(kind) -> int:
+    return ORDERS[kind] if isinstance(kind, str) else int(kind)
+
+
+def rs_plan_order(specs, kind) -> List[int]:
+    arr = specs_array(specs)
+    perm = (c_int32 * len(specs))()
+    check(lib().rs_plan_order(arr, len(specs), _order_kind(kind), perm))
+    return list(perm)
+
+
+def rs_plan_ordered(specs, m: int, align: int = 1, kind="given", S_cap: int = 0
+                    ) -> Tuple[List[int], List[int], Dict]:
+    """-> (perm, offsets indexed as specs, info)."""
+    arr = specs_array(specs)
+    perm = (c_int32 * len(specs))()
+    offs = (c_int64 * len(specs))()
+    info = rs_plan_info()
+    check(lib().rs_plan_ordered(arr, len(specs), m, align, S_cap, _order_kind(kind), perm, offs,
+                                byref(info)))
+    return list(perm), list(offs), {f: getattr(info, f) for f, _ in rs_plan_info._fields_}
 
 
 def rs_layout_create(specs, m: int, S: int, offsets: Sequence[int], chunk_elems: int = 0) -> c_void_p:
@@ -190,10 +217,22 @@ class Layout:
         self.ws = torch.zeros(max(self.info["workspace_bytes"], 8), dtype=torch.uint8, device=device)
 
     @classmethod
-    def plan(cls, specs, m: int, align: int = 16, chunk_elems: int = 0, device="cuda"):
-        offs, info = rs_plan(specs, m, align)
+    def plan(cls, specs, m: int, align: int = 16, chunk_elems: int = 0, device="cuda",
+             order=None):
+        """Plan and build.  With `order` ("given", "block", "shape", "best")
+        the tensors are laid out in that order: the layout's tensor i is
+        specs[perm[i]], and `perm` is kept on the returned object."""
+        specs = list(specs)
+        if order is None:
+            offs, info = rs_plan(specs, m, align)
+            perm = list(range(len(specs)))
+        else:
+            perm, offs_by_t, info = rs_plan_ordered(specs, m, align, order)
+            specs = [specs[t] for t in perm]
+            offs = [offs_by_t[t] for t in perm]
         lay = cls(specs, m, info["S"], offs, chunk_elems, device)
         lay.plan_info = info
+        lay.perm = perm
         return lay
 
     @property

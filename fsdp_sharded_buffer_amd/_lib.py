@@ -48,6 +48,10 @@ class RsError(RuntimeError):
 SIGNATURES = {
     "rs_plan": (c_int32, [POINTER(rs_tensor_spec), c_int32, c_int32, c_int64, c_int64,
                           POINTER(c_int64), POINTER(rs_plan_info)]),
+    "rs_plan_order": (c_int32, [POINTER(rs_tensor_spec), c_int32, c_int32, POINTER(c_int32)]),
+    "rs_plan_ordered": (c_int32, [POINTER(rs_tensor_spec), c_int32, c_int32, c_int64, c_int64,
+                                  c_int32, POINTER(c_int32), POINTER(c_int64),
+                                  POINTER(rs_plan_info)]),
     "rs_layout_create": (c_int32, [POINTER(rs_tensor_spec), c_int32, c_int32, c_int64,
                                    POINTER(c_int64), c_int64, POINTER(c_void_p)]),
     "rs_layout_get_info": (c_int32, [c_void_p, POINTER(rs_layout_info)]),

@@ -85,25 +85,14 @@ bool place_all(const std::vector<PItem>& items, int64_t S, int32_t m, int64_t A,
   return true;
 }
 
-}  // namespace
-}  // namespace rs
-
-extern "C" rs_status rs_plan(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t align,
-                             int64_t S_cap, int64_t* offsets, rs_plan_info* info) {
-  using namespace rs;
-  const auto t0 = std::chrono::steady_clock::now();
-  if (!specs || !offsets || n <= 0 || m <= 0 || align <= 0)
-    return fail(RS_ERR_INVALID_ARG, "rs_plan: null pointer or non-positive n/m/align");
-  std::vector<PItem> items(n);
+// Minimum S for the items in the given order; offsets written to offs.
+rs_status plan_items(const std::vector<PItem>& items, int32_t m, int64_t align, int64_t S_cap,
+                     int64_t* offs, int64_t* S_out, int64_t* lb_out) {
+  const int32_t n = int32_t(items.size());
   int64_t total = 0, lb = 1;
-  for (int32_t t = 0; t < n; ++t) {
-    const rs_tensor_spec& s = specs[t];
-    if (s.rows <= 0 || s.cols <= 0 || s.gran_rows < 0)
-      return fail(RS_ERR_INVALID_ARG, "rs_plan: tensor " + std::to_string(t) + " has a bad shape");
-    items[t].E = s.rows * s.cols;
-    items[t].g = s.gran_rows > 0 ? s.gran_rows * s.cols : 1;
-    total += items[t].E;
-    lb = std::max(lb, std::min(items[t].g, items[t].E));
+  for (const PItem& it : items) {
+    total += it.E;
+    lb = std::max(lb, std::min(it.g, it.E));
   }
   lb = std::max(lb, (total + m - 1) / m);
   lb = round_up(lb, align);
@@ -116,33 +105,156 @@ extern "C" rs_status rs_plan(const rs_tensor_spec* specs, int32_t n, int32_t m, 
   std::vector<PItem> by_len(items);
   std::sort(by_len.begin(), by_len.end(), [](const PItem& a, const PItem& b) { return a.E > b.E; });
 
-  std::vector<int64_t> offs(n);
-  int64_t found = -1;
-  for (int64_t S = lb; S <= cap; S += align) {
+  *lb_out = lb;
+  for (int64_t S = lb; S <= cap;) {
+    int64_t next = S + align;
     bool ok = true;
     for (const PItem& it : by_len) {
       if (it.E <= 2 * S) break;
-      if (S % it.g) { ok = false; break; }
+      if (S % it.g) {
+        // the aligned S that this tensor rejects run up to the next
+        // multiple of lcm(g, align) or to the first S with E <= 2S
+        ok = false;
+        const int64_t L = std::lcm(it.g, align);
+        next = std::max(next, std::min((S / L + 1) * L, round_up((it.E + 1) / 2, align)));
+        break;
+      }
     }
-    if (ok && place_all(items, S, m, align, offs.data())) {
-      found = S;
-      break;
+    if (ok && place_all(items, S, m, align, offs)) {
+      *S_out = S;
+      return RS_OK;
     }
+    S = next;
   }
-  if (found < 0)
-    return fail(RS_ERR_INFEASIBLE, "rs_plan: no layout with S <= " + std::to_string(cap));
+  return fail(RS_ERR_INFEASIBLE, "rs_plan: no layout with S <= " + std::to_string(cap));
+}
+
+rs_status read_items(const char* fn, const rs_tensor_spec* specs, int32_t n,
+                     std::vector<PItem>& items) {
+  items.resize(n);
+  for (int32_t t = 0; t < n; ++t) {
+    const rs_tensor_spec& s = specs[t];
+    if (s.rows <= 0 || s.cols <= 0 || s.gran_rows < 0)
+      return fail(RS_ERR_INVALID_ARG,
+                  std::string(fn) + ": tensor " + std::to_string(t) + " has a bad shape");
+    items[t].E = s.rows * s.cols;
+    items[t].g = s.gran_rows > 0 ? s.gran_rows * s.cols : 1;
+  }
+  return RS_OK;
+}
+
+void fill_info(rs_plan_info* info, const std::vector<PItem>& items, int32_t m, int64_t S,
+               int64_t lb, std::chrono::steady_clock::time_point t0) {
+  if (!info) return;
+  int64_t total = 0;
+  for (const PItem& it : items) total += it.E;
+  info->S = S;
+  info->total = S * m;
+  info->numel = total;
+  info->pad_elems = S * m - total;
+  info->pad_frac = double(S * m - total) / double(total);
+  info->lower_bound = lb;
+  info->peak_param_bytes = 4 * S + 2 * int64_t(m) * S;
+  info->seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+}
+
+// The tensor orders the pages compare (veScale-FSDP, "Planning Algorithm":
+// the given order, by block size, by tensor shape).  Stable sorts, so
+// tensors with equal keys keep their given order.
+void order_perm(const rs_tensor_spec* specs, int32_t n, rs_order kind, int32_t* perm) {
+  std::iota(perm, perm + n, 0);
+  auto granule = [&](int32_t t) {
+    return specs[t].gran_rows > 0 ? specs[t].gran_rows * specs[t].cols : int64_t(1);
+  };
+  if (kind == RS_ORDER_BLOCK)
+    std::stable_sort(perm, perm + n, [&](int32_t a, int32_t b) { return granule(a) > granule(b); });
+  else if (kind == RS_ORDER_SHAPE)
+    std::stable_sort(perm, perm + n, [&](int32_t a, int32_t b) {
+      if (specs[a].rows != specs[b].rows) return specs[a].rows > specs[b].rows;
+      return specs[a].cols > specs[b].cols;
+    });
+}
+
+}  // namespace
+}  // namespace rs
+
+extern "C" rs_status rs_plan(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t align,
+                             int64_t S_cap, int64_t* offsets, rs_plan_info* info) {
+  using namespace rs;
+  const auto t0 = std::chrono::steady_clock::now();
+  if (!specs || !offsets || n <= 0 || m <= 0 || align <= 0)
+    return fail(RS_ERR_INVALID_ARG, "rs_plan: null pointer or non-positive n/m/align");
+  std::vector<PItem> items;
+  rs_status st = read_items("rs_plan", specs, n, items);
+  if (st != RS_OK) return st;
+  std::vector<int64_t> offs(n);
+  int64_t S = 0, lb = 0;
+  st = plan_items(items, m, align, S_cap, offs.data(), &S, &lb);
+  if (st != RS_OK) return st;
   std::copy(offs.begin(), offs.end(), offsets);
-  if (info) {
-    info->S = found;
-    info->total = found * m;
-    info->numel = total;
-    info->pad_elems = found * m - total;
-    info->pad_frac = double(found * m - total) / double(total);
-    info->lower_bound = lb;
-    info->peak_param_bytes = 4 * found + 2 * int64_t(m) * found;
-    info->seconds =
-        std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+  fill_info(info, items, m, S, lb, t0);
+  clear_error();
+  return RS_OK;
+}
+
+extern "C" rs_status rs_plan_order(const rs_tensor_spec* specs, int32_t n, rs_order kind,
+                                   int32_t* perm) {
+  using namespace rs;
+  if (!specs || !perm || n <= 0)
+    return fail(RS_ERR_INVALID_ARG, "rs_plan_order: null pointer or non-positive n");
+  if (kind != RS_ORDER_GIVEN && kind != RS_ORDER_BLOCK && kind != RS_ORDER_SHAPE)
+    return fail(RS_ERR_INVALID_ARG, "rs_plan_order: kind must be GIVEN, BLOCK or SHAPE");
+  order_perm(specs, n, kind, perm);
+  clear_error();
+  return RS_OK;
+}
+
+extern "C" rs_status rs_plan_ordered(const rs_tensor_spec* specs, int32_t n, int32_t m,
+                                     int64_t align, int64_t S_cap, rs_order kind, int32_t* perm,
+                                     int64_t* offsets, rs_plan_info* info) {
+  using namespace rs;
+  const auto t0 = std::chrono::steady_clock::now();
+  if (!specs || !perm || !offsets || n <= 0 || m <= 0 || align <= 0)
+    return fail(RS_ERR_INVALID_ARG, "rs_plan_ordered: null pointer or non-positive n/m/align");
+  if (kind != RS_ORDER_GIVEN && kind != RS_ORDER_BLOCK && kind != RS_ORDER_SHAPE &&
+      kind != RS_ORDER_BEST)
+    return fail(RS_ERR_INVALID_ARG, "rs_plan_ordered: unknown order kind");
+  std::vector<PItem> items;
+  rs_status st = read_items("rs_plan_ordered", specs, n, items);
+  if (st != RS_OK) return st;
+  const rs_order kinds[3] = {RS_ORDER_GIVEN, RS_ORDER_BLOCK, RS_ORDER_SHAPE};
+  int64_t best_S = -1, best_lb = 0;
+  std::vector<int32_t> best_perm;
+  std::vector<int64_t> best_offs;
+  for (rs_order k : kinds) {
+    if (kind != RS_ORDER_BEST && k != kind) continue;
+    std::vector<int32_t> pm(n);
+    order_perm(specs, n, k, pm.data());
+    std::vector<PItem> ordered(n);
+    for (int32_t i = 0; i < n; ++i) ordered[i] = items[pm[i]];
+    std::vector<int64_t> offs(n);
+    int64_t S = 0, lb = 0;
+    // a later order has to beat the best S so far (ties keep the earlier)
+    int64_t cap = S_cap;
+    if (best_S > 0) {
+      if (best_S - 1 < 1) continue;
+      cap = S_cap > 0 ? std::min(S_cap, best_S - 1) : best_S - 1;
+    }
+    st = plan_items(ordered, m, align, cap, offs.data(), &S, &lb);
+    if (st == RS_ERR_INFEASIBLE) continue;
+    if (st != RS_OK) return st;
+    best_S = S;
+    best_lb = lb;
+    best_perm = pm;
+    best_offs = offs;
   }
+  if (best_S < 0)
+    return fail(RS_ERR_INFEASIBLE, "rs_plan_ordered: no layout within S_cap");
+  for (int32_t i = 0; i < n; ++i) {
+    perm[i] = best_perm[i];
+    offsets[best_perm[i]] = best_offs[i];
+  }
+  fill_info(info, items, m, best_S, best_lb, t0);
   clear_error();
   return RS_OK;
 }

@@ -106,6 +106,41 @@ rs_status rs_plan(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t ali
  * caller-owned device buffer (the persistent descriptor table every grouped
  * kernel reads; veScale-FSDP, "DBuffer": one kernel per group instead of
  * one per tensor). */
+/* Tensor orders for rs_plan_ordered (veScale-FSDP, "Planning Algorithm":
+ * the pages compare the given order, an order by block size and one by
+ * tensor shape, and keep the given one).  Orders are stable: tensors with
+ * equal keys keep their given order.
+ *   RS_ORDER_GIVEN  the given order
+ *   RS_ORDER_BLOCK  granule size (gran_rows*cols, or 1) descending
+ *   RS_ORDER_SHAPE  (rows, cols) descending, lexicographic
+ *   RS_ORDER_BEST   plan all three, keep the smallest S; ties go to the
+ *                   earlier of GIVEN, BLOCK, SHAPE */
+typedef enum {
+  RS_ORDER_GIVEN = 0,
+  RS_ORDER_BLOCK = 1,
+  RS_ORDER_SHAPE = 2,
+  RS_ORDER_BEST = 3
+} rs_order;
+
+/* rs_plan_order - the buffer order of one of the orders above.
+ *   specs  host [n] tensor specs
+ *   kind   RS_ORDER_GIVEN, RS_ORDER_BLOCK or RS_ORDER_SHAPE
+ *   perm   host [n] out: perm[i] = index into specs of the i-th tensor in
+ *          the buffer
+ * Host only. */
+rs_status rs_plan_order(const rs_tensor_spec* specs, int32_t n, rs_order kind, int32_t* perm);
+
+/* rs_plan_ordered - rs_plan on the group taken in the order `kind` gives.
+ *   perm     host [n] out: buffer order, as rs_plan_order
+ *   offsets  host [n] out: offsets[t] = l_t of tensor t (indexed as specs)
+ *   others   as rs_plan
+ * A layout is then built from the tensors in buffer order: specs[perm[i]]
+ * with offsets[perm[i]] for i = 0..n-1.  Host only.  RS_ERR_INFEASIBLE if
+ * no order fits S_cap. */
+rs_status rs_plan_ordered(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t align,
+                          int64_t S_cap, rs_order kind, int32_t* perm, int64_t* offsets,
+                          rs_plan_info* info);
+
 typedef struct rs_layout rs_layout;
 
 /* Counts describing a layout (for sizing caller buffers). */

@@ -246,3 +246,48 @@ def peak_param_bytes(S: int, m: int, k_full: int = 4, k_low: int = 2) -> int:
 def padding_fraction(items: Sequence[Item], S: int, m: int) -> float:
     total = sum(it.numel for it in items)
     return (m * S - total) / total
+
+
+# ---------------------------------------------------------------- orders
+#
+# The pages compare three tensor orders for the planner - the given one, one
+# by block size and one by tensor shape - and keep the given one, which was
+# optimal or near it in their runs (veScale-FSDP, "Planning Algorithm").
+# They do not define the other two; the readings here are: by block size =
+# granule elements descending, by shape = (rows, cols) descending, both
+# stable (equal keys keep the given order).  "best" plans all three and
+# keeps the smallest S, ties going to the earlier of given, block, shape.
+
+ORDER_KINDS = ("given", "block", "shape")
+
+
+def order_perm(specs, kind: str) -> List[int]:
+    """Buffer order: perm[i] is the index of the tensor placed i-th."""
+    idx = list(range(len(specs)))
+    if kind == "given":
+        return idx
+    if kind == "block":
+        gran = [s.gran_rows * s.cols if s.gran_rows > 0 else 1 for s in specs]
+        return sorted(idx, key=lambda t: gran[t], reverse=True)
+    if kind == "shape":
+        return sorted(idx, key=lambda t: (specs[t].rows, specs[t].cols), reverse=True)
+    raise ValueError(kind)
+
+
+def plan_ordered(specs, m: int, A: int = 1, kind: str = "given"):
+    """-> (perm, offsets indexed as specs, S) or None.  The plan of the
+    tensors taken in buffer order perm; kind "best" tries the three orders."""
+    kinds = ORDER_KINDS if kind == "best" else (kind,)
+    best = None
+    for k in kinds:
+        perm = order_perm(specs, k)
+        items = items_from_specs([specs[t] for t in perm])
+        p = plan(items, m, A)
+        if p is None:
+            continue
+        if best is None or p.S < best[2]:
+            offs = [0] * len(specs)
+            for i, t in enumerate(perm):
+                offs[t] = p.offsets[i]
+            best = (perm, offs, p.S)
+    return best

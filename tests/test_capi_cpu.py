@@ -76,6 +76,100 @@ def test_planner_matches_bruteforce_random():
         assert (info["S"], offs) == (bf[0], bf[1]), (pairs, m, A)
 
 
+def _rand_specs(rng, max_t=5):
+    out = []
+    for i in range(int(rng.integers(1, max_t + 1))):
+        rows, cols = int(rng.integers(1, 7)), int(rng.integers(1, 6))
+        gran = 0 if rows == 1 else int(rng.integers(0, rows + 1))
+        out.append(W.TensorSpec(f"t{i}", rows, cols, gran))
+    return out
+
+
+def _study_groups():
+    moe = W.WORKLOADS["moe_experts"]
+    groups = {n: w.tensors for n, w in W.WORKLOADS.items()}
+    groups["moe_experts_fused"] = W.fused_experts(moe).tensors
+    for n in ("llama3_8b_layer", "ragged_mixed", "moe_experts_fused"):
+        for r in (1, 16, 128):
+            groups[f"{n}@{r}"] = W.regranulated(groups[n], r)
+    return groups
+
+
+def test_plan_order_matches_oracle():
+    for name, specs in _study_groups().items():
+        for k in ("given", "block", "shape"):
+            assert R.rs_plan_order(specs, k) == P.order_perm(specs, k), (name, k)
+    rng = np.random.default_rng(53)
+    for _ in range(200):
+        specs = _rand_specs(rng)
+        for k in ("given", "block", "shape"):
+            assert R.rs_plan_order(specs, k) == P.order_perm(specs, k)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_plan_ordered_matches_oracle_on_configs(name):
+    w = W.WORKLOADS[name]
+    for k in ("given", "block", "shape", "best"):
+        perm, offs, info = R.rs_plan_ordered(w.tensors, w.m, 16, k)
+        o = P.plan_ordered(w.tensors, w.m, 16, k)
+        assert (perm, offs, info["S"]) == (o[0], o[1], o[2]), k
+        assert info["seconds"] < 0.3 * (3 if k == "best" else 1)
+
+
+def test_plan_ordered_matches_oracle_random_and_study_cases():
+    rng = np.random.default_rng(59)
+    for _ in range(300):
+        specs = _rand_specs(rng)
+        m = int(rng.integers(1, 6))
+        A = int(rng.choice([1, 2, 3, 4]))
+        for k in ("given", "block", "shape", "best"):
+            perm, offs, info = R.rs_plan_ordered(specs, m, A, k)
+            o = P.plan_ordered(specs, m, A, k)
+            assert (perm, offs, info["S"]) == (o[0], o[1], o[2]), (specs, m, A, k)
+    # regranulated groups where long tensors force S to a multiple of their
+    # granules (the planner skips the S values they reject), at A = 1
+    g = _study_groups()
+    for name, m in (("llama3_8b_layer@16", 64), ("llama70b_layer", 32), ("ragged_mixed@128", 16),
+                    ("moe_experts_fused@16", 128), ("moe_experts_fused@128", 16)):
+        specs = g[name] if "@" in name else W.regranulated(g[name], 16)
+        for k in ("given", "best"):
+            perm, offs, info = R.rs_plan_ordered(specs, m, 1, k)
+            o = P.plan_ordered(specs, m, 1, k)
+            assert (perm, offs, info["S"]) == (o[0], o[1], o[2]), (name, m, k)
+
+
+def test_lcm_of_granules_sets_S():
+    """Llama-8B layer, 16-row granules, 64 ranks: Wgate, Wup (14336x4096) and
+    Wdown (4096x14336) are each longer than 2S, so S must be a multiple of
+    both 16*4096 and 16*14336, i.e. of lcm = 2^16 * 7; the smallest such S
+    above ceil(E/64) is 8 * 458752, and a layout exists there."""
+    specs = W.regranulated(W.WORKLOADS["llama3_8b_layer"].tensors, 16)
+    E = sum(s.numel for s in specs)
+    L = 458752
+    assert L == np.lcm(16 * 4096, 16 * 14336)
+    expect = -(-(-(-E // 64)) // L) * L
+    assert expect == 8 * L
+    _, info = R.rs_plan(specs, 64, 1)
+    assert info["S"] == expect
+    assert abs(info["pad_frac"] - (64 * expect / E - 1)) < 1e-12
+
+
+def test_layout_accepts_ordered_plan():
+    w = W.WORKLOADS["ragged_mixed"]
+    specs = W.regranulated(w.tensors, 128)
+    perm, offs, info = R.rs_plan_ordered(specs, 16, 1, "best")
+    assert perm != list(range(len(specs)))          # another order wins here
+    ordered = [specs[t] for t in perm]
+    h = R.rs_layout_create(ordered, 16, info["S"], [offs[t] for t in perm])
+    li = R.rs_layout_get_info(h)
+    R.rs_layout_destroy(h)
+    assert li["total"] == 16 * info["S"] and li["n"] == len(specs)
+    # in the given order the same offsets are rejected (tensors overlap or
+    # are out of order)
+    with pytest.raises(R.RsError):
+        R.rs_layout_create(specs, 16, info["S"], offs)
+
+
 def test_planner_infeasible_cap_and_bad_args():
     specs = [W.TensorSpec("a", 12, 1, 4)]
     with pytest.raises(R.RsError) as e:

@@ -4,6 +4,7 @@ Each test checks the oracle against something other than itself: the
 hand-derived toy plan, closed forms, a non-monotone instance, exhaustive
 search on tiny inputs and the layout constraints restated independently.
 """
+import itertools
 import json
 import math
 import os
@@ -186,3 +187,82 @@ def test_fragments_cover_tensors():
         assert tot == it.numel
     for tid, k, lo, hi in fr:
         assert k * p.S <= lo < hi <= (k + 1) * p.S
+
+
+# ------------------------------------------------------------ tensor orders
+
+def test_order_perm_hand_example():
+    """The three orders worked by hand on four tensors:
+    t0 4x8 gran 2 rows (g=16), t1 1x5 vector (g=1), t2 8x4 gran 4 rows
+    (g=16), t3 4x8 gran 1 row (g=8).
+    block (g descending, stable): t0, t2, t3, t1.
+    shape ((rows, cols) descending, stable): t2 (8,4), t0 (4,8), t3 (4,8), t1 (1,5)."""
+    specs = [W.TensorSpec("t0", 4, 8, 2), W.TensorSpec("t1", 1, 5, 0),
+             W.TensorSpec("t2", 8, 4, 4), W.TensorSpec("t3", 4, 8, 1)]
+    assert P.order_perm(specs, "given") == [0, 1, 2, 3]
+    assert P.order_perm(specs, "block") == [0, 2, 3, 1]
+    assert P.order_perm(specs, "shape") == [2, 0, 3, 1]
+
+
+def _rand_specs(rng, max_t=5):
+    """Random small row-major specs: vectors, row-granular and block-granular."""
+    out = []
+    for i in range(int(rng.integers(1, max_t + 1))):
+        rows, cols = int(rng.integers(1, 7)), int(rng.integers(1, 6))
+        gran = 0 if rows == 1 else int(rng.integers(0, rows + 1))
+        out.append(W.TensorSpec(f"t{i}", rows, cols, gran))
+    return out
+
+
+def _layout_ok(specs, perm, offs, S, m, A):
+    items = P.items_from_specs([specs[t] for t in perm])
+    starts = [offs[t] for t in perm]
+    ends = [l + it.numel for l, it in zip(starts, items)]
+    return P.check_layout(items, starts, ends, [k * S for k in range(m + 1)], A) == []
+
+
+def test_plan_ordered_valid_and_best_is_min():
+    rng = np.random.default_rng(41)
+    for _ in range(150):
+        specs = _rand_specs(rng, 5)
+        m = int(rng.integers(1, 5))
+        A = int(rng.choice([1, 1, 2, 3]))
+        got = {k: P.plan_ordered(specs, m, A, k) for k in ("given", "block", "shape", "best")}
+        for k, (perm, offs, S) in got.items():
+            assert sorted(perm) == list(range(len(specs)))
+            assert _layout_ok(specs, perm, offs, S, m, A), (k, specs, m, A)
+        Ss = [got[k][2] for k in ("given", "block", "shape")]
+        assert got["best"][2] == min(Ss)
+        # ties go to the earliest order in (given, block, shape)
+        first = ("given", "block", "shape")[Ss.index(min(Ss))]
+        assert got["best"][0] == got[first][0]
+        # the given order is the plain planner
+        p = P.plan(P.items_from_specs(specs), m, A)
+        assert got["given"][2] == p.S and got["given"][1] == p.offsets
+
+
+def test_orders_against_every_permutation():
+    """Exhaustive over tensor orders on tiny groups: no order beats the
+    minimum over all permutations, and that minimum is attained by some
+    permutation (sanity of the order-free optimum the pages' NP-hardness
+    refers to)."""
+    rng = np.random.default_rng(43)
+    for _ in range(60):
+        specs = _rand_specs(rng, 4)
+        m = int(rng.integers(1, 4))
+        best_any = min(P.plan(P.items_from_specs([specs[t] for t in perm]), m, 1).S
+                       for perm in itertools.permutations(range(len(specs))))
+        assert P.plan_ordered(specs, m, 1, "best")[2] >= best_any
+
+
+def test_coarser_granule_never_shrinks_S():
+    """Row granules r | r': every layout valid with granule r' rows is valid
+    with r rows, so S*(1 row) <= S*(2 rows) <= S*(4 rows) for the same order."""
+    rng = np.random.default_rng(47)
+    for _ in range(80):
+        n = int(rng.integers(1, 5))
+        specs = [W.TensorSpec(f"t{i}", int(rng.integers(1, 9)) * 4, int(rng.integers(1, 5)), 1)
+                 for i in range(n)]
+        m = int(rng.integers(1, 6))
+        S = [P.plan(P.items_from_specs(W.regranulated(specs, r)), m, 1).S for r in (1, 2, 4)]
+        assert S[0] <= S[1] <= S[2], (specs, m, S)

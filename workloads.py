@@ -154,6 +154,39 @@ WORKLOADS = {w.name: w for w in (toy_unit(), llama8b_layer(), ragged_mixed(),
                                   moe_experts(), llama70b_layer())}
 
 
+def regranulated(specs: Sequence[TensorSpec], rows: int) -> Tuple[TensorSpec, ...]:
+    """The same tensors with every matrix (more than one row) given a granule
+    of `rows` rows and vectors left element-granular; quantisation tiles are
+    dropped (the planner alone is studied).  The row-granularity sweep of
+    the pages' padding study (veScale-FSDP, section 6.4) runs 1, 16 and 128
+    rows."""
+    return tuple(TensorSpec(s.name, s.rows, s.cols, rows if s.rows > 1 else 0)
+                 for s in specs)
+
+
+def fused_experts(w: Workload) -> Workload:
+    """The expert unit with each expert matrix kind fused into one tensor
+    (all experts' W1 stacked by rows, likewise W3 and W2), router kept.
+    The pages trace their largest padding spikes to models that store all
+    experts as one parameter tensor (veScale-FSDP, section 6.4); this is
+    that storage applied to the expert unit's own shapes."""
+    kinds: Dict[str, List[TensorSpec]] = {}
+    rest: List[TensorSpec] = []
+    for s in w.tensors:
+        if s.name.startswith("e") and "." in s.name:
+            kinds.setdefault(s.name.split(".", 1)[1], []).append(s)
+        else:
+            rest.append(s)
+    fused = []
+    for kind, ss in kinds.items():
+        r0 = ss[0]
+        assert all(x.cols == r0.cols and x.gran_rows == r0.gran_rows for x in ss)
+        fused.append(TensorSpec("experts." + kind, sum(x.rows for x in ss), r0.cols, r0.gran_rows,
+                                r0.q_rows, r0.q_cols))
+    return Workload(w.name + "_fused", tuple(fused + rest), m=w.m, qfmt=w.qfmt, block=w.block,
+                    grad_dist=w.grad_dist, description="expert unit with fused expert tensors")
+
+
 def scaled_workload(w: Workload, row_div: int, col_div: int = 1, max_tensors: int = 0,
                     m: int = 0) -> Workload:
     """A smaller copy of a workload with every matrix dimension divided.
