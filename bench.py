@@ -187,6 +187,8 @@ def main():
     ap.add_argument("--only", default="", help="comma list of ops to time per op (default all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) to scale HBM counters")
+    ap.add_argument("--no-torch-ref", action="store_true",
+                    help="skip timing torch's own copy/axpy/fill/fused optimizers for context")
     ap.add_argument("--padding-study", action="store_true",
                     help="planner-only padding study over granularity and FSDP size (no GPU)")
     ap.add_argument("--study-out", default="", help="JSON lines of the padding study")
@@ -294,8 +296,9 @@ def main():
     per_op, per_extra = {}, {}
     allops = dict(ops, **extra)
     allbytes = dict(nbytes, **xbytes)
-    for name in only:
-        f = allops[name]
+    def event_ms(f, n_samples):
+        """Median and minimum ms per call, HIP events on the launch stream,
+        each sample at least ~20 ms of back-to-back calls."""
         for _ in range(3):
             f()
         torch.cuda.synchronize()
@@ -307,14 +310,18 @@ def main():
         one = max(e0.elapsed_time(e1), 1e-3)
         reps = max(1, int(20.0 / one))
         samples = []
-        for _ in range(args.samples):
+        for _ in range(n_samples):
             e0.record(stream)
             for _ in range(reps):
                 f()
             e1.record(stream)
             e1.synchronize()
             samples.append(e0.elapsed_time(e1) / reps)
-        med = float(np.median(samples))
+        return float(np.median(samples)), samples, reps
+
+    for name in only:
+        f = allops[name]
+        med, samples, reps = event_ms(f, args.samples)
         gbs = allbytes[name] / (med * 1e-3) / 1e9
         (per_op if name in ops else per_extra)[name] = {
             "us": round(med * 1e3, 2), "min_us": round(min(samples) * 1e3, 2),
@@ -329,6 +336,36 @@ def main():
             "frac": timed[dom]["frac_peak"],
             "traffic": read_counters(w.name) if dom == "scale_add" else None,
             "bytes_per_launch": allbytes[dom], "avg_launch_us": timed[dom]["us"]}
+
+    # torch's own kernels on one contiguous tensor, same box, same timing:
+    # context for the grouped kernels' rates (not a target)
+    ref = None
+    if not args.no_torch_ref:
+        del deq, mom, var, codes2, scales2
+        torch.cuda.empty_cache()
+        n = 1 << 28
+        a = torch.empty(n, dtype=torch.float32, device=dev).normal_()
+        b = torch.empty_like(a).normal_()
+        ref = {}
+        med, _, _ = event_ms(lambda: b.copy_(a), 5)
+        ref["copy_1GiB"] = round(8 * n / (med * 1e-3) / 1e9, 1)
+        med, _, _ = event_ms(lambda: b.add_(a, alpha=0.5), 5)
+        ref["axpy_inplace_1GiB"] = round(12 * n / (med * 1e-3) / 1e9, 1)
+        med, _, _ = event_ms(lambda: b.zero_(), 5)
+        ref["fill_1GiB"] = round(4 * n / (med * 1e-3) / 1e9, 1)
+        del a, b
+        k = 1 << 26
+        prm = torch.nn.Parameter(torch.randn(k, device=dev) * 0.02)
+        prm.grad = torch.randn(k, device=dev) * 1e-3
+        opt = torch.optim.AdamW([prm], lr=1e-4, fused=True)
+        med, _, _ = event_ms(opt.step, 5)
+        ref["fused_adamw_64M"] = round(28 * k / (med * 1e-3) / 1e9, 1)
+        opt = torch.optim.SGD([prm], lr=1e-4, momentum=0.9, fused=True)
+        med, _, _ = event_ms(opt.step, 5)
+        ref["fused_sgd_64M"] = round(20 * k / (med * 1e-3) / 1e9, 1)
+        del prm, opt
+        ref["unit"] = "GB/s"
+        log(f"torch reference: {ref}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -351,6 +388,7 @@ def main():
         "next_ops": per_extra,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "torch_reference": ref,
         "device": torch.cuda.get_device_name(0),
         "host": platform.processor() or platform.machine(),
     }
