@@ -96,6 +96,7 @@ struct rs_layout {
 
   // per-rank begin indices, size m + 1
   std::vector<int64_t> rank_chunk, rank_cchunk, rank_frag, rank_tile, rank_work;
+  std::vector<int32_t> rank_min_tile_rows;  // per rank; INT32_MAX when it has no tile
 
   // byte offsets of each table inside the device blob
   size_t off_tensors = 0, off_frags = 0, off_chunks = 0, off_cchunks = 0, off_tiles = 0,

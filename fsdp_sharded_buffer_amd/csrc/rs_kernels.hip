@@ -88,7 +88,16 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #define RS_QUANT_NT 1
 #endif
 #ifndef RS_FILL_BYTES
-#define RS_FILL_BYTES 262144
+#define RS_FILL_BYTES 4096
+#endif
+#ifndef RS_ADAMW_SPLIT
+#define RS_ADAMW_SPLIT 4
+#endif
+#ifndef RS_SGD_SPLIT
+#define RS_SGD_SPLIT 4
+#endif
+#ifndef RS_DEQ_SPLIT
+#define RS_DEQ_SPLIT 4
 #endif
 #ifndef RS_DEQ_LDS
 #define RS_DEQ_LDS 1
@@ -752,20 +761,30 @@ __device__ __forceinline__ void store4(char* yb, int64_t elem, const float d[4],
 // all loads of a lane issued before its stores; unaligned tiles one code
 // per lane.  (16 codes per lane - 16-byte loads, lane-strided stores - was
 // several times slower.)
-template <int FMT, int YK>
+// With F > 1, F workgroups share a work item, each taking one band of
+// about rows/F rows of every tile (more, shorter workgroups); the host uses
+// F = 1 when some tile of the range has fewer than F rows.
+template <int FMT, int YK, int F>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const QuantWork* __restrict__ work,
                                                            int64_t w0,
                                                            const TileDesc* __restrict__ tiles,
                                                            const uint8_t* __restrict__ codes,
                                                            const float* __restrict__ scales,
                                                            void* __restrict__ y, int vec_ok) {
-  const QuantWork w = work[w0 + blockIdx.x];
+  const QuantWork w = work[w0 + blockIdx.x / F];
+  const int band = blockIdx.x % F;
   const int team = w.team;
   const int slot = threadIdx.x / team;
   const int lane = threadIdx.x % team;
   const bool active = slot < w.count;
-  const TileDesc td = tiles[w.tile_begin + (active ? slot : 0)];
+  TileDesc td = tiles[w.tile_begin + (active ? slot : 0)];
   const float scale = scales[td.scale_idx];
+  if (F > 1) {
+    const int rp = (td.rows + F - 1) / F;
+    const int r0 = min(td.rows, band * rp);
+    td.buf_off += int64_t(r0) * td.ld;
+    td.rows = min(td.rows - r0, rp);
+  }
   const uint8_t* cb = codes + td.buf_off;
   char* yb = static_cast<char*>(y) + td.buf_off * esize<YK>();
 #if RS_DEQ_LDS
@@ -867,19 +886,40 @@ __device__ __forceinline__ void adamw1(float& p, float g, float& m, float& v, co
   v = v2;
 }
 
+// With SPLIT > 1 workgroup ii takes piece ii % SPLIT of chunk ii / SPLIT:
+// more, shorter workgroups for the many-stream optimizer kernels.  Pieces
+// are whole multiples of 64 elements, so 16-byte alignment is kept.
+template <int SPLIT>
+__device__ __forceinline__ bool piece_of(const ChunkDesc& c, int q, int64_t& off, int& n) {
+  if (SPLIT == 1) {
+    off = c.buf_off;
+    n = c.len;
+    return true;
+  }
+  const int per = ((c.len + SPLIT - 1) / SPLIT + 63) & ~63;
+  const int lo = q * per;
+  if (lo >= c.len) return false;
+  off = c.buf_off + lo;
+  n = c.len - lo < per ? c.len - lo : per;
+  return true;
+}
+
+template <int SPLIT>
 __global__ __launch_bounds__(kThreads) void adamw_kernel(
     const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* __restrict__ p,
     const float* __restrict__ g, float* __restrict__ m, float* __restrict__ v, AdamConst k,
     const uint8_t* __restrict__ mask, const uint32_t* __restrict__ found_inf, int m_ranks) {
   if (skip_step(found_inf, m_ranks)) return;
-  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
-    const ChunkDesc c = chunks[c0 + i];
+  for (int64_t ii = blockIdx.x; ii < nc * SPLIT; ii += gridDim.x) {
+    const ChunkDesc c = chunks[c0 + ii / SPLIT];
     if (c.tensor < 0 || (mask && !mask[c.tensor])) continue;
-    float* pp = p + c.buf_off;
-    const float* gp = g + c.buf_off;
-    float* mp = m + c.buf_off;
-    float* vp = v + c.buf_off;
-    const int n = c.len;
+    int64_t off;
+    int n;
+    if (!piece_of<SPLIT>(c, int(ii % SPLIT), off, n)) continue;
+    float* pp = p + off;
+    const float* gp = g + off;
+    float* mp = m + off;
+    float* vp = v + off;
     const bool vec = aligned16(pp) && aligned16(gp) && aligned16(mp) && aligned16(vp);
     const int nv = vec ? n / 4 : 0;
     for (int q0 = threadIdx.x; q0 < nv; q0 += kUnroll * kThreads) {
@@ -933,18 +973,21 @@ __device__ __forceinline__ void sgd1(float& p, float g, float& b, const SgdConst
   b = b2;
 }
 
+template <int SPLIT>
 __global__ __launch_bounds__(kThreads) void sgd_kernel(
     const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* __restrict__ p,
     const float* __restrict__ g, float* __restrict__ buf, SgdConst k,
     const uint8_t* __restrict__ mask, const uint32_t* __restrict__ found_inf, int m_ranks) {
   if (skip_step(found_inf, m_ranks)) return;
-  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
-    const ChunkDesc c = chunks[c0 + i];
+  for (int64_t ii = blockIdx.x; ii < nc * SPLIT; ii += gridDim.x) {
+    const ChunkDesc c = chunks[c0 + ii / SPLIT];
     if (c.tensor < 0 || (mask && !mask[c.tensor])) continue;
-    float* pp = p + c.buf_off;
-    const float* gp = g + c.buf_off;
-    float* bp = buf + c.buf_off;
-    const int n = c.len;
+    int64_t off;
+    int n;
+    if (!piece_of<SPLIT>(c, int(ii % SPLIT), off, n)) continue;
+    float* pp = p + off;
+    const float* gp = g + off;
+    float* bp = buf + off;
     const bool vec = aligned16(pp) && aligned16(gp) && aligned16(bp);
     const int nv = vec ? n / 4 : 0;
     for (int q0 = threadIdx.x; q0 < nv; q0 += kUnroll * kThreads) {
@@ -1442,17 +1485,31 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
   const int64_t w0 = L->rank_work[k0], nw = L->rank_work[k1] - w0;
   if (nw == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 g(static_cast<unsigned>(nw)), b(kThreads);
+  // row bands per work item when every tile of the range has that many rows
+  int32_t min_rows = INT32_MAX;
+  for (int32_t k = k0; k < k1; ++k) min_rows = std::min(min_rows, L->rank_min_tile_rows[k]);
+  const bool split = RS_DEQ_SPLIT > 1 && min_rows >= RS_DEQ_SPLIT;
+  const dim3 g(static_cast<unsigned>(split ? nw * RS_DEQ_SPLIT : nw)), b(kThreads);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
   const TileDesc* tl = table<TileDesc>(L, L->off_tiles);
+#define RS_DEQ_LAUNCH(FM, YK)                                                                 \
+  do {                                                                                        \
+    if (split)                                                                                \
+      hipLaunchKernelGGL((dequant_kernel<FM, YK, RS_DEQ_SPLIT>), g, b, 0, s, wk, w0, tl, codes, \
+                         scales, y, vec_ok);                                                  \
+    else                                                                                      \
+      hipLaunchKernelGGL((dequant_kernel<FM, YK, 1>), g, b, 0, s, wk, w0, tl, codes, scales, y, \
+                         vec_ok);                                                             \
+  } while (0)
   if (fmt == RS_Q_FP8_E4M3 && y_dt == RS_F32)
-    hipLaunchKernelGGL((dequant_kernel<RS_Q_FP8_E4M3, 0>), g, b, 0, s, wk, w0, tl, codes, scales, y, vec_ok);
+    RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 0);
   else if (fmt == RS_Q_FP8_E4M3)
-    hipLaunchKernelGGL((dequant_kernel<RS_Q_FP8_E4M3, 1>), g, b, 0, s, wk, w0, tl, codes, scales, y, vec_ok);
+    RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 1);
   else if (y_dt == RS_F32)
-    hipLaunchKernelGGL((dequant_kernel<RS_Q_INT8, 0>), g, b, 0, s, wk, w0, tl, codes, scales, y, vec_ok);
+    RS_DEQ_LAUNCH(RS_Q_INT8, 0);
   else
-    hipLaunchKernelGGL((dequant_kernel<RS_Q_INT8, 1>), g, b, 0, s, wk, w0, tl, codes, scales, y, vec_ok);
+    RS_DEQ_LAUNCH(RS_Q_INT8, 1);
+#undef RS_DEQ_LAUNCH
   return after_launch(fn);
 }
 
@@ -1483,7 +1540,7 @@ extern "C" rs_status rs_adamw_step(const rs_layout* L, float* p, const float* g,
   k.inv = 1.0f / hp->grad_scale;
   const int64_t c0 = L->rank_chunk[k0], nc = L->rank_chunk[k1] - c0;
   if (nc == 0) return RS_OK;
-  hipLaunchKernelGGL(adamw_kernel, chunk_grid(nc), dim3(kThreads), 0,
+  hipLaunchKernelGGL(adamw_kernel<RS_ADAMW_SPLIT>, chunk_grid(nc * RS_ADAMW_SPLIT), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), table<ChunkDesc>(L, L->off_chunks), c0, nc,
                      p, g, m, v, k, tensor_mask, found_inf, L->m);
   return after_launch(fn);
@@ -1508,7 +1565,7 @@ extern "C" rs_status rs_sgd_step(const rs_layout* L, float* p, const float* g, f
   k.nesterov = hp->nesterov ? 1 : 0;
   const int64_t c0 = L->rank_chunk[k0], nc = L->rank_chunk[k1] - c0;
   if (nc == 0) return RS_OK;
-  hipLaunchKernelGGL(sgd_kernel, chunk_grid(nc), dim3(kThreads), 0,
+  hipLaunchKernelGGL(sgd_kernel<RS_SGD_SPLIT>, chunk_grid(nc * RS_SGD_SPLIT), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), table<ChunkDesc>(L, L->off_chunks), c0, nc,
                      p, g, buf, k, tensor_mask, found_inf, L->m);
   return after_launch(fn);

@@ -97,6 +97,7 @@ rs_status build(rs_layout* L) {
   L->rank_frag.assign(m + 1, 0);
   L->rank_tile.assign(m + 1, 0);
   L->rank_work.assign(m + 1, 0);
+  L->rank_min_tile_rows.assign(m, INT32_MAX);
 
   build_chunks(L, L->chunk_elems, L->chunks, L->rank_chunk, true);
   build_chunks(L, L->chunk_elems * kCoarseFactor, L->cchunks, L->rank_cchunk, false);
@@ -151,6 +152,7 @@ rs_status build(rs_layout* L) {
     L->rank_work[k] = int64_t(L->work.size());
     while (i < L->tiles.size() && L->tiles[i].rank == k) {
       const TileDesc& a = L->tiles[i];
+      L->rank_min_tile_rows[k] = std::min(L->rank_min_tile_rows[k], a.rows);
       const int team = team_for(int64_t(a.rows) * a.cols);
       const int vec = (a.cols % 4 == 0 && a.ld % 4 == 0 && a.buf_off % 4 == 0) ? 1 : 0;
       QuantWork w{int32_t(i), 0, team, vec};

@@ -165,6 +165,14 @@ def _mixed_small():
                                         nonfinite_frac=1e-3), 32, 16)
 
 
+def _bands():
+    """Tiles of 30 and 7 rows (every tile at least 4 rows, heights not
+    multiples of 4): dequantisation splits each tile into row bands here."""
+    ts = (W.TensorSpec("a", 90, 64, 30, 30, 32), W.TensorSpec("v", 1, 100, 0),
+          W.TensorSpec("b", 21, 48, 7, 7, 16), W.TensorSpec("c", 60, 40, 30, 30, 40))
+    return W.Workload("bands", ts, m=3, qfmt="int8", block=32)
+
+
 SMALL = {
     "toy": lambda: (W.toy_unit(), 16, 0),
     "toy_a1_c64": lambda: (W.toy_unit(), 1, 64),
@@ -175,6 +183,7 @@ SMALL = {
     "mixed_div": lambda: (_mixed_small(), 16, 512),
     "moe_div8": lambda: (_moe_small(), 16, 2048),
     "llama70b_div32": lambda: (W.scaled_workload(W.llama70b_layer(), 32, 32), 16, 0),
+    "bands": lambda: (_bands(), 16, 128),
 }
 
 _cases = {}
