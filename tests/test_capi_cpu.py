@@ -183,6 +183,29 @@ def test_planner_infeasible_cap_and_bad_args():
     assert "rs_plan" in R.rs_last_error()
 
 
+def test_plan_order_entry_points_reject_bad_args():
+    specs = [W.TensorSpec("a", 12, 1, 4), W.TensorSpec("b", 4, 2, 1)]
+    with pytest.raises(R.RsError) as e:
+        R.rs_plan_order(specs, 3)             # BEST is not a single order
+    assert e.value.status == -1 and "rs_plan_order" in R.rs_last_error()
+    with pytest.raises(R.RsError) as e:
+        R.rs_plan_ordered(specs, 2, 1, 7)
+    assert e.value.status == -1
+    with pytest.raises(R.RsError) as e:
+        R.rs_plan_ordered(specs, 0, 1, "best")
+    assert e.value.status == -1
+    with pytest.raises(R.RsError) as e:
+        R.rs_plan_ordered([W.TensorSpec("a", 0, 4, 0)], 2, 1, "given")
+    assert e.value.status == -1
+    # infeasible under the cap for every order
+    with pytest.raises(R.RsError) as e:
+        R.rs_plan_ordered(specs, 3, 1, "best", S_cap=3)
+    assert e.value.status == -4
+    # success clears the message
+    R.rs_plan_ordered(specs, 2, 1, "best")
+    assert R.rs_last_error() == ""
+
+
 def test_layout_create_validates():
     w = W.toy_unit()
     offs, info = R.rs_plan(w.tensors, w.m, 16)
