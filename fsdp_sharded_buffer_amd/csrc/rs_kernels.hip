@@ -64,11 +64,20 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 
 // ------------------------------------------------------- 8-element vectors
 
-// Tuning knobs (compile-time).  RS_UNROLL: 8-element vectors in flight per
-// lane in the copy and scale/add loops.  The *_NT switches choose, per
-// operation, whether streaming loads and stores carry the nontemporal hint
-// (measured on MI355X: it helps the pure streams - copies, the norm read -
-// and hurts the read-modify-write of scale/add).
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+//   RS_UNROLL        8-element vectors in flight per lane (copies, scale/add)
+//   RS_*_NT          per operation: nontemporal hint on streaming accesses;
+//                    it helps the pure streams (copies, the norm read,
+//                    quantisation input) and hurts read-modify-write
+//                    (scale/add, zero, the fp32 optimizers)
+//   RS_FILL_BYTES    bytes per workgroup of the unmasked zero: one 16-byte
+//                    store per lane, as many short workgroups write fastest
+//   RS_ADAMW_SPLIT,  workgroups per chunk of the AdamW / SGD steps
+//   RS_SGD_SPLIT
+//   RS_DEQ_SPLIT     row bands (workgroups) per dequantised tile
+//   RS_DEQ_LDS       stage a tile's codes in LDS before decoding
+//   RS_ADAM8_F       256-lane sub-blocks per 8-bit Adam work item
+//   RS_ADAM8_BATCH   8-bit Adam slots loaded ahead of their arithmetic
 #ifndef RS_UNROLL
 #define RS_UNROLL 2
 #endif
@@ -110,11 +119,6 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_ADAM8_NT
 #define RS_ADAM8_NT 1
-#endif
-#ifdef RS_ADAM8_WPE
-#define RS_ADAM8_ATTR __attribute__((amdgpu_waves_per_eu(RS_ADAM8_WPE)))
-#else
-#define RS_ADAM8_ATTR
 #endif
 
 
@@ -1110,7 +1114,7 @@ __device__ __forceinline__ float adam_p(float p, float m2, float v2, const AdamC
 }
 
 template <int FMT, int F>
-__global__ __launch_bounds__(kThreads* F) RS_ADAM8_ATTR void adamw8_kernel(
+__global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
     const QuantWork* __restrict__ work, int64_t w0, const TileDesc* __restrict__ tiles,
     float* __restrict__ p, const float* __restrict__ g, uint8_t* __restrict__ mc,
     float* __restrict__ ms, uint8_t* __restrict__ vc, float* __restrict__ vs, AdamConst k,
