@@ -180,6 +180,26 @@ def test_full_adamw(fx):
     del p, g, m, v
 
 
+@pytest.mark.timeout(600)
+def test_full_sgd(fx):
+    import torch
+    from oracle import optim as OP
+    R = fx.R
+    log(f"full sgd {fx.w.name}")
+    rng = np.random.default_rng(37)
+    b0 = (rng.standard_normal(fx.total) * 1e-3).astype(np.float32)
+    p = torch.from_numpy(fx.param_host).cuda()
+    g = torch.from_numpy(fx.grad_host).cuda()
+    b = torch.from_numpy(b0).cuda()
+    R.rs_sgd_step(fx.lay.handle, p, g, b, 0.05, 0.9, 1e-4, True, 1.0, None, None, 0, fx.m)
+    _sync()
+    ep, eb = OP.sgd_step(fx.param_host, fx.grad_host, b0, fx.items, fx.offsets, fx.S, fx.m, 0, fx.m,
+                         0.05, 0.9, 1e-4, True, 1.0)
+    assert_f32_equal_nan_class(to_np(p), ep, f"full sgd {fx.w.name} p")
+    assert_f32_equal_nan_class(to_np(b), eb, f"full sgd {fx.w.name} buf")
+    del p, g, b
+
+
 def _tile_sample(fx, rng, n_random):
     specs = fx.w.tensors
     nt = O.num_tiles(specs)
