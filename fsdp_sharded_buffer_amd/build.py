@@ -48,8 +48,8 @@ def build(verbose: bool = True) -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs,
-                   check=True)
+    subprocess.run([hipcc(), "-shared", "-fPIC", "-pthread", f"--offload-arch={ARCH}", "-o", tmp]
+                   + objs, check=True)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

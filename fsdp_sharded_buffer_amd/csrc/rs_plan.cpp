@@ -15,8 +15,11 @@
 // three cases appear in the per-rank step below.
 #include <algorithm>
 #include <chrono>
+#include <cstdlib>
 #include <cstring>
 #include <numeric>
+#include <system_error>
+#include <thread>
 
 #include "rs_internal.h"
 
@@ -74,6 +77,22 @@ int64_t earliest(int64_t lo, const PItem& it, int64_t S, int32_t m, int64_t A) {
   return -1;
 }
 
+// Candidates tried in order before the scan goes parallel, and candidates
+// per thread and round after that.
+constexpr int64_t kSequentialCandidates = 4096;
+constexpr int64_t kBlockCandidates = 2048;
+
+// Host threads for a long S scan: RS_PLAN_THREADS if set (>= 1), else the
+// hardware concurrency, at most 16.
+int plan_threads() {
+  if (const char* e = std::getenv("RS_PLAN_THREADS")) {
+    const int v = std::atoi(e);
+    if (v >= 1) return std::min(v, 64);
+  }
+  const unsigned hc = std::thread::hardware_concurrency();
+  return int(std::max(1u, std::min(hc, 16u)));
+}
+
 bool place_all(const std::vector<PItem>& items, int64_t S, int32_t m, int64_t A, int64_t* offs) {
   int64_t prev = 0;
   for (size_t t = 0; t < items.size(); ++t) {
@@ -106,25 +125,66 @@ rs_status plan_items(const std::vector<PItem>& items, int32_t m, int64_t align, 
   std::sort(by_len.begin(), by_len.end(), [](const PItem& a, const PItem& b) { return a.E > b.E; });
 
   *lb_out = lb;
-  for (int64_t S = lb; S <= cap;) {
-    int64_t next = S + align;
-    bool ok = true;
-    for (const PItem& it : by_len) {
-      if (it.E <= 2 * S) break;
-      if (S % it.g) {
-        // the aligned S that this tensor rejects run up to the next
-        // multiple of lcm(g, align) or to the first S with E <= 2S
-        ok = false;
-        const int64_t L = std::lcm(it.g, align);
-        next = std::max(next, std::min((S / L + 1) * L, round_up((it.E + 1) / 2, align)));
-        break;
+  // First feasible S in [lo, hi] (aligned), or -1; offsets into out.
+  auto scan = [&](int64_t lo, int64_t hi, int64_t* out) -> int64_t {
+    for (int64_t S = lo; S <= hi;) {
+      int64_t next = S + align;
+      bool ok = true;
+      for (const PItem& it : by_len) {
+        if (it.E <= 2 * S) break;
+        if (S % it.g) {
+          // the aligned S that this tensor rejects run up to the next
+          // multiple of lcm(g, align) or to the first S with E <= 2S
+          ok = false;
+          const int64_t L = std::lcm(it.g, align);
+          next = std::max(next, std::min((S / L + 1) * L, round_up((it.E + 1) / 2, align)));
+          break;
+        }
       }
+      if (ok && place_all(items, S, m, align, out)) return S;
+      S = next;
     }
-    if (ok && place_all(items, S, m, align, offs)) {
-      *S_out = S;
-      return RS_OK;
+    return -1;
+  };
+  // The first candidates in order; a long scan then goes on in rounds of
+  // consecutive blocks, one per host thread.  The earliest block with a
+  // feasible S holds the smallest one, so the result is the sequential
+  // scan's.
+  const int64_t head = std::min(cap, lb + kSequentialCandidates * align - align);
+  int64_t S = scan(lb, head, offs);
+  if (S < 0 && head < cap) {
+    const int T = plan_threads();
+    const int64_t block = kBlockCandidates * align;
+    std::vector<std::vector<int64_t>> outs(T, std::vector<int64_t>(n));
+    std::vector<int64_t> found(T);
+    for (int64_t base = head + align; base <= cap && S < 0; base += T * block) {
+      auto work = [&](int j) {
+        const int64_t lo = base + j * block;
+        found[j] = lo <= cap ? scan(lo, std::min(cap, lo + block - align), outs[j].data()) : -1;
+      };
+      if (T == 1) {
+        work(0);
+      } else {
+        std::vector<std::thread> pool;
+        int j = 0;
+        try {
+          for (; j < T; ++j) pool.emplace_back(work, j);
+        } catch (const std::system_error&) {  // no more threads: finish inline
+          for (; j < T; ++j) work(j);
+        }
+        for (std::thread& t : pool) t.join();
+      }
+      for (int j = 0; j < T; ++j)
+        if (found[j] >= 0) {
+          S = found[j];
+          std::copy(outs[j].begin(), outs[j].end(), offs);
+          break;
+        }
     }
-    S = next;
+  }
+  if (S >= 0) {
+    *S_out = S;
+    return RS_OK;
   }
   return fail(RS_ERR_INFEASIBLE, "rs_plan: no layout with S <= " + std::to_string(cap));
 }

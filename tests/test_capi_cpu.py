@@ -138,6 +138,22 @@ def test_plan_ordered_matches_oracle_random_and_study_cases():
             assert (perm, offs, info["S"]) == (o[0], o[1], o[2]), (name, m, k)
 
 
+def test_parallel_scan_equals_sequential(monkeypatch):
+    """Long S scans (thousands of candidates past the lower bound) run in
+    blocks on host threads; the plan must be the single-threaded one.  The
+    separate-expert unit at 128-row granules and m = 128 scans about 130K
+    candidates."""
+    moe = W.WORKLOADS["moe_experts"]
+    cases = [(W.regranulated(moe.tensors, 128), 128), (W.regranulated(moe.tensors, 16), 256)]
+    got = {}
+    for th in ("1", "7"):
+        monkeypatch.setenv("RS_PLAN_THREADS", th)
+        got[th] = [R.rs_plan_ordered(sp, m, 1, "best") for sp, m in cases]
+    for a, b in zip(got["1"], got["7"]):
+        assert a[0] == b[0] and a[1] == b[1] and a[2]["S"] == b[2]["S"]
+        assert a[2]["S"] - a[2]["lower_bound"] > 4096      # the threaded path ran
+
+
 def test_lcm_of_granules_sets_S():
     """Llama-8B layer, 16-row granules, 64 ranks: Wgate, Wup (14336x4096) and
     Wdown (4096x14336) are each longer than 2S, so S must be a multiple of
