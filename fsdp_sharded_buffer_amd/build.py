@@ -56,8 +56,8 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
-PROBE_SRC = os.path.join(ROOT, "tests", "native", "e4m3_probe.hip")
-PROBE_LIB = os.path.join(ROOT, "tests", "native", "libe4m3_probe.so")
+PROBE_SRC = os.path.join(ROOT, "tests", "native", "hw_probes.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "native", "libhw_probes.so")
 
 
 def build_probe(verbose: bool = True) -> str:

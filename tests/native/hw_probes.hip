@@ -1,8 +1,8 @@
-// Test-only probe: applies gfx950's packed fp32 -> OCP E4M3 conversion
-// (the instruction the block quantisation fast path uses) to consecutive
-// fp32 bit patterns, four at a time exactly as the kernel packs a word, so
-// a test can compare every input of the fast path's domain with the CPU
-// oracle.  Not part of librs.so.
+// Test-only probe of device arithmetic the kernels rely on; not part of
+// librs.so: gfx950's packed fp32 -> OCP E4M3 conversion (the block
+// quantisation fast path), applied to consecutive fp32 bit patterns four at
+// a time exactly as the kernel packs a word, so a test can compare every
+// input of the fast path's domain with the CPU oracle.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

@@ -16,7 +16,7 @@ from harness import log
 
 pytestmark = pytest.mark.gpu
 
-LIB = os.path.join(os.path.dirname(__file__), "native", "libe4m3_probe.so")
+LIB = os.path.join(os.path.dirname(__file__), "native", "libhw_probes.so")
 LO, HI = 0x3C800010, 0x43E80000     # the fast path's |q| bit-pattern domain
 CHUNK = 1 << 24
 
@@ -57,3 +57,4 @@ def test_e4m3_instruction_equals_oracle_on_fast_path_domain():
     bad = [r for r in results if isinstance(r, str)]
     assert not bad, bad[0]
     assert sum(results) == 2 * (HI - LO)
+
