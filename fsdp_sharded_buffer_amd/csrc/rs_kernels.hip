@@ -1453,7 +1453,7 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
     return fail(RS_ERR_DTYPE, "rs_block_quant: fmt must be RS_Q_FP8_E4M3 or RS_Q_INT8");
   RS_TRY(check_ptr(x, 4, fn, "x"));
   RS_TRY(check_ptr(codes, 1, fn, "codes"));
-  RS_TRY(check_ptr(scales, 4, fn, "scales"));
+  if (!L->tiles.empty()) RS_TRY(check_ptr(scales, 4, fn, "scales"));  // no tiles: may be null
   if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
   // the 16-byte path needs x 16-byte aligned and codes 4-byte aligned
   const int vec_ok = (reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
@@ -1481,7 +1481,7 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
     return fail(RS_ERR_DTYPE, "rs_block_dequant: fmt must be RS_Q_FP8_E4M3 or RS_Q_INT8");
   if (!float_kind(y_dt)) return fail(RS_ERR_DTYPE, "rs_block_dequant: y must be RS_F32 or RS_BF16");
   RS_TRY(check_ptr(codes, 1, fn, "codes"));
-  RS_TRY(check_ptr(scales, 4, fn, "scales"));
+  if (!L->tiles.empty()) RS_TRY(check_ptr(scales, 4, fn, "scales"));  // no tiles: may be null
   RS_TRY(check_ptr(y, y_dt == RS_F32 ? 4 : 2, fn, "y"));
   const uintptr_t ca = reinterpret_cast<uintptr_t>(codes), ya = reinterpret_cast<uintptr_t>(y);
   int vec_ok = (ca % 4 == 0 && ya % (y_dt == RS_F32 ? 16 : 8) == 0) ? 1 : 0;
@@ -1589,8 +1589,10 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
   RS_TRY(check_ptr(g, 4, fn, "g"));
   RS_TRY(check_ptr(m_codes, 1, fn, "m_codes"));
   RS_TRY(check_ptr(v_codes, 1, fn, "v_codes"));
-  RS_TRY(check_ptr(m_scales, 4, fn, "m_scales"));
-  RS_TRY(check_ptr(v_scales, 4, fn, "v_scales"));
+  if (!L->tiles.empty()) {  // no tiles: the scale arrays may be null
+    RS_TRY(check_ptr(m_scales, 4, fn, "m_scales"));
+    RS_TRY(check_ptr(v_scales, 4, fn, "v_scales"));
+  }
   if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
   if (!(hp->bias_correction1 > 0.0f) || !(hp->bias_correction2 > 0.0f) || !(hp->grad_scale != 0.0f))
     return fail(RS_ERR_INVALID_ARG, "rs_adamw8_step: bias corrections must be > 0, grad_scale != 0");

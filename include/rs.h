@@ -261,7 +261,8 @@ rs_status rs_ragged_sqnorm(const rs_layout* layout, const float* x, double* sq, 
  *   x       device fp32, m*S elements
  *   codes   device uint8, m*S bytes: codes[p] encodes x[p]; positions of
  *           padding and of tensors that are not quantised are not written
- *   scales  device fp32 [info.num_tiles]: tiles numbered tensor by tensor
+ *   scales  device fp32 [info.num_tiles] (may be NULL when num_tiles is 0):
+ *           tiles numbered tensor by tensor
  *           (quantised tensors only, in group order), row-major inside a
  *           tensor; only tiles in the range are written
  *   found_inf device uint32 [m] or NULL: found_inf[k] is set to 1 when a
@@ -279,7 +280,7 @@ rs_status rs_block_quant(const rs_layout* layout, const float* x, rs_qfmt fmt, u
  * even).  Positions of padding and of tensors that are not quantised are not
  * written.
  *   codes   device uint8, m*S bytes (as written by rs_block_quant)
- *   scales  device fp32 [info.num_tiles]
+ *   scales  device fp32 [info.num_tiles] (may be NULL when num_tiles is 0)
  *   y       device, m*S elements of y_dt (RS_F32 or RS_BF16) */
 rs_status rs_block_dequant(const rs_layout* layout, const uint8_t* codes, rs_qfmt fmt,
                            const float* scales, void* y, rs_dtype y_dt, int32_t k0, int32_t k1,
@@ -321,7 +322,8 @@ rs_status rs_adamw_step(const rs_layout* layout, float* p, const float* g, float
  * with rs_adamw_step and a tensor mask).  found_inf as in rs_adamw_step.
  *   p, g               device fp32, m*S elements (buffer layout)
  *   m_codes, v_codes   device uint8, m*S bytes, in place
- *   m_scales, v_scales device fp32 [info.num_tiles], in place
+ *   m_scales, v_scales device fp32 [info.num_tiles], in place (may be NULL
+ *                      when num_tiles is 0)
  *   fmt                RS_Q_INT8 or RS_Q_FP8_E4M3 */
 rs_status rs_adamw8_step(const rs_layout* layout, float* p, const float* g, uint8_t* m_codes,
                          float* m_scales, uint8_t* v_codes, float* v_scales, rs_qfmt fmt,

@@ -173,6 +173,27 @@ def _bands():
     return W.Workload("bands", ts, m=3, qfmt="int8", block=32)
 
 
+def _pad_ranks():
+    """One 4x8 tensor whose granule is the whole tensor, on 4 ranks: rank 0
+    holds it, ranks 1-3 are padding only."""
+    return W.Workload("pad_ranks", (W.TensorSpec("a", 4, 8, 4, 4, 8),), m=4, qfmt="fp8_e4m3",
+                      block=8)
+
+
+def _tiny():
+    """One-element tensors, a 3-element vector and a row-granular 3x5 tensor
+    with 1x5 tiles, on 3 ranks."""
+    ts = (W.TensorSpec("a", 1, 1, 0), W.TensorSpec("b", 1, 1, 0), W.TensorSpec("c", 3, 5, 1, 1, 5),
+          W.TensorSpec("d", 1, 3, 0))
+    return W.Workload("tiny", ts, m=3, qfmt="int8", block=5)
+
+
+def _no_quant():
+    """Vectors only: no quantisation tiles at all."""
+    ts = (W.TensorSpec("v1", 1, 1000, 0), W.TensorSpec("v2", 1, 77, 0))
+    return W.Workload("no_quant", ts, m=2, qfmt="fp8_e4m3", block=1)
+
+
 SMALL = {
     "toy": lambda: (W.toy_unit(), 16, 0),
     "toy_a1_c64": lambda: (W.toy_unit(), 1, 64),
@@ -184,6 +205,11 @@ SMALL = {
     "moe_div8": lambda: (_moe_small(), 16, 2048),
     "llama70b_div32": lambda: (W.scaled_workload(W.llama70b_layer(), 32, 32), 16, 0),
     "bands": lambda: (_bands(), 16, 128),
+    "single_rank": lambda: (W.Workload("toy_m1", W.toy_unit().tensors, m=1, qfmt="fp8_e4m3",
+                                       block=32), 16, 0),
+    "pad_ranks": lambda: (_pad_ranks(), 1, 64),
+    "tiny": lambda: (_tiny(), 1, 64),
+    "no_quant": lambda: (_no_quant(), 16, 128),
 }
 
 _cases = {}

@@ -467,3 +467,22 @@ def test_block_quant_found_inf():
     R.rs_block_quant(c.lay.handle, from_np(x0), R.RS_Q_INT8, codes, scales, 0, c.m, found_inf=fi)
     _sync()
     assert np.array_equal(to_np(fi).astype(np.uint32), ef)
+
+
+def test_no_tiles_accepts_null_scales():
+    """A layout without quantisation tiles: quantise, dequantise and the
+    8-bit step accept NULL scale arrays and write nothing."""
+    import torch
+    c = case("no_quant")
+    R = c.R
+    assert c.lay.info["num_tiles"] == 0
+    x = from_np(c.flat(c.inputs().grads))
+    codes = torch.full((c.total,), U8_CANARY, dtype=torch.uint8, device="cuda")
+    y = torch.full((c.total,), 3.0, dtype=torch.float32, device="cuda")
+    for fmt in (R.RS_Q_FP8_E4M3, R.RS_Q_INT8):
+        R.rs_block_quant(c.lay.handle, x, fmt, codes, None, 0, c.m)
+        R.rs_block_dequant(c.lay.handle, codes, fmt, None, y, R.RS_F32, 0, c.m)
+        R.rs_adamw8_step(c.lay.handle, y, x, codes, None, codes, None, fmt, 1e-3, 0.9, 0.95, 1e-8, 0.0,
+                         0.5, 0.5, 1.0, None, 0, c.m)
+    _sync()
+    assert bool((codes == U8_CANARY).all()) and bool((y == 3.0).all())
