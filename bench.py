@@ -53,6 +53,29 @@ def op_bytes(w, S, n_tiles):
     }
 
 
+def rank_bytes(w, offs, S):
+    """Algorithmic bytes of each operation over one rank's shard [kS, (k+1)S):
+    the tensor elements and quantisation tiles that fall in it."""
+    m = w.m
+    E = np.zeros(m, np.int64)
+    Eq = np.zeros(m, np.int64)
+    tiles = np.zeros(m, np.int64)
+    for t, l in zip(w.tensors, offs):
+        for k in range(l // S, (l + t.numel - 1) // S + 1):
+            n = min(l + t.numel, (k + 1) * S) - max(l, k * S)
+            E[k] += n
+            if t.q_rows:
+                Eq[k] += n
+        if t.q_rows:
+            r0 = np.arange(0, t.rows, t.q_rows, dtype=np.int64)
+            c0 = np.arange(0, t.cols, t.q_cols, dtype=np.int64)
+            first = l + r0[:, None] * t.cols + c0[None, :]
+            tiles += np.bincount((first // S).reshape(-1), minlength=m)
+    return [{"pack": 4 * int(E[k]) + 2 * S, "unpack": 4 * int(E[k]), "scale_add": 12 * int(E[k]),
+             "sqnorm": 4 * int(E[k]), "block_quant": 5 * int(Eq[k]) + 4 * int(tiles[k]),
+             "zero": 4 * S} for k in range(m)]
+
+
 def extra_bytes(w, S, n_tiles):
     """Algorithmic bytes of the operations measured beside the step."""
     Eq = sum(t.numel for t in w.tensors if t.q_rows)
@@ -187,6 +210,8 @@ def main():
     ap.add_argument("--only", default="", help="comma list of ops to time per op (default all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) to scale HBM counters")
+    ap.add_argument("--per-rank", action="store_true",
+                    help="also time each operation on one rank's shard, cycling over the ranks")
     ap.add_argument("--no-torch-ref", action="store_true",
                     help="skip timing torch's own copy/axpy/fill/fused optimizers for context")
     ap.add_argument("--padding-study", action="store_true",
@@ -236,15 +261,17 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
-    ops = {
-        "pack": lambda: R.rs_pack(h, ptab, R.RS_F32, pbuf, R.RS_BF16, 0, m, sp),
-        "unpack": lambda: R.rs_unpack(h, pbuf, R.RS_BF16, otab, R.RS_BF16, 0, m, sp),
-        "scale_add": lambda: R.rs_group_scale_add(h, acc, grad, R.RS_F32, 1.0, 1.0, None, found,
-                                                  0, m, sp),
-        "sqnorm": lambda: R.rs_ragged_sqnorm(h, acc, sq, None, None, lay.ws, 0, m, sp),
-        "block_quant": lambda: R.rs_block_quant(h, acc, qfmt, codes, scales, 0, m, sp),
-        "zero": lambda: R.rs_group_zero(h, grad, R.RS_F32, None, 0, m, sp),
+    # each operation over ranks [a, b)
+    ranged = {
+        "pack": lambda a, b: R.rs_pack(h, ptab, R.RS_F32, pbuf, R.RS_BF16, a, b, sp),
+        "unpack": lambda a, b: R.rs_unpack(h, pbuf, R.RS_BF16, otab, R.RS_BF16, a, b, sp),
+        "scale_add": lambda a, b: R.rs_group_scale_add(h, acc, grad, R.RS_F32, 1.0, 1.0, None,
+                                                       found, a, b, sp),
+        "sqnorm": lambda a, b: R.rs_ragged_sqnorm(h, acc, sq, None, None, lay.ws, a, b, sp),
+        "block_quant": lambda a, b: R.rs_block_quant(h, acc, qfmt, codes, scales, a, b, sp),
+        "zero": lambda a, b: R.rs_group_zero(h, grad, R.RS_F32, None, a, b, sp),
     }
+    ops = {name: (lambda f=f: f(0, m)) for name, f in ranged.items()}
     nbytes = op_bytes(w, S, lay.info["num_tiles"])
     deq = torch.empty(total, dtype=torch.float32, device=dev)
     mom = torch.zeros(total, dtype=torch.float32, device=dev)
@@ -322,12 +349,45 @@ def main():
     for name in only:
         f = allops[name]
         med, samples, reps = event_ms(f, args.samples)
+        p90 = float(np.percentile(samples, 90))
         gbs = allbytes[name] / (med * 1e-3) / 1e9
         (per_op if name in ops else per_extra)[name] = {
             "us": round(med * 1e3, 2), "min_us": round(min(samples) * 1e3, 2),
+            "p90_us": round(p90 * 1e3, 2),
             "bytes": allbytes[name], "GB/s": round(gbs, 1),
             "frac_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps}
         log(f"{name:12s} {med*1e3:9.1f} us  {gbs:8.1f} GB/s  {gbs/HBM_PEAK_GBS*100:5.1f}% of peak")
+
+    # one rank's shard: launches over [k, k+1), cycling k so that each
+    # launch reads other memory than the last.  The mean comes from whole
+    # cycles timed at their ends only; the slowest rank from a pass with an
+    # event between launches (which adds the events' own cost to it).
+    per_rank = None
+    if args.per_rank:
+        rb = rank_bytes(w, offs, S)
+        per_rank = {}
+        for name, f in ranged.items():
+            cycle = lambda f=f: [f(k, k + 1) for k in range(m)]
+            med, _, _ = event_ms(cycle, args.samples)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(m + 1)]
+            times = [[] for _ in range(m)]
+            for _ in range(5):
+                ev[0].record(stream)
+                for k in range(m):
+                    f(k, k + 1)
+                    ev[k + 1].record(stream)
+                ev[m].synchronize()
+                for k in range(m):
+                    times[k].append(ev[k].elapsed_time(ev[k + 1]))
+            each = np.array([np.median(t) for t in times])
+            worst = int(np.argmax(each))
+            byt = sum(rb[k][name] for k in range(m))
+            per_rank[name] = {
+                "mean_us": round(med / m * 1e3, 2),
+                "GB/s": round(byt / (med * 1e-3) / 1e9, 1),
+                "slowest_rank": worst, "slowest_us_with_events": round(float(each[worst]) * 1e3, 2)}
+            log(f"per rank {name:12s} mean {med / m * 1e3:8.1f} us  {per_rank[name]['GB/s']:8.1f} GB/s; "
+                f"slowest rank {worst}")
 
     timed = dict(per_op, **per_extra)
     dom = "scale_add" if "scale_add" in timed else next(iter(timed))
@@ -389,6 +449,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "torch_reference": ref,
+        "per_rank": per_rank,
         "device": torch.cuda.get_device_name(0),
         "host": platform.processor() or platform.machine(),
     }

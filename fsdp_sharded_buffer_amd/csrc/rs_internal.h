@@ -47,26 +47,26 @@ static_assert(sizeof(TensorDesc) == 16, "TensorDesc layout");
 
 // One quantisation tile: rows x cols elements at buffer position buf_off
 // with row stride ld; its scale goes to scales[scale_idx].
-struct TileDesc {
-  int64_t buf_off;
-  int64_t ld;
-  int32_t rows;
-  int32_t cols;
-  int32_t scale_idx;
-  int32_t rank;
-};
-static_assert(sizeof(TileDesc) == 32, "TileDesc layout");
-
-// One workgroup of the quantisation kernel: `count` consecutive tiles, each
-// handled by a team of `team` lanes (power of two, 8..256); vec = 1 when
-// every tile of the item allows 16-byte loads.
+// One workgroup of the tile kernels (quantise, dequantise, 8-bit Adam): a
+// run of `count` consecutive tiles of one tensor in row-major tile order,
+// all in one rank and with the same team size and vector flag.  Tile j of
+// the run is tile (t0 + j) of the tensor; lanes [j*team, (j+1)*team) take
+// it.  Kernels derive each tile's place and shape from these fields, so no
+// per-tile table is read.
 struct QuantWork {
-  int32_t tile_begin;
-  int32_t count;
-  int32_t team;
-  int32_t vec;
+  int64_t base;            // buffer offset of the tensor
+  int32_t t0;              // first tile (row-major index within the tensor)
+  int32_t count;           // tiles in the run (<= 256 / team)
+  int32_t team;            // lanes per tile
+  int32_t vec;             // 1: every tile of the run allows 16-byte access
+  int32_t rows, cols;      // tensor shape; cols is the leading dimension
+  int32_t q_rows, q_cols;  // tile shape (edge tiles are clipped)
+  int32_t ntc;             // tiles per tile row
+  int32_t scale0;          // scale index of tile t0
+  int32_t rank;            // rank holding the run
+  int32_t pad[3];
 };
-static_assert(sizeof(QuantWork) == 16, "QuantWork layout");
+static_assert(sizeof(QuantWork) == 64, "QuantWork layout");
 
 constexpr int kMaxTileElems = 16384;  // 256 lanes x 64 elements held in registers
 #ifndef RS_DEFAULT_CHUNK
@@ -91,15 +91,15 @@ struct rs_layout {
   std::vector<rs::FragDesc> frags;
   std::vector<rs::ChunkDesc> chunks;   // fine chunks (copies, scale/add)
   std::vector<rs::ChunkDesc> cchunks;  // coarse chunks (norms, masked zero)
-  std::vector<rs::TileDesc> tiles;
+  int64_t num_tiles = 0;
   std::vector<rs::QuantWork> work;
 
   // per-rank begin indices, size m + 1
-  std::vector<int64_t> rank_chunk, rank_cchunk, rank_frag, rank_tile, rank_work;
+  std::vector<int64_t> rank_chunk, rank_cchunk, rank_frag, rank_work;
   std::vector<int32_t> rank_min_tile_rows;  // per rank; INT32_MAX when it has no tile
 
   // byte offsets of each table inside the device blob
-  size_t off_tensors = 0, off_frags = 0, off_chunks = 0, off_cchunks = 0, off_tiles = 0,
+  size_t off_tensors = 0, off_frags = 0, off_chunks = 0, off_cchunks = 0,
          off_work = 0;
   size_t device_bytes = 0;
   size_t workspace_bytes = 0;

@@ -589,6 +589,26 @@ struct SlotWalk {
   }
 };
 
+// Place and shape of tile j of a work item (a run of consecutive tiles of
+// one tensor; edge tiles clipped).
+struct Tile {
+  int64_t buf_off, ld;
+  int rows, cols, scale_idx;
+};
+
+__device__ __forceinline__ Tile tile_of(const QuantWork& w, int j) {
+  const int idx = w.t0 + j;
+  const int tr = idx / w.ntc, tc = idx - tr * w.ntc;
+  const int r0 = tr * w.q_rows, c0 = tc * w.q_cols;
+  Tile t;
+  t.buf_off = w.base + int64_t(r0) * w.cols + c0;
+  t.ld = w.cols;
+  t.rows = min(w.q_rows, w.rows - r0);
+  t.cols = min(w.q_cols, w.cols - c0);
+  t.scale_idx = w.scale0 + j;
+  return t;
+}
+
 // Each workgroup takes `count` consecutive tiles; tile j of the item is
 // handled by lanes [j*team, (j+1)*team).  On the 16-byte path a lane keeps
 // its (at most 64) elements in registers between the absmax and the encode
@@ -596,7 +616,6 @@ struct SlotWalk {
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __restrict__ work,
                                                          int64_t w0,
-                                                         const TileDesc* __restrict__ tiles,
                                                          const float* __restrict__ x,
                                                          uint8_t* __restrict__ codes,
                                                          float* __restrict__ scales,
@@ -609,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
   const int slot = threadIdx.x / team;
   const int lane = threadIdx.x % team;
   const bool active = slot < w.count;
-  const TileDesc td = tiles[w.tile_begin + (active ? slot : 0)];
+  const Tile td = tile_of(w, active ? slot : 0);
   const float* base = x + td.buf_off;
   uint8_t* cbase = codes + td.buf_off;
   float v[64];
@@ -658,13 +677,16 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
   if (lane == 0) {
     scales[td.scale_idx] = scale;
     // an Inf or NaN |x| pattern is >= the +Inf pattern
-    if (found_inf && amax >= 0x7f800000u) found_inf[td.rank] = 1u;
+    if (found_inf && amax >= 0x7f800000u) found_inf[w.rank] = 1u;
   }
   const bool zero_tile = scale == 0.0f;
   const float rcp = 1.0f / scale;
   // the reciprocal path needs a normal, finite scale (and so a finite rcp)
   const uint32_t sb = __float_as_uint(scale);
   const bool fast = sb >= 0x00800000u && sb < 0x7f800000u;
+  // an Inf scale (an Inf but no NaN in the tile): rcp = 0 and x * 0 is
+  // exactly x / Inf for every x of the tile (+-0, or NaN for +-Inf)
+  const bool inf_scale = sb == 0x7f800000u;
   if (!vec) {
     for (int e = lane; e < ne; e += team) {
       const int r = e / td.cols;
@@ -684,7 +706,16 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
         for (int j = 0; j < 4; ++j) q[j] = v[4 * i + j] * rcp;
         bool safe = fast;
         uint32_t word;
-        if constexpr (FMT == RS_Q_FP8_E4M3) {
+        if (!fast) {  // tile-uniform: codes that need no division, else exact
+          safe = zero_tile || nan_tile || inf_scale;
+          if (zero_tile)
+            word = 0u;
+          else if (nan_tile)
+            word = FMT == RS_Q_FP8_E4M3 ? 0x7f7f7f7fu : 0u;
+          else
+            word = encode<FMT>(q[0]) | (encode<FMT>(q[1]) << 8) | (encode<FMT>(q[2]) << 16) |
+                   (encode<FMT>(q[3]) << 24);
+        } else if constexpr (FMT == RS_Q_FP8_E4M3) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) safe = safe && e4m3_safe(u32(q[j]));
           word = e4m3_pack4_normal(q[0], q[1], q[2], q[3]);
@@ -771,7 +802,6 @@ __device__ __forceinline__ void store4(char* yb, int64_t elem, const float d[4],
 template <int FMT, int YK, int F>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const QuantWork* __restrict__ work,
                                                            int64_t w0,
-                                                           const TileDesc* __restrict__ tiles,
                                                            const uint8_t* __restrict__ codes,
                                                            const float* __restrict__ scales,
                                                            void* __restrict__ y, int vec_ok) {
@@ -781,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const QuantWork* __re
   const int slot = threadIdx.x / team;
   const int lane = threadIdx.x % team;
   const bool active = slot < w.count;
-  TileDesc td = tiles[w.tile_begin + (active ? slot : 0)];
+  Tile td = tile_of(w, active ? slot : 0);
   const float scale = scales[td.scale_idx];
   if (F > 1) {
     const int rp = (td.rows + F - 1) / F;
@@ -1115,8 +1145,7 @@ __device__ __forceinline__ float adam_p(float p, float m2, float v2, const AdamC
 
 template <int FMT, int F>
 __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
-    const QuantWork* __restrict__ work, int64_t w0, const TileDesc* __restrict__ tiles,
-    float* __restrict__ p, const float* __restrict__ g, uint8_t* __restrict__ mc,
+    const QuantWork* __restrict__ work, int64_t w0, float* __restrict__ p, const float* __restrict__ g, uint8_t* __restrict__ mc,
     float* __restrict__ ms, uint8_t* __restrict__ vc, float* __restrict__ vs, AdamConst k,
     const uint32_t* __restrict__ found_inf, int m_ranks, int vec_ok) {
   constexpr int NS = 16 / F;  // slots per lane
@@ -1131,7 +1160,7 @@ __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
   const int slot = tt / team;
   const int lane = tt % team;
   const bool active = slot < w.count;
-  const TileDesc td = tiles[w.tile_begin + (active ? slot : 0)];
+  const Tile td = tile_of(w, active ? slot : 0);
   const int64_t o0 = td.buf_off;
   const float sm_old = ms[td.scale_idx], sv_old = vs[td.scale_idx];
   const int c4 = td.cols >> 2;
@@ -1453,7 +1482,7 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
     return fail(RS_ERR_DTYPE, "rs_block_quant: fmt must be RS_Q_FP8_E4M3 or RS_Q_INT8");
   RS_TRY(check_ptr(x, 4, fn, "x"));
   RS_TRY(check_ptr(codes, 1, fn, "codes"));
-  if (!L->tiles.empty()) RS_TRY(check_ptr(scales, 4, fn, "scales"));  // no tiles: may be null
+  if (L->num_tiles > 0) RS_TRY(check_ptr(scales, 4, fn, "scales"));  // no tiles: may be null
   if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
   // the 16-byte path needs x 16-byte aligned and codes 4-byte aligned
   const int vec_ok = (reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
@@ -1464,11 +1493,10 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
   const dim3 g(static_cast<unsigned>(nw)), b(kThreads);
   if (fmt == RS_Q_FP8_E4M3)
     hipLaunchKernelGGL((quant_kernel<RS_Q_FP8_E4M3>), g, b, 0, s,
-                       table<QuantWork>(L, L->off_work), w0, table<TileDesc>(L, L->off_tiles), x,
-                       codes, scales, found_inf, vec_ok);
+                       table<QuantWork>(L, L->off_work), w0, x, codes, scales, found_inf, vec_ok);
   else
     hipLaunchKernelGGL((quant_kernel<RS_Q_INT8>), g, b, 0, s, table<QuantWork>(L, L->off_work),
-                       w0, table<TileDesc>(L, L->off_tiles), x, codes, scales, found_inf, vec_ok);
+                       w0, x, codes, scales, found_inf, vec_ok);
   return after_launch(fn);
 }
 
@@ -1481,7 +1509,7 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
     return fail(RS_ERR_DTYPE, "rs_block_dequant: fmt must be RS_Q_FP8_E4M3 or RS_Q_INT8");
   if (!float_kind(y_dt)) return fail(RS_ERR_DTYPE, "rs_block_dequant: y must be RS_F32 or RS_BF16");
   RS_TRY(check_ptr(codes, 1, fn, "codes"));
-  if (!L->tiles.empty()) RS_TRY(check_ptr(scales, 4, fn, "scales"));  // no tiles: may be null
+  if (L->num_tiles > 0) RS_TRY(check_ptr(scales, 4, fn, "scales"));  // no tiles: may be null
   RS_TRY(check_ptr(y, y_dt == RS_F32 ? 4 : 2, fn, "y"));
   const uintptr_t ca = reinterpret_cast<uintptr_t>(codes), ya = reinterpret_cast<uintptr_t>(y);
   int vec_ok = (ca % 4 == 0 && ya % (y_dt == RS_F32 ? 16 : 8) == 0) ? 1 : 0;
@@ -1495,14 +1523,13 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
   const bool split = RS_DEQ_SPLIT > 1 && min_rows >= RS_DEQ_SPLIT;
   const dim3 g(static_cast<unsigned>(split ? nw * RS_DEQ_SPLIT : nw)), b(kThreads);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
-  const TileDesc* tl = table<TileDesc>(L, L->off_tiles);
 #define RS_DEQ_LAUNCH(FM, YK)                                                                 \
   do {                                                                                        \
     if (split)                                                                                \
-      hipLaunchKernelGGL((dequant_kernel<FM, YK, RS_DEQ_SPLIT>), g, b, 0, s, wk, w0, tl, codes, \
+      hipLaunchKernelGGL((dequant_kernel<FM, YK, RS_DEQ_SPLIT>), g, b, 0, s, wk, w0, codes,     \
                          scales, y, vec_ok);                                                  \
     else                                                                                      \
-      hipLaunchKernelGGL((dequant_kernel<FM, YK, 1>), g, b, 0, s, wk, w0, tl, codes, scales, y, \
+      hipLaunchKernelGGL((dequant_kernel<FM, YK, 1>), g, b, 0, s, wk, w0, codes, scales, y,     \
                          vec_ok);                                                             \
   } while (0)
   if (fmt == RS_Q_FP8_E4M3 && y_dt == RS_F32)
@@ -1589,7 +1616,7 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
   RS_TRY(check_ptr(g, 4, fn, "g"));
   RS_TRY(check_ptr(m_codes, 1, fn, "m_codes"));
   RS_TRY(check_ptr(v_codes, 1, fn, "v_codes"));
-  if (!L->tiles.empty()) {  // no tiles: the scale arrays may be null
+  if (L->num_tiles > 0) {  // no tiles: the scale arrays may be null
     RS_TRY(check_ptr(m_scales, 4, fn, "m_scales"));
     RS_TRY(check_ptr(v_scales, 4, fn, "v_scales"));
   }
@@ -1616,12 +1643,11 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 gr(static_cast<unsigned>(nw)), b(kThreads * RS_ADAM8_F);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
-  const TileDesc* tl = table<TileDesc>(L, L->off_tiles);
   if (fmt == RS_Q_FP8_E4M3)
-    hipLaunchKernelGGL((adamw8_kernel<RS_Q_FP8_E4M3, RS_ADAM8_F>), gr, b, 0, s, wk, w0, tl, p, g,
+    hipLaunchKernelGGL((adamw8_kernel<RS_Q_FP8_E4M3, RS_ADAM8_F>), gr, b, 0, s, wk, w0, p, g,
                        m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
   else
-    hipLaunchKernelGGL((adamw8_kernel<RS_Q_INT8, RS_ADAM8_F>), gr, b, 0, s, wk, w0, tl, p, g,
+    hipLaunchKernelGGL((adamw8_kernel<RS_Q_INT8, RS_ADAM8_F>), gr, b, 0, s, wk, w0, p, g,
                        m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
   return after_launch(fn);
 }

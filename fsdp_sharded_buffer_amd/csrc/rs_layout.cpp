@@ -92,10 +92,9 @@ rs_status build(rs_layout* L) {
   const int64_t S = L->S;
   L->tensors.assign(n, TensorDesc{});
   L->frags.clear();
-  L->tiles.clear();
   L->work.clear();
+  L->num_tiles = 0;
   L->rank_frag.assign(m + 1, 0);
-  L->rank_tile.assign(m + 1, 0);
   L->rank_work.assign(m + 1, 0);
   L->rank_min_tile_rows.assign(m, INT32_MAX);
 
@@ -118,57 +117,68 @@ rs_status build(rs_layout* L) {
     td.rank_hi = L->frags[f].rank + 1;
   }
 
-  // quantisation tiles, tensor by tensor, row-major; ranks are
-  // non-decreasing in this order because tensors and tile rows are
-  int32_t scale_idx = 0;
+  // quantisation tiles, tensor by tensor, row-major (ranks are
+  // non-decreasing in this order because tensors and tile rows are), cut
+  // into runs of consecutive tiles of one tensor and rank with the same team
+  // size and vector flag
+  int64_t scale_idx = 0;
+  bool open = false;
+  QuantWork cur{};
   for (int32_t t = 0; t < n; ++t) {
     const rs_tensor_spec& s = L->specs[t];
     if (s.q_rows <= 0) continue;
-    for (int64_t r0 = 0; r0 < s.rows; r0 += s.q_rows) {
-      const int64_t r1 = std::min(s.rows, r0 + s.q_rows);
-      for (int64_t c0 = 0; c0 < s.cols; c0 += s.q_cols) {
-        const int64_t c1 = std::min(s.cols, c0 + s.q_cols);
-        TileDesc td;
-        td.buf_off = L->offsets[t] + r0 * s.cols + c0;
-        td.ld = s.cols;
-        td.rows = int32_t(r1 - r0);
-        td.cols = int32_t(c1 - c0);
-        td.scale_idx = scale_idx++;
-        const int64_t last = L->offsets[t] + (r1 - 1) * s.cols + (c1 - 1);
-        td.rank = int32_t(td.buf_off / S);
-        if (last / S != td.buf_off / S)
+    const int64_t l = L->offsets[t];
+    const int64_t ntr = (s.rows + s.q_rows - 1) / s.q_rows, ntc = (s.cols + s.q_cols - 1) / s.q_cols;
+    for (int64_t tr = 0; tr < ntr; ++tr) {
+      const int64_t r0 = tr * s.q_rows, rows = std::min<int64_t>(s.q_rows, s.rows - r0);
+      for (int64_t tc = 0; tc < ntc; ++tc) {
+        const int64_t c0 = tc * s.q_cols, cols = std::min<int64_t>(s.q_cols, s.cols - c0);
+        const int64_t first = l + r0 * s.cols + c0, last = l + (r0 + rows - 1) * s.cols + c0 + cols - 1;
+        if (last / S != first / S)
           return fail(RS_ERR_INVALID_ARG,
                       "rs_layout_create: a quantisation tile of tensor " + std::to_string(t) +
                           " crosses a shard boundary");
-        L->tiles.push_back(td);
+        const int32_t rank = int32_t(first / S);
+        const int32_t team = team_for(rows * cols);
+        const int32_t vec = (cols % 4 == 0 && s.cols % 4 == 0 && first % 4 == 0) ? 1 : 0;
+        const int64_t idx = tr * ntc + tc;
+        if (scale_idx >= INT32_MAX)
+          return fail(RS_ERR_INVALID_ARG, "rs_layout_create: more than 2^31 quantisation tiles");
+        L->rank_min_tile_rows[rank] = std::min(L->rank_min_tile_rows[rank], int32_t(rows));
+        if (open && cur.rank == rank && cur.team == team && cur.vec == vec &&
+            cur.count < 256 / team && cur.base == l && int64_t(cur.t0) + cur.count == idx) {
+          ++cur.count;
+        } else {
+          if (open) L->work.push_back(cur);
+          cur = QuantWork{};
+          cur.base = l;
+          cur.t0 = int32_t(idx);
+          cur.count = 1;
+          cur.team = team;
+          cur.vec = vec;
+          cur.rows = int32_t(s.rows);
+          cur.cols = int32_t(s.cols);
+          cur.q_rows = s.q_rows;
+          cur.q_cols = s.q_cols;
+          cur.ntc = int32_t(ntc);
+          cur.scale0 = int32_t(scale_idx);
+          cur.rank = rank;
+          open = true;
+        }
+        ++scale_idx;
       }
     }
   }
-  // tiles per rank and workgroup items (consecutive tiles of one rank with
-  // the same team size and vector flag)
-  size_t i = 0;
-  for (int32_t k = 0; k < m; ++k) {
-    L->rank_tile[k] = int64_t(i);
-    L->rank_work[k] = int64_t(L->work.size());
-    while (i < L->tiles.size() && L->tiles[i].rank == k) {
-      const TileDesc& a = L->tiles[i];
-      L->rank_min_tile_rows[k] = std::min(L->rank_min_tile_rows[k], a.rows);
-      const int team = team_for(int64_t(a.rows) * a.cols);
-      const int vec = (a.cols % 4 == 0 && a.ld % 4 == 0 && a.buf_off % 4 == 0) ? 1 : 0;
-      QuantWork w{int32_t(i), 0, team, vec};
-      const int cap = 256 / team;
-      while (i < L->tiles.size() && L->tiles[i].rank == k && w.count < cap) {
-        const TileDesc& b = L->tiles[i];
-        const int vb = (b.cols % 4 == 0 && b.ld % 4 == 0 && b.buf_off % 4 == 0) ? 1 : 0;
-        if (team_for(int64_t(b.rows) * b.cols) != team || vb != vec) break;
-        ++w.count;
-        ++i;
-      }
-      L->work.push_back(w);
+  if (open) L->work.push_back(cur);
+  L->num_tiles = scale_idx;
+  // each rank's first work item
+  {
+    size_t i = 0;
+    for (int32_t k = 0; k <= m; ++k) {
+      while (i < L->work.size() && L->work[i].rank < k) ++i;
+      L->rank_work[k] = int64_t(i);
     }
   }
-  L->rank_tile[m] = int64_t(L->tiles.size());
-  L->rank_work[m] = int64_t(L->work.size());
 
   size_t off = 0;
   L->off_tensors = off;
@@ -179,8 +189,6 @@ rs_status build(rs_layout* L) {
   off = align256(off + sizeof(ChunkDesc) * L->chunks.size());
   L->off_cchunks = off;
   off = align256(off + sizeof(ChunkDesc) * L->cchunks.size());
-  L->off_tiles = off;
-  off = align256(off + sizeof(TileDesc) * L->tiles.size());
   L->off_work = off;
   off = align256(off + sizeof(QuantWork) * L->work.size());
   L->device_bytes = std::max<size_t>(off, 256);
@@ -207,9 +215,13 @@ extern "C" rs_status rs_layout_create(const rs_tensor_spec* specs, int32_t n, in
       return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name + " has a bad shape");
     if ((s.q_rows > 0) != (s.q_cols > 0) || s.q_rows < 0 || s.q_cols < 0 ||
         int64_t(s.q_rows) * s.q_cols > kMaxTileElems ||
-        int64_t(s.q_rows) * s.cols > int64_t(INT32_MAX))
+        int64_t(s.q_rows) * s.cols > int64_t(INT32_MAX) ||
+        (s.q_rows > 0 && (s.rows > INT32_MAX || s.cols > INT32_MAX ||
+                          ((s.rows + s.q_rows - 1) / s.q_rows) * ((s.cols + s.q_cols - 1) / s.q_cols) >
+                              int64_t(INT32_MAX))))
       return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name +
-                                          " has a bad quantisation tile (at most 16384 elements, q_rows * cols < 2^31)");
+                                          " has a bad quantisation tile (at most 16384 elements, q_rows * cols < 2^31, "
+                                          "fewer than 2^31 rows, columns and tiles)");
     const int64_t l = offsets[t], E = s.rows * s.cols, g = granule_of(s);
     if (l < prev_end)
       return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name + " overlaps the previous tensor");
@@ -247,7 +259,7 @@ extern "C" rs_status rs_layout_get_info(const rs_layout* L, rs_layout_info* info
   info->num_chunks = int64_t(L->chunks.size());
   info->num_coarse_chunks = int64_t(L->cchunks.size());
   info->num_frags = int64_t(L->frags.size());
-  info->num_tiles = int64_t(L->tiles.size());
+  info->num_tiles = L->num_tiles;
   info->chunk_elems = L->chunk_elems;
   info->device_bytes = int64_t(L->device_bytes);
   info->workspace_bytes = int64_t(L->workspace_bytes);
@@ -266,7 +278,6 @@ extern "C" rs_status rs_layout_upload(rs_layout* L, void* dev_table, void* strea
   put(L->off_frags, L->frags.data(), sizeof(FragDesc) * L->frags.size());
   put(L->off_chunks, L->chunks.data(), sizeof(ChunkDesc) * L->chunks.size());
   put(L->off_cchunks, L->cchunks.data(), sizeof(ChunkDesc) * L->cchunks.size());
-  put(L->off_tiles, L->tiles.data(), sizeof(TileDesc) * L->tiles.size());
   put(L->off_work, L->work.data(), sizeof(QuantWork) * L->work.size());
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(dev_table, blob.data(), blob.size(), hipMemcpyHostToDevice, s);
