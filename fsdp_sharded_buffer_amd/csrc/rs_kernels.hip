@@ -539,6 +539,31 @@ __device__ __forceinline__ uint32_t e4m3_pack4_normal(float q0, float q1, float 
   return uint32_t(w);
 }
 
+// Four fast-path E4M3 codes.  Values in the instruction's checked domain
+// take its code; values below it lie on the uniform 2^-9 grid of codes 0-16
+// (subnormals and the first binade alike), so their code is rint(|q'|*512)
+// with the sign bit - safe under the INT8 midpoint rule on |q'|*512 (x512
+// is exact).  safe turns false when some value needs the exact quotient.
+__device__ __forceinline__ bool int8_safe(float q, float r);
+
+__device__ __forceinline__ uint32_t e4m3_fast4(const float* q, bool& safe) {
+  uint32_t w = e4m3_pack4_normal(q[0], q[1], q[2], q[3]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t u = __float_as_uint(q[j]), a = u & 0x7fffffffu;
+    if (a < 0x3c800010u) {
+      const float p = __uint_as_float(a) * 512.0f;
+      const float r = __builtin_rintf(p);
+      safe = safe && int8_safe(p, r);
+      const uint32_t code = uint32_t(r) | ((u >> 24) & 0x80u);
+      w = (w & ~(0xffu << (8 * j))) | (code << (8 * j));
+    } else {
+      safe = safe && e4m3_safe(u);
+    }
+  }
+  return w;
+}
+
 // INT8: q' is safe when its distance to the nearest integer is below
 // 0.5 - |q'| * 2^-20, i.e. more than |q'| * 2^-20 (>= 8 ulp) from a
 // half-integer; r = rint(q') is then also the rounded true quotient.
@@ -716,9 +741,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
             word = encode<FMT>(q[0]) | (encode<FMT>(q[1]) << 8) | (encode<FMT>(q[2]) << 16) |
                    (encode<FMT>(q[3]) << 24);
         } else if constexpr (FMT == RS_Q_FP8_E4M3) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) safe = safe && e4m3_safe(u32(q[j]));
-          word = e4m3_pack4_normal(q[0], q[1], q[2], q[3]);
+          word = e4m3_fast4(q, safe);
         } else {
           float r[4];
 #pragma unroll
@@ -1100,9 +1123,7 @@ __device__ __forceinline__ uint32_t fast_encode4(const float* a, float rcp, bool
 #pragma unroll
   for (int j = 0; j < 4; ++j) q[j] = a[j] * rcp;
   if constexpr (FMT == RS_Q_FP8_E4M3) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) safe = safe && e4m3_safe(u32(q[j]));
-    return e4m3_pack4_normal(q[0], q[1], q[2], q[3]);
+    return e4m3_fast4(q, safe);
   } else {
     float r[4];
 #pragma unroll
