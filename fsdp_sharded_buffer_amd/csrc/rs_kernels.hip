@@ -70,6 +70,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    it helps the pure streams (copies, the norm read,
 //                    quantisation input) and hurts read-modify-write
 //                    (scale/add, zero, the fp32 optimizers)
+//   RS_QUANT_F,      256-lane sub-blocks per quantisation work item, for
+//   RS_QUANT_F_SMALL launches of at least / fewer than RS_QUANT_SMALL_ITEMS
+//                    work items
 //   RS_FILL_BYTES    bytes per workgroup of the unmasked zero: one 16-byte
 //                    store per lane, as many short workgroups write fastest
 //   RS_ADAMW_SPLIT,  workgroups per chunk of the AdamW / SGD steps
@@ -95,6 +98,15 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_QUANT_NT
 #define RS_QUANT_NT 1
+#endif
+#ifndef RS_QUANT_F
+#define RS_QUANT_F 2
+#endif
+#ifndef RS_QUANT_F_SMALL
+#define RS_QUANT_F_SMALL 4
+#endif
+#ifndef RS_QUANT_SMALL_ITEMS
+#define RS_QUANT_SMALL_ITEMS 1024
 #endif
 #ifndef RS_FILL_BYTES
 #define RS_FILL_BYTES 4096
@@ -635,38 +647,46 @@ __device__ __forceinline__ Tile tile_of(const QuantWork& w, int j) {
 }
 
 // Each workgroup takes `count` consecutive tiles; tile j of the item is
-// handled by lanes [j*team, (j+1)*team).  On the 16-byte path a lane keeps
-// its (at most 64) elements in registers between the absmax and the encode
-// pass, so x is read once; the other path reads x twice.
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __restrict__ work,
-                                                         int64_t w0,
-                                                         const float* __restrict__ x,
-                                                         uint8_t* __restrict__ codes,
-                                                         float* __restrict__ scales,
-                                                         uint32_t* __restrict__ found_inf,
-                                                         int vec_ok) {
-  __shared__ uint32_t lds[kThreads / kWave];
+// handled by lanes [j*team, (j+1)*team) of each of F sub-blocks of kThreads
+// lanes, sub-block f taking slots [f*16/F, (f+1)*16/F) of the lane's 16
+// four-element slots.  On the 16-byte path a lane keeps its (at most 64/F)
+// elements in registers between the absmax and the encode pass, so x is
+// read once; the other path reads x twice.  F > 1 finishes each tile
+// sooner, for launches with few tiles.
+template <int FMT, int F>
+__global__ __launch_bounds__(kThreads* F) void quant_kernel(const QuantWork* __restrict__ work,
+                                                            int64_t w0,
+                                                            const float* __restrict__ x,
+                                                            uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scales,
+                                                            uint32_t* __restrict__ found_inf,
+                                                            int vec_ok) {
+  constexpr int NS = 16 / F;
+  __shared__ uint32_t lds[kThreads * F / kWave];
+  __shared__ uint32_t ldt[F][kThreads];
   const QuantWork w = work[w0 + blockIdx.x];
   const bool vec = w.vec && vec_ok;
   const int team = w.team;
-  const int slot = threadIdx.x / team;
-  const int lane = threadIdx.x % team;
+  const int sub = threadIdx.x / kThreads;
+  const int tt = threadIdx.x % kThreads;
+  const int slot = tt / team;
+  const int lane = tt % team;
   const bool active = slot < w.count;
   const Tile td = tile_of(w, active ? slot : 0);
   const float* base = x + td.buf_off;
   uint8_t* cbase = codes + td.buf_off;
-  float v[64];
+  const int s0 = sub * NS;
+  float v[4 * NS];
   uint32_t amax = 0;
   const int c4 = td.cols >> 2;
   const int nf = active ? td.rows * c4 : 0;
   const int ne = active ? td.rows * td.cols : 0;
   if (vec) {
-    SlotWalk sw(lane, team, c4, int(td.ld));
+    SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NS; ++i) {
       u32x4 q = {0u, 0u, 0u, 0u};
-      if (lane + i * team < nf) q = ld16<RS_QUANT_NT>(base + sw.off);
+      if (lane + (s0 + i) * team < nf) q = ld16<RS_QUANT_NT>(base + sw.off);
       sw.next();
       v[4 * i + 0] = f32(q.x);
       v[4 * i + 1] = f32(q.y);
@@ -676,7 +696,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
                            max(q.z & 0x7fffffffu, q.w & 0x7fffffffu)));
     }
   } else {
-    for (int e = lane; e < ne; e += team) {
+    for (int e = lane + sub * team; e < ne; e += team * F) {
       const int r = e / td.cols;
       amax = max(amax, __float_as_uint(base[int64_t(r) * td.ld + (e - r * td.cols)]) & 0x7fffffffu);
     }
@@ -685,13 +705,20 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
   // above +Inf, so a NaN anywhere yields a NaN amax
   const int red = team < kWave ? team : kWave;
   for (int o = red / 2; o >= 1; o >>= 1) amax = max(amax, uint32_t(__shfl_xor(int(amax), o)));
-  if (team > kWave) {  // uniform
+  if (team > kWave) {  // uniform: the waves of a tile within a sub-block
     if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = amax;
     __syncthreads();
-    const int first = (threadIdx.x / team) * (team / kWave);
+    const int first = sub * (kThreads / kWave) + (tt / team) * (team / kWave);
     uint32_t a = lds[first];
     for (int i = 1; i < team / kWave; ++i) a = max(a, lds[first + i]);
     amax = a;
+  }
+  if constexpr (F > 1) {  // the sub-blocks of a tile
+    ldt[sub][tt] = amax;
+    __syncthreads();
+    amax = ldt[0][tt];
+#pragma unroll
+    for (int j = 1; j < F; ++j) amax = max(amax, ldt[j][tt]);
   }
   if (!active) return;
   constexpr float Q = FMT == RS_Q_FP8_E4M3 ? 448.0f : 127.0f;
@@ -699,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
   float scale = famax / Q;
   const bool nan_tile = amax > 0x7f800000u;
   if (nan_tile) scale = __uint_as_float(0x7fc00000u);
-  if (lane == 0) {
+  if (lane == 0 && sub == 0) {
     scales[td.scale_idx] = scale;
     // an Inf or NaN |x| pattern is >= the +Inf pattern
     if (found_inf && amax >= 0x7f800000u) found_inf[w.rank] = 1u;
@@ -713,19 +740,19 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
   // exactly x / Inf for every x of the tile (+-0, or NaN for +-Inf)
   const bool inf_scale = sb == 0x7f800000u;
   if (!vec) {
-    for (int e = lane; e < ne; e += team) {
+    for (int e = lane + sub * team; e < ne; e += team * F) {
       const int r = e / td.cols;
       const int64_t o = int64_t(r) * td.ld + (e - r * td.cols);
       cbase[o] = uint8_t(encode_exact<FMT>(base[o], scale, zero_tile, nan_tile));
     }
     return;
   }
-  uint32_t slow = 0;  // bit i: slot i needs the exact path
+  uint32_t slow = 0;  // bit i: slot s0 + i needs the exact path
   {
-    SlotWalk sw(lane, team, c4, int(td.ld));
+    SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (lane + i * team < nf) {
+    for (int i = 0; i < NS; ++i) {
+      if (lane + (s0 + i) * team < nf) {
         float q[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) q[j] = v[4 * i + j] * rcp;
@@ -761,9 +788,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const QuantWork* __rest
     }
   }
   if (slow) {  // rare: re-read the slot (cache resident) and divide
-    SlotWalk sw(lane, team, c4, int(td.ld));
+    SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
 #pragma unroll 1
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NS; ++i) {
       if (slow & (1u << i)) {
         const u32x4 q = ld16<false>(base + sw.off);
         const uint32_t word = encode_exact<FMT>(f32(q.x), scale, zero_tile, nan_tile) |
@@ -1511,13 +1538,24 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
   const int64_t w0 = L->rank_work[k0], nw = L->rank_work[k1] - w0;
   if (nw == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 g(static_cast<unsigned>(nw)), b(kThreads);
+  const QuantWork* wk = table<QuantWork>(L, L->off_work);
+  // launches with few work items spread each over more lanes
+  const bool small = nw < RS_QUANT_SMALL_ITEMS;
+  const dim3 g(static_cast<unsigned>(nw)), b(kThreads * (small ? RS_QUANT_F_SMALL : RS_QUANT_F));
+#define RS_QUANT_LAUNCH(FM)                                                                      \
+  do {                                                                                           \
+    if (small)                                                                                   \
+      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F_SMALL>), g, b, 0, s, wk, w0, x, codes,     \
+                         scales, found_inf, vec_ok);                                             \
+    else                                                                                         \
+      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F>), g, b, 0, s, wk, w0, x, codes, scales,   \
+                         found_inf, vec_ok);                                                     \
+  } while (0)
   if (fmt == RS_Q_FP8_E4M3)
-    hipLaunchKernelGGL((quant_kernel<RS_Q_FP8_E4M3>), g, b, 0, s,
-                       table<QuantWork>(L, L->off_work), w0, x, codes, scales, found_inf, vec_ok);
+    RS_QUANT_LAUNCH(RS_Q_FP8_E4M3);
   else
-    hipLaunchKernelGGL((quant_kernel<RS_Q_INT8>), g, b, 0, s, table<QuantWork>(L, L->off_work),
-                       w0, x, codes, scales, found_inf, vec_ok);
+    RS_QUANT_LAUNCH(RS_Q_INT8);
+#undef RS_QUANT_LAUNCH
   return after_launch(fn);
 }
 
