@@ -73,6 +73,8 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //   RS_QUANT_F,      256-lane sub-blocks per quantisation work item, for
 //   RS_QUANT_F_SMALL launches of at least / fewer than RS_QUANT_SMALL_ITEMS
 //                    work items
+//   RS_SQNORM_FINE_BELOW  the norm reads fine chunks when the range has
+//                    fewer coarse chunks than this (too few workgroups)
 //   RS_FILL_BYTES    bytes per workgroup of the unmasked zero: one 16-byte
 //                    store per lane, as many short workgroups write fastest
 //   RS_ADAMW_SPLIT,  workgroups per chunk of the AdamW / SGD steps
@@ -107,6 +109,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_QUANT_SMALL_ITEMS
 #define RS_QUANT_SMALL_ITEMS 1024
+#endif
+#ifndef RS_SQNORM_FINE_BELOW
+#define RS_SQNORM_FINE_BELOW 256
 #endif
 #ifndef RS_FILL_BYTES
 #define RS_FILL_BYTES 4096
@@ -489,11 +494,12 @@ __global__ __launch_bounds__(kThreads) void sqnorm_partial_kernel(
 }
 
 // Per tensor: fragment sums in rank order, each the fixed-order sum of its
-// coarse-chunk partials; writes partial[k*n + t] for every k of the range.
+// chunk partials (fine or coarse chunks, as the partial kernel used);
+// writes partial[k*n + t] for every k of the range.
 __global__ __launch_bounds__(kThreads) void sqnorm_combine_kernel(
     const TensorDesc* __restrict__ tensors, const FragDesc* __restrict__ frags,
     const double* __restrict__ part, int32_t n, int32_t k0, int32_t k1, double* __restrict__ sq_out,
-    double* __restrict__ partial) {
+    double* __restrict__ partial, int fine) {
   __shared__ double lds[kThreads / kWave];
   const int t = blockIdx.x;
   const TensorDesc td = tensors[t];
@@ -505,14 +511,16 @@ __global__ __launch_bounds__(kThreads) void sqnorm_combine_kernel(
       const FragDesc fd = frags[td.frag_begin + (k - td.rank_lo)];
       // lanes stride over the partials; four loads in flight per lane
       double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-      int i = fd.cchunk_begin + threadIdx.x;
-      for (; i + 3 * kThreads < fd.cchunk_end; i += 4 * kThreads) {
+      const int cb = fine ? fd.chunk_begin : fd.cchunk_begin;
+      const int ce = fine ? fd.chunk_end : fd.cchunk_end;
+      int i = cb + threadIdx.x;
+      for (; i + 3 * kThreads < ce; i += 4 * kThreads) {
         a0 += part[i];
         a1 += part[i + kThreads];
         a2 += part[i + 2 * kThreads];
         a3 += part[i + 3 * kThreads];
       }
-      for (; i < fd.cchunk_end; i += kThreads) a0 += part[i];
+      for (; i < ce; i += kThreads) a0 += part[i];
       s = block_sum((a0 + a1) + (a2 + a3), lds);
       if (threadIdx.x == 0) total += s;
     }
@@ -1510,14 +1518,18 @@ extern "C" rs_status rs_ragged_sqnorm(const rs_layout* L, const float* x, double
   if (partial) RS_TRY(check_ptr(partial, 8, fn, "partial"));
   if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t c0 = L->rank_cchunk[k0], nc = L->rank_cchunk[k1] - c0;
+  // coarse chunks, unless the range has too few of them to fill the chip
+  const int fine = (L->rank_cchunk[k1] - L->rank_cchunk[k0]) < RS_SQNORM_FINE_BELOW ? 1 : 0;
+  const std::vector<int64_t>& rb = fine ? L->rank_chunk : L->rank_cchunk;
+  const int64_t c0 = rb[k0], nc = rb[k1] - c0;
   double* part = static_cast<double*>(ws);
   if (nc > 0)
     hipLaunchKernelGGL(sqnorm_partial_kernel, chunk_grid(nc), dim3(kThreads), 0, s,
-                       table<ChunkDesc>(L, L->off_cchunks), c0, nc, x, part, found_inf);
+                       table<ChunkDesc>(L, fine ? L->off_chunks : L->off_cchunks), c0, nc, x, part,
+                       found_inf);
   hipLaunchKernelGGL(sqnorm_combine_kernel, dim3(unsigned(L->n)), dim3(kThreads), 0, s,
                      table<TensorDesc>(L, L->off_tensors), table<FragDesc>(L, L->off_frags), part,
-                     L->n, k0, k1, sq_out, partial);
+                     L->n, k0, k1, sq_out, partial, fine);
   return after_launch(fn);
 }
 

@@ -192,8 +192,10 @@ rs_status build(rs_layout* L) {
   L->off_work = off;
   off = align256(off + sizeof(QuantWork) * L->work.size());
   L->device_bytes = std::max<size_t>(off, 256);
-  // sqnorm scratch: one fp64 partial per coarse chunk
-  L->workspace_bytes = align256(sizeof(double) * std::max<size_t>(L->cchunks.size(), 1));
+  // sqnorm scratch: one fp64 partial per chunk of the finer table (small
+  // rank ranges read fine chunks)
+  L->workspace_bytes =
+      align256(sizeof(double) * std::max<size_t>({L->chunks.size(), L->cchunks.size(), size_t(1)}));
   return RS_OK;
 }
 
