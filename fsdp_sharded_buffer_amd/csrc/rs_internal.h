@@ -97,6 +97,8 @@ struct rs_layout {
   // per-rank begin indices, size m + 1
   std::vector<int64_t> rank_chunk, rank_cchunk, rank_frag, rank_work;
   std::vector<int32_t> rank_min_tile_rows;  // per rank; INT32_MAX when it has no tile
+  std::vector<int64_t> rank_small_tiles;    // per rank: tiles taken by fewer than 256 lanes
+  std::vector<int64_t> rank_big_tiles;      // per rank: tiles taken by 256 lanes
 
   // byte offsets of each table inside the device blob
   size_t off_tensors = 0, off_frags = 0, off_chunks = 0, off_cchunks = 0,

@@ -72,7 +72,7 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    (scale/add, zero, the fp32 optimizers)
 //   RS_QUANT_F,      256-lane sub-blocks per quantisation work item, for
 //   RS_QUANT_F_SMALL launches of at least / fewer than RS_QUANT_SMALL_ITEMS
-//                    work items
+//                    work items (one sub-block where most tiles are small)
 //   RS_SQNORM_FINE_BELOW  the norm reads fine chunks when the range has
 //                    fewer coarse chunks than this (too few workgroups)
 //   RS_FILL_BYTES    bytes per workgroup of the unmasked zero: one 16-byte
@@ -1551,12 +1551,24 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
   if (nw == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
-  // launches with few work items spread each over more lanes
-  const bool small = nw < RS_QUANT_SMALL_ITEMS;
-  const dim3 g(static_cast<unsigned>(nw)), b(kThreads * (small ? RS_QUANT_F_SMALL : RS_QUANT_F));
+  // Big tiles (256 lanes each) are spread over sub-blocks, more of them in
+  // launches with few work items; ranges where most tiles are small (a few
+  // lanes each, whose absmax stays within a wave) keep one sub-block.
+  int64_t small_tiles = 0, big_tiles = 0;
+  for (int32_t k = k0; k < k1; ++k) {
+    small_tiles += L->rank_small_tiles[k];
+    big_tiles += L->rank_big_tiles[k];
+  }
+  const int F = small_tiles > big_tiles ? 1
+                : nw < RS_QUANT_SMALL_ITEMS ? RS_QUANT_F_SMALL
+                                            : RS_QUANT_F;
+  const dim3 g(static_cast<unsigned>(nw)), b(kThreads * F);
 #define RS_QUANT_LAUNCH(FM)                                                                      \
   do {                                                                                           \
-    if (small)                                                                                   \
+    if (F == 1)                                                                                  \
+      hipLaunchKernelGGL((quant_kernel<FM, 1>), g, b, 0, s, wk, w0, x, codes, scales,            \
+                         found_inf, vec_ok);                                                     \
+    else if (F == RS_QUANT_F_SMALL)                                                              \
       hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F_SMALL>), g, b, 0, s, wk, w0, x, codes,     \
                          scales, found_inf, vec_ok);                                             \
     else                                                                                         \

@@ -97,6 +97,8 @@ rs_status build(rs_layout* L) {
   L->rank_frag.assign(m + 1, 0);
   L->rank_work.assign(m + 1, 0);
   L->rank_min_tile_rows.assign(m, INT32_MAX);
+  L->rank_small_tiles.assign(m, 0);
+  L->rank_big_tiles.assign(m, 0);
 
   build_chunks(L, L->chunk_elems, L->chunks, L->rank_chunk, true);
   build_chunks(L, L->chunk_elems * kCoarseFactor, L->cchunks, L->rank_cchunk, false);
@@ -145,6 +147,7 @@ rs_status build(rs_layout* L) {
         if (scale_idx >= INT32_MAX)
           return fail(RS_ERR_INVALID_ARG, "rs_layout_create: more than 2^31 quantisation tiles");
         L->rank_min_tile_rows[rank] = std::min(L->rank_min_tile_rows[rank], int32_t(rows));
+        ++(team < 256 ? L->rank_small_tiles : L->rank_big_tiles)[rank];
         if (open && cur.rank == rank && cur.team == team && cur.vec == vec &&
             cur.count < 256 / team && cur.base == l && int64_t(cur.t0) + cur.count == idx) {
           ++cur.count;
