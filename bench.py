@@ -101,13 +101,17 @@ def read_counters(workload: str):
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, offs, S, inp, k1, min_seconds=10.0):
+def cpu_baseline(w, offs, S, inp, k1, align, min_seconds=10.0):
     """The oracle, as it stands, on ranks [0, k1) of the same workload:
-    whole passes of all six operations, repeated until min_seconds."""
+    whole passes of all six operations, repeated until min_seconds; and the
+    oracle's planner on the whole group."""
     from oracle import ops as O
     from oracle import plan as P
 
     items = P.items_from_specs(w.tensors)
+    t0 = time.perf_counter()
+    P.plan(items, w.m, align)
+    plan_s = time.perf_counter() - t0
     total = w.m * S
     m = w.m
     y0 = np.zeros(total, np.float32)
@@ -141,7 +145,8 @@ def cpu_baseline(w, offs, S, inp, k1, min_seconds=10.0):
     b = (4 * E_in + 2 * k1 * S) + 4 * E_in + 12 * E_in + 4 * E_in + 5 * eq_in + 4 * k1 * S
     return {"value": round(b * passes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"ranks [0,{k1}) of {m} ({k1 * S} buffer positions): {passes} passes of all "
-                      f"six operations in {dt:.1f} s, numpy on one host core"}
+                      f"six operations in {dt:.1f} s, numpy on one host core",
+            "planner_ms": round(plan_s * 1e3, 2)}
 
 
 STUDY_MS = (8, 16, 32, 64, 128, 256, 512, 1024)
@@ -431,7 +436,7 @@ def main():
     if not args.no_cpu_baseline:
         k1 = args.cpu_ranks or m
         log(f"cpu baseline: oracle on ranks [0,{k1})")
-        cpu = cpu_baseline(w, offs, S, inp, k1)
+        cpu = cpu_baseline(w, offs, S, inp, k1, args.align)
         log(f"cpu baseline {cpu['value']} GB/s ({cpu['sample']})")
 
     out = {

@@ -210,6 +210,7 @@ SMALL = {
     "pad_ranks": lambda: (_pad_ranks(), 1, 64),
     "tiny": lambda: (_tiny(), 1, 64),
     "no_quant": lambda: (_no_quant(), 16, 128),
+    "toy_chunk_max": lambda: (W.toy_unit(), 16, 1 << 22),   # largest chunk: one per fragment
 }
 
 _cases = {}
