@@ -101,11 +101,6 @@ typedef struct {
 rs_status rs_plan(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t align,
                   int64_t S_cap, int64_t* offsets, rs_plan_info* info);
 
-/* Opaque host-side layout: tensor, fragment, chunk, quantisation-tile and
- * work tables built from a plan.  The device copy of the tables lives in a
- * caller-owned device buffer (the persistent descriptor table every grouped
- * kernel reads; veScale-FSDP, "DBuffer": one kernel per group instead of
- * one per tensor). */
 /* Tensor orders for rs_plan_ordered (veScale-FSDP, "Planning Algorithm":
  * the pages compare the given order, an order by block size and one by
  * tensor shape, and keep the given one).  Orders are stable: tensors with
@@ -141,6 +136,11 @@ rs_status rs_plan_ordered(const rs_tensor_spec* specs, int32_t n, int32_t m, int
                           int64_t S_cap, rs_order kind, int32_t* perm, int64_t* offsets,
                           rs_plan_info* info);
 
+/* Opaque host-side layout: tensor, fragment and chunk tables and the tile
+ * work items (runs of consecutive quantisation tiles) built from a plan.
+ * The device copy of the tables lives in a caller-owned device buffer (the
+ * persistent descriptor table every grouped kernel reads; veScale-FSDP,
+ * "DBuffer": one kernel per group instead of one per tensor). */
 typedef struct rs_layout rs_layout;
 
 /* Counts describing a layout (for sizing caller buffers). */
