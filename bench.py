@@ -215,8 +215,10 @@ def main():
     ap.add_argument("--only", default="", help="comma list of ops to time per op (default all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) to scale HBM counters")
-    ap.add_argument("--per-rank", action="store_true",
-                    help="also time each operation on one rank's shard, cycling over the ranks")
+    ap.add_argument("--per-rank", action="store_true", default=True,
+                    help="also time each operation on one rank's shard, cycling over the ranks "
+                         "(default)")
+    ap.add_argument("--no-per-rank", dest="per_rank", action="store_false")
     ap.add_argument("--no-torch-ref", action="store_true",
                     help="skip timing torch's own copy/axpy/fill/fused optimizers for context")
     ap.add_argument("--padding-study", action="store_true",
