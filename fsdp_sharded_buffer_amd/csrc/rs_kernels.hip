@@ -77,6 +77,8 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    fewer coarse chunks than this (too few workgroups)
 //   RS_FILL_BYTES    bytes per workgroup of the unmasked zero: one 16-byte
 //                    store per lane, as many short workgroups write fastest
+//   RS_OPT_G_NT      nontemporal loads of the gradient (read once) in the
+//                    AdamW / SGD steps, beside their read-modify-write streams
 //   RS_ADAMW_SPLIT,  workgroups per chunk of the AdamW / SGD steps
 //   RS_SGD_SPLIT
 //   RS_DEQ_SPLIT     row bands (workgroups) per dequantised tile
@@ -115,6 +117,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_FILL_BYTES
 #define RS_FILL_BYTES 4096
+#endif
+#ifndef RS_OPT_G_NT
+#define RS_OPT_G_NT 1
 #endif
 #ifndef RS_ADAMW_SPLIT
 #define RS_ADAMW_SPLIT 4
@@ -1021,7 +1026,7 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(
         const int q = q0 + u * kThreads;
         if (q < nv) {
           P[u] = ld16<false>(pp + 4 * q);
-          G[u] = ld16<false>(gp + 4 * q);
+          G[u] = ld16<RS_OPT_G_NT>(gp + 4 * q);
           M[u] = ld16<false>(mp + 4 * q);
           V[u] = ld16<false>(vp + 4 * q);
         }
@@ -1089,7 +1094,7 @@ __global__ __launch_bounds__(kThreads) void sgd_kernel(
         const int q = q0 + u * kThreads;
         if (q < nv) {
           P[u] = ld16<false>(pp + 4 * q);
-          G[u] = ld16<false>(gp + 4 * q);
+          G[u] = ld16<RS_OPT_G_NT>(gp + 4 * q);
           B[u] = ld16<false>(bp + 4 * q);
         }
       }
