@@ -230,7 +230,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the m virtual ranks are slices of one device buffer "
-              "and this build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+              "and this library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -78,7 +78,7 @@ int64_t earliest(int64_t lo, const PItem& it, int64_t S, int32_t m, int64_t A) {
 }
 
 // Candidates tried in order before the scan goes parallel, and candidates
-// per thread and round after that.
+// per thread in each pass after that.
 constexpr int64_t kSequentialCandidates = 4096;
 constexpr int64_t kBlockCandidates = 2048;
 
@@ -146,7 +146,7 @@ rs_status plan_items(const std::vector<PItem>& items, int32_t m, int64_t align, 
     }
     return -1;
   };
-  // The first candidates in order; a long scan then goes on in rounds of
+  // The first candidates in order; a long scan then goes on in passes of
   // consecutive blocks, one per host thread.  The earliest block with a
   // feasible S holds the smallest one, so the result is the sequential
   // scan's.
