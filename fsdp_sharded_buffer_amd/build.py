@@ -71,7 +71,24 @@ def build_probe(verbose: bool = True) -> str:
     return PROBE_LIB
 
 
+DEMO_SRC = os.path.join(ROOT, "tests", "native", "capi_demo.cpp")
+DEMO_EXE = os.path.join(ROOT, "tests", "native", "capi_demo")
+
+
+def build_capi_demo(verbose: bool = True) -> str:
+    """Test-only C++ program that drives librs.so through include/rs.h with
+    no Python in the process (tests/native)."""
+    tmp = DEMO_EXE + ".tmp"
+    subprocess.run([hipcc(), DEMO_SRC, "-O2", "-std=c++17", "-I", INCLUDE, "-L", PKG, "-lrs",
+                    "-Wl,-rpath,$ORIGIN/../../fsdp_sharded_buffer_amd", "-o", tmp], check=True)
+    os.replace(tmp, DEMO_EXE)
+    if verbose:
+        print(f"built {DEMO_EXE}")
+    return DEMO_EXE
+
+
 if __name__ == "__main__":
     build()
     build_probe()
+    build_capi_demo()
     sys.exit(0)
