@@ -1,8 +1,12 @@
-// Test-only probe of device arithmetic the kernels rely on; not part of
-// librs.so: gfx950's packed fp32 -> OCP E4M3 conversion (the block
-// quantisation fast path), applied to consecutive fp32 bit patterns four at
-// a time exactly as the kernel packs a word, so a test can compare every
-// input of the fast path's domain with the CPU oracle.
+// Test-only probes of device arithmetic the kernels rely on; not part of
+// librs.so.
+//  * gfx950's packed fp32 -> OCP E4M3 conversion (the block quantisation
+//    fast path), applied to consecutive fp32 bit patterns four at a time
+//    exactly as the kernel packs a word, so a test can compare every input
+//    of the fast path's domain with the CPU oracle;
+//  * fp32 division and square root as the kernels compile them (the exact
+//    quantisation path and the AdamW steps rely on both being correctly
+//    rounded).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -23,7 +27,24 @@ __global__ void probe_kernel(uint32_t first, int64_t n, uint32_t sign, uint8_t* 
     if (i + j < n) out[i + j] = uint8_t(uint32_t(w) >> (8 * j));
 }
 
+__global__ void divsqrt_kernel(const float* x, const float* y, int64_t n, float* q, float* r) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  q[i] = x[i] / y[i];
+  r[i] = sqrtf(x[i]);
+}
+
 }  // namespace
+
+// q[i] = x[i] / y[i] and r[i] = sqrtf(x[i]) for i < n (device arrays).
+extern "C" int probe_div_sqrt(const float* x, const float* y, int64_t n, float* q, float* r,
+                              void* stream) {
+  if (n <= 0 || !x || !y || !q || !r) return -1;
+  const unsigned grid = unsigned((n + 255) / 256);
+  hipLaunchKernelGGL(divsqrt_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), x,
+                     y, n, q, r);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
 
 // out[k] = E4M3 code of the fp32 with bits (first + k) | sign, k < n.
 extern "C" int probe_e4m3_hw(uint32_t first, int64_t n, uint32_t sign, uint8_t* out, void* stream) {

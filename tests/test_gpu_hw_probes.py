@@ -58,3 +58,48 @@ def test_e4m3_instruction_equals_oracle_on_fast_path_domain():
     assert not bad, bad[0]
     assert sum(results) == 2 * (HI - LO)
 
+
+
+def _random_f32(rng, n):
+    """Random finite fp32 values over the whole range: uniform bit patterns
+    (subnormals included), NaN/Inf patterns replaced."""
+    u = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+    u = np.where((u & 0x7F800000) == 0x7F800000, u & 0x807FFFFF, u)
+    return u.view(np.float32)
+
+
+@pytest.mark.timeout(900)
+def test_division_and_sqrt_are_correctly_rounded():
+    """The device's fp32 x / y and sqrtf, compiled as the kernels compile
+    them, bit-equal to NumPy's IEEE float32 division and square root on
+    10^8 seeded pairs over the whole range, subnormals included (NaN results
+    compare by class)."""
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib = ctypes.CDLL(LIB)
+    lib.probe_div_sqrt.restype = ctypes.c_int
+    lib.probe_div_sqrt.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    rng = np.random.default_rng(71)
+    n = 1 << 24
+    stream = torch.cuda.current_stream().cuda_stream
+    for it in range(6):
+        log(f"div/sqrt batch {it}")
+        x = _random_f32(rng, n)
+        y = _random_f32(rng, n)
+        if it == 0:                         # near-equal magnitudes and tiny quotients too
+            y[: n // 2] = (x[: n // 2] * np.float32(1.0000001)).astype(np.float32)
+        dx, dy = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
+        q = torch.empty_like(dx)
+        r = torch.empty_like(dx)
+        assert lib.probe_div_sqrt(dx.data_ptr(), dy.data_ptr(), n, q.data_ptr(), r.data_ptr(), stream) == 0
+        torch.cuda.synchronize()
+        with np.errstate(all="ignore"):
+            eq = (x / y).astype(np.float32)
+            er = np.sqrt(x).astype(np.float32)
+        for got, exp, what in ((q.cpu().numpy(), eq, "division"), (r.cpu().numpy(), er, "sqrt")):
+            gn, en = np.isnan(got), np.isnan(exp)
+            assert np.array_equal(gn, en), what + ": NaN positions differ"
+            bad = (got.view(np.uint32) != exp.view(np.uint32)) & ~gn
+            assert not bad.any(), f"{what}: {int(bad.sum())} results differ, e.g. x={x[bad][0]!r}"

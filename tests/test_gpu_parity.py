@@ -8,6 +8,8 @@ too) with NaN where the oracle has NaN; squared norms within 1e-5 relative
 of the fp64 oracle with the same non-finite class.  Every device output is
 surrounded by canary elements that must survive.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -486,3 +488,47 @@ def test_no_tiles_accepts_null_scales():
                          0.5, 0.5, 1.0, None, 0, c.m)
     _sync()
     assert bool((codes == U8_CANARY).all()) and bool((y == 3.0).all())
+
+
+@pytest.mark.timeout(900)
+def test_pack_bf16_cast_every_fp32_pattern():
+    """rs_pack's fp32 -> bf16 cast on all 2^32 fp32 bit patterns (one vector
+    tensor, one rank, 2^24 patterns per launch) against the oracle's RNE
+    cast, NaN payloads included.  The oracle runs on host threads, a wave of
+    chunks at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+    R = case("toy").R
+    N = 1 << 24
+    spec = [W.TensorSpec("v", 1, N, 0)]
+    offs, info = R.rs_plan(spec, 1, 16)
+    lay = R.Layout(spec, 1, info["S"], offs)
+    src = torch.empty(N, dtype=torch.int32, device="cuda")
+    table = R.ptr_table([src])
+    buf = torch.empty(info["S"], dtype=torch.bfloat16, device="cuda")
+    base = torch.arange(N, dtype=torch.int64, device="cuda")
+
+    def expected(first):
+        return OC.bf16_bits_from_f32(np.arange(first, first + N, dtype=np.uint64).astype(np.uint32)
+                                     .view(np.float32))
+
+    wave = 16
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        for w0 in range(0, 1 << 32, wave * N):
+            firsts = list(range(w0, min(w0 + wave * N, 1 << 32), N))
+            futs = [ex.submit(expected, f) for f in firsts]
+            got = []
+            for first in firsts:
+                v = base + first
+                src.copy_(torch.where(v >= (1 << 31), v - (1 << 32), v).to(torch.int32))
+                R.rs_pack(lay.handle, table, R.RS_F32, buf, R.RS_BF16, 0, 1)
+                got.append(to_np(buf)[:N].copy())
+            log(f"bf16 cast: patterns up to {firsts[-1] + N:#011x}")
+            for first, g, f in zip(firsts, got, futs):
+                exp = f.result()
+                if not np.array_equal(g, exp):
+                    i = int(np.flatnonzero(g != exp)[0])
+                    raise AssertionError(f"bf16 cast of {first + i:#010x}: got {g[i]:#06x} "
+                                         f"expected {exp[i]:#06x}")
+    lay.close()
