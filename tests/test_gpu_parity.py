@@ -532,3 +532,70 @@ def test_pack_bf16_cast_every_fp32_pattern():
                     raise AssertionError(f"bf16 cast of {first + i:#010x}: got {g[i]:#06x} "
                                          f"expected {exp[i]:#06x}")
     lay.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "int8"])
+def test_quant_every_fp32_up_to_amax(fmt):
+    """Quantisation of every fp32 value x with |x| <= 1344, both signs, in
+    1 x 16384 tiles whose first element is 1344: the scale is then
+    fl(1344/Q) (3 for E4M3, an inexact reciprocal either way), so the codes
+    come through the reciprocal fast path, its safety windows and the exact
+    fallback over the whole code range.  Against the oracle's cast of the
+    fp32 quotient, with the oracle on host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+    R = case("toy").R
+    T = 16384
+    N = 1024 * T
+    spec = [W.TensorSpec("v", 1, N, 1, 1, T)]
+    offs, info = R.rs_plan(spec, 1, 16)
+    lay = R.Layout(spec, 1, info["S"], offs)
+    qf = R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8
+    Q = np.float32(448.0 if fmt == "fp8_e4m3" else 127.0)
+    amax = np.float32(1344.0)
+    scale = np.float32(amax / Q)
+    top = int(amax.view(np.uint32))            # every magnitude pattern 0 .. top
+    per = N - N // T                           # test values per launch (tile heads hold amax)
+    x = torch.empty(N, dtype=torch.int32, device="cuda")
+    codes = torch.empty(info["S"], dtype=torch.uint8, device="cuda")
+    scales = torch.empty(N // T, dtype=torch.float32, device="cuda")
+    body = torch.ones(N, dtype=torch.bool, device="cuda")
+    body[::T] = False
+    ar = torch.arange(per, dtype=torch.int64, device="cuda")
+
+    def expected(first, sign):
+        u = (np.arange(first, first + per, dtype=np.uint64).clip(max=top) | sign).astype(np.uint32)
+        q = (u.view(np.float32) / scale).astype(np.float32)
+        c = OC.e4m3fn_bits_from_f32(q) if fmt == "fp8_e4m3" else OC.int8_from_f32(q).view(np.uint8)
+        return c
+
+    hq = np.array([amax], np.float32) / scale
+    head = int((OC.e4m3fn_bits_from_f32(hq) if fmt == "fp8_e4m3"
+                else OC.int8_from_f32(hq).view(np.uint8))[0])
+    body_np = to_np(body)
+    jobs = [(first, sign) for sign in (0, 0x80000000) for first in range(0, top + 1, per)]
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        for j0 in range(0, len(jobs), 16):
+            wave = jobs[j0:j0 + 16]
+            futs = [ex.submit(expected, f, sg) for f, sg in wave]
+            got = []
+            for first, sign in wave:
+                v = (ar + first).clamp(max=top) | sign
+                v = torch.where(v >= (1 << 31), v - (1 << 32), v).to(torch.int32)
+                x.fill_(int(amax.view(np.int32)))
+                x[body] = v
+                R.rs_block_quant(lay.handle, x.view(torch.float32), qf, codes, scales, 0, 1)
+                c = to_np(codes)[:N]
+                assert np.all(to_np(scales).view(np.uint32) == scale.view(np.uint32))
+                assert np.all(c[::T] == head)
+                got.append(c[body_np])
+            log(f"quant {fmt}: {j0 + len(wave)} of {len(jobs)} launches")
+            for (first, sign), g, f in zip(wave, got, futs):
+                e = f.result()
+                if not np.array_equal(g, e):
+                    i = int(np.flatnonzero(g != e)[0])
+                    raise AssertionError(f"{fmt} code of x = {(min(first + i, top) | sign):#010x} "
+                                         f"/ {float(scale)}: got {g[i]:#04x} expected {e[i]:#04x}")
+    lay.close()
