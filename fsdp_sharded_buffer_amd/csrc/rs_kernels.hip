@@ -11,8 +11,10 @@
 // both sides of a run are 16-byte aligned, element accesses otherwise.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <string>
 
 #include "rs_internal.h"
@@ -1387,8 +1389,24 @@ rs_status check_ptr(const void* p, size_t align, const char* fn, const char* wha
   return RS_OK;
 }
 
-// Workgroups for nc chunks: one per chunk.
-dim3 chunk_grid(int64_t nc) { return dim3(static_cast<unsigned>(nc)); }
+// Largest grid of one launch, in workgroups of `threads` lanes.  HIP takes
+// fewer than 2^32 lanes per grid dimension; launches stay within 2^31.  The
+// environment variable RS_MAX_GRID, read once, lowers the cap (tests use it
+// to run the batched launch paths on small groups).
+int64_t max_groups(int threads) {
+  static const int64_t env_cap = [] {
+    const char* e = std::getenv("RS_MAX_GRID");
+    return e ? std::max<int64_t>(0, std::atoll(e)) : int64_t(0);
+  }();
+  const int64_t hw = (int64_t(1) << 31) / threads;
+  return env_cap > 0 ? std::min(env_cap, hw) : hw;
+}
+
+// Workgroups for n chunk-kernel items: one per item, up to the launch cap;
+// the chunk kernels stride by the grid beyond it.
+dim3 chunk_grid(int64_t n) {
+  return dim3(static_cast<unsigned>(std::min(n, max_groups(kThreads))));
+}
 
 rs_status after_launch(const char* fn) {
   const hipError_t e = hipGetLastError();
@@ -1495,11 +1513,17 @@ extern "C" rs_status rs_group_zero(const rs_layout* L, void* y, rs_dtype dt,
   char* lo = static_cast<char*>(y) + int64_t(k0) * L->S * es;
   const int64_t nbytes = int64_t(k1 - k0) * L->S * es;
   if (!tensor_mask && reinterpret_cast<uintptr_t>(lo) % 16 == 0 && nbytes % 16 == 0) {
-    // the whole rank range, padding included: one contiguous fill
-    const int64_t g = (nbytes + RS_FILL_BYTES - 1) / RS_FILL_BYTES;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s, lo,
-                       nbytes);
-    return after_launch(fn);
+    // the whole rank range, padding included: one contiguous fill, in
+    // launches of at most the grid cap
+    const int64_t per = max_groups(kThreads) * RS_FILL_BYTES;
+    for (int64_t o = 0; o < nbytes; o += per) {
+      const int64_t nb = std::min(per, nbytes - o);
+      const int64_t g = (nb + RS_FILL_BYTES - 1) / RS_FILL_BYTES;
+      hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s,
+                         lo + o, nb);
+      RS_TRY(after_launch(fn));
+    }
+    return RS_OK;
   }
   const int64_t c0 = L->rank_cchunk[k0], nc = L->rank_cchunk[k1] - c0;
   if (nc == 0) return RS_OK;
@@ -1567,25 +1591,30 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
   const int F = small_tiles > big_tiles ? 1
                 : nw < RS_QUANT_SMALL_ITEMS ? RS_QUANT_F_SMALL
                                             : RS_QUANT_F;
-  const dim3 g(static_cast<unsigned>(nw)), b(kThreads * F);
-#define RS_QUANT_LAUNCH(FM)                                                                      \
-  do {                                                                                           \
-    if (F == 1)                                                                                  \
-      hipLaunchKernelGGL((quant_kernel<FM, 1>), g, b, 0, s, wk, w0, x, codes, scales,            \
-                         found_inf, vec_ok);                                                     \
-    else if (F == RS_QUANT_F_SMALL)                                                              \
-      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F_SMALL>), g, b, 0, s, wk, w0, x, codes,     \
-                         scales, found_inf, vec_ok);                                             \
-    else                                                                                         \
-      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F>), g, b, 0, s, wk, w0, x, codes, scales,   \
-                         found_inf, vec_ok);                                                     \
+  const dim3 b(kThreads * F);
+  const int64_t per = max_groups(kThreads * F);
+  for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one work item per workgroup
+    const dim3 g(static_cast<unsigned>(std::min(per, w0 + nw - w1)));
+#define RS_QUANT_LAUNCH(FM)                                                                    \
+  do {                                                                                         \
+    if (F == 1)                                                                                \
+      hipLaunchKernelGGL((quant_kernel<FM, 1>), g, b, 0, s, wk, w1, x, codes, scales,          \
+                         found_inf, vec_ok);                                                   \
+    else if (F == RS_QUANT_F_SMALL)                                                            \
+      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F_SMALL>), g, b, 0, s, wk, w1, x, codes,   \
+                         scales, found_inf, vec_ok);                                           \
+    else                                                                                       \
+      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F>), g, b, 0, s, wk, w1, x, codes, scales, \
+                         found_inf, vec_ok);                                                   \
   } while (0)
-  if (fmt == RS_Q_FP8_E4M3)
-    RS_QUANT_LAUNCH(RS_Q_FP8_E4M3);
-  else
-    RS_QUANT_LAUNCH(RS_Q_INT8);
+    if (fmt == RS_Q_FP8_E4M3)
+      RS_QUANT_LAUNCH(RS_Q_FP8_E4M3);
+    else
+      RS_QUANT_LAUNCH(RS_Q_INT8);
 #undef RS_QUANT_LAUNCH
-  return after_launch(fn);
+    RS_TRY(after_launch(fn));
+  }
+  return RS_OK;
 }
 
 extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, rs_qfmt fmt,
@@ -1609,27 +1638,33 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
   int32_t min_rows = INT32_MAX;
   for (int32_t k = k0; k < k1; ++k) min_rows = std::min(min_rows, L->rank_min_tile_rows[k]);
   const bool split = RS_DEQ_SPLIT > 1 && min_rows >= RS_DEQ_SPLIT;
-  const dim3 g(static_cast<unsigned>(split ? nw * RS_DEQ_SPLIT : nw)), b(kThreads);
+  const int64_t bands = split ? RS_DEQ_SPLIT : 1;
+  const dim3 b(kThreads);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
-#define RS_DEQ_LAUNCH(FM, YK)                                                                 \
-  do {                                                                                        \
-    if (split)                                                                                \
-      hipLaunchKernelGGL((dequant_kernel<FM, YK, RS_DEQ_SPLIT>), g, b, 0, s, wk, w0, codes,     \
-                         scales, y, vec_ok);                                                  \
-    else                                                                                      \
-      hipLaunchKernelGGL((dequant_kernel<FM, YK, 1>), g, b, 0, s, wk, w0, codes, scales, y,     \
-                         vec_ok);                                                             \
+  const int64_t per = std::max<int64_t>(1, max_groups(kThreads) / bands);  // items per launch
+  for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one workgroup per band of a work item
+    const dim3 g(static_cast<unsigned>(std::min(per, w0 + nw - w1) * bands));
+#define RS_DEQ_LAUNCH(FM, YK)                                                                  \
+  do {                                                                                         \
+    if (split)                                                                                 \
+      hipLaunchKernelGGL((dequant_kernel<FM, YK, RS_DEQ_SPLIT>), g, b, 0, s, wk, w1, codes,      \
+                         scales, y, vec_ok);                                                   \
+    else                                                                                       \
+      hipLaunchKernelGGL((dequant_kernel<FM, YK, 1>), g, b, 0, s, wk, w1, codes, scales, y,      \
+                         vec_ok);                                                              \
   } while (0)
-  if (fmt == RS_Q_FP8_E4M3 && y_dt == RS_F32)
-    RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 0);
-  else if (fmt == RS_Q_FP8_E4M3)
-    RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 1);
-  else if (y_dt == RS_F32)
-    RS_DEQ_LAUNCH(RS_Q_INT8, 0);
-  else
-    RS_DEQ_LAUNCH(RS_Q_INT8, 1);
+    if (fmt == RS_Q_FP8_E4M3 && y_dt == RS_F32)
+      RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 0);
+    else if (fmt == RS_Q_FP8_E4M3)
+      RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 1);
+    else if (y_dt == RS_F32)
+      RS_DEQ_LAUNCH(RS_Q_INT8, 0);
+    else
+      RS_DEQ_LAUNCH(RS_Q_INT8, 1);
 #undef RS_DEQ_LAUNCH
-  return after_launch(fn);
+    RS_TRY(after_launch(fn));
+  }
+  return RS_OK;
 }
 
 extern "C" rs_status rs_adamw_step(const rs_layout* L, float* p, const float* g, float* m, float* v,
@@ -1729,13 +1764,18 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
   const int64_t w0 = L->rank_work[k0], nw = L->rank_work[k1] - w0;
   if (nw == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 gr(static_cast<unsigned>(nw)), b(kThreads * RS_ADAM8_F);
+  const dim3 b(kThreads * RS_ADAM8_F);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
-  if (fmt == RS_Q_FP8_E4M3)
-    hipLaunchKernelGGL((adamw8_kernel<RS_Q_FP8_E4M3, RS_ADAM8_F>), gr, b, 0, s, wk, w0, p, g,
-                       m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
-  else
-    hipLaunchKernelGGL((adamw8_kernel<RS_Q_INT8, RS_ADAM8_F>), gr, b, 0, s, wk, w0, p, g,
-                       m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
-  return after_launch(fn);
+  const int64_t per = max_groups(kThreads * RS_ADAM8_F);
+  for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one work item per workgroup
+    const dim3 gr(static_cast<unsigned>(std::min(per, w0 + nw - w1)));
+    if (fmt == RS_Q_FP8_E4M3)
+      hipLaunchKernelGGL((adamw8_kernel<RS_Q_FP8_E4M3, RS_ADAM8_F>), gr, b, 0, s, wk, w1, p, g,
+                         m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
+    else
+      hipLaunchKernelGGL((adamw8_kernel<RS_Q_INT8, RS_ADAM8_F>), gr, b, 0, s, wk, w1, p, g,
+                         m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
+    RS_TRY(after_launch(fn));
+  }
+  return RS_OK;
 }

@@ -18,10 +18,15 @@
  * ... rs_block_quant) only enqueue kernels on `stream`: they never allocate,
  * copy from the host or synchronise, and return before the work is done.
  *
- * Errors.  Every call returns an rs_status.  On a non-zero status nothing
- * was enqueued, no output was touched, and rs_last_error() returns a
- * message for the calling thread.  RS_ERR_HIP reports a failed launch
- * (hipGetLastError after the launch).
+ * Launches.  A call enqueues one kernel (the norms: two).  A range with
+ * more workgroups than one launch may hold (2^31 lanes) is covered by
+ * several launches of the same kernel on `stream`, in order.
+ *
+ * Errors.  Every call returns an rs_status.  On a non-zero status from
+ * argument checking nothing was enqueued, no output was touched, and
+ * rs_last_error() returns a message for the calling thread.  RS_ERR_HIP
+ * reports a failed launch (hipGetLastError after each launch); launches of
+ * the same call before the failed one stay enqueued.
  *
  * Alignment.  Kernels use 128-bit accesses where a fragment's buffer and
  * tensor addresses are 16-byte aligned, and element accesses elsewhere, so
