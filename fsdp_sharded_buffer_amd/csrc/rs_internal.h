@@ -69,6 +69,20 @@ struct QuantWork {
 static_assert(sizeof(QuantWork) == 64, "QuantWork layout");
 
 constexpr int kMaxTileElems = 16384;  // 256 lanes x 64 elements held in registers
+
+// Size limits that keep every product and sum of sizes inside int64: fewer
+// than 2^40 elements per tensor, per granule and per group, at most 2^20
+// tensors, 2^18 ranks and an alignment of 2^20 elements.  Then S <= 2^41
+// and m*S <= 2^59.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int32_t kMaxTensors = 1 << 20;
+constexpr int32_t kMaxRanks = 1 << 18;
+constexpr int64_t kMaxAlign = int64_t(1) << 20;
+
+inline bool spec_sizes_ok(const rs_tensor_spec& s) {
+  return s.rows > 0 && s.cols > 0 && s.gran_rows >= 0 && s.rows < kMaxElems / s.cols &&
+         s.gran_rows < kMaxElems / s.cols;
+}
 #ifndef RS_DEFAULT_CHUNK
 #define RS_DEFAULT_CHUNK 2048
 #endif

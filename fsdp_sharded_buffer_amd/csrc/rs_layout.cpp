@@ -209,6 +209,9 @@ extern "C" rs_status rs_layout_create(const rs_tensor_spec* specs, int32_t n, in
                                       rs_layout** out) {
   if (!specs || !offsets || !out || n <= 0 || m <= 0 || S <= 0)
     return fail(RS_ERR_INVALID_ARG, "rs_layout_create: null pointer or non-positive n/m/S");
+  if (n > kMaxTensors || m > kMaxRanks || S > 2 * kMaxElems)
+    return fail(RS_ERR_INVALID_ARG,
+                "rs_layout_create: more than 2^20 tensors or 2^18 ranks, or S above 2^41");
   if (chunk_elems == 0) chunk_elems = kDefaultChunk;
   if (chunk_elems < 64 || chunk_elems % 64 || chunk_elems > (int64_t(1) << 22))
     return fail(RS_ERR_INVALID_ARG, "rs_layout_create: chunk_elems must be a multiple of 64");
@@ -216,8 +219,10 @@ extern "C" rs_status rs_layout_create(const rs_tensor_spec* specs, int32_t n, in
   for (int32_t t = 0; t < n; ++t) {
     const rs_tensor_spec& s = specs[t];
     const std::string name = "tensor " + std::to_string(t);
-    if (s.rows <= 0 || s.cols <= 0 || s.gran_rows < 0)
-      return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name + " has a bad shape");
+    if (!spec_sizes_ok(s))
+      return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name +
+                                          " has a bad shape (positive, fewer than 2^40 elements "
+                                          "per tensor and granule)");
     if ((s.q_rows > 0) != (s.q_cols > 0) || s.q_rows < 0 || s.q_cols < 0 ||
         int64_t(s.q_rows) * s.q_cols > kMaxTileElems ||
         int64_t(s.q_rows) * s.cols > int64_t(INT32_MAX) ||
@@ -230,7 +235,7 @@ extern "C" rs_status rs_layout_create(const rs_tensor_spec* specs, int32_t n, in
     const int64_t l = offsets[t], E = s.rows * s.cols, g = granule_of(s);
     if (l < prev_end)
       return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name + " overlaps the previous tensor");
-    if (l + E > S * m)
+    if (l > S * m - E)
       return fail(RS_ERR_INVALID_ARG, "rs_layout_create: " + name + " ends past the buffer");
     for (int64_t b = (l / S + 1) * S; b < l + E; b += S)
       if ((b - l) % g)

@@ -191,14 +191,21 @@ rs_status plan_items(const std::vector<PItem>& items, int32_t m, int64_t align, 
 
 rs_status read_items(const char* fn, const rs_tensor_spec* specs, int32_t n,
                      std::vector<PItem>& items) {
+  if (n > kMaxTensors)
+    return fail(RS_ERR_INVALID_ARG, std::string(fn) + ": more than 2^20 tensors");
   items.resize(n);
+  int64_t total = 0;
   for (int32_t t = 0; t < n; ++t) {
     const rs_tensor_spec& s = specs[t];
-    if (s.rows <= 0 || s.cols <= 0 || s.gran_rows < 0)
-      return fail(RS_ERR_INVALID_ARG,
-                  std::string(fn) + ": tensor " + std::to_string(t) + " has a bad shape");
+    if (!spec_sizes_ok(s))
+      return fail(RS_ERR_INVALID_ARG, std::string(fn) + ": tensor " + std::to_string(t) +
+                                          " has a bad shape (positive, fewer than 2^40 elements "
+                                          "per tensor and granule)");
     items[t].E = s.rows * s.cols;
     items[t].g = s.gran_rows > 0 ? s.gran_rows * s.cols : 1;
+    total += items[t].E;
+    if (total >= kMaxElems)
+      return fail(RS_ERR_INVALID_ARG, std::string(fn) + ": 2^40 or more elements in the group");
   }
   return RS_OK;
 }
@@ -244,6 +251,8 @@ extern "C" rs_status rs_plan(const rs_tensor_spec* specs, int32_t n, int32_t m, 
   const auto t0 = std::chrono::steady_clock::now();
   if (!specs || !offsets || n <= 0 || m <= 0 || align <= 0)
     return fail(RS_ERR_INVALID_ARG, "rs_plan: null pointer or non-positive n/m/align");
+  if (m > kMaxRanks || align > kMaxAlign)
+    return fail(RS_ERR_INVALID_ARG, "rs_plan: more than 2^18 ranks or align above 2^20");
   std::vector<PItem> items;
   rs_status st = read_items("rs_plan", specs, n, items);
   if (st != RS_OK) return st;
@@ -276,6 +285,8 @@ extern "C" rs_status rs_plan_ordered(const rs_tensor_spec* specs, int32_t n, int
   const auto t0 = std::chrono::steady_clock::now();
   if (!specs || !perm || !offsets || n <= 0 || m <= 0 || align <= 0)
     return fail(RS_ERR_INVALID_ARG, "rs_plan_ordered: null pointer or non-positive n/m/align");
+  if (m > kMaxRanks || align > kMaxAlign)
+    return fail(RS_ERR_INVALID_ARG, "rs_plan_ordered: more than 2^18 ranks or align above 2^20");
   if (kind != RS_ORDER_GIVEN && kind != RS_ORDER_BLOCK && kind != RS_ORDER_SHAPE &&
       kind != RS_ORDER_BEST)
     return fail(RS_ERR_INVALID_ARG, "rs_plan_ordered: unknown order kind");

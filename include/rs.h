@@ -18,6 +18,10 @@
  * ... rs_block_quant) only enqueue kernels on `stream`: they never allocate,
  * copy from the host or synchronise, and return before the work is done.
  *
+ * Limits.  Fewer than 2^40 elements per tensor, per granule and per group;
+ * at most 2^20 tensors, 2^18 ranks and an alignment of 2^20 elements; S at
+ * most 2^41.  Calls outside them return RS_ERR_INVALID_ARG.
+ *
  * Launches.  A call enqueues one kernel (the norms: two).  A range with
  * more workgroups than one launch may hold (2^31 lanes) is covered by
  * several launches of the same kernel on `stream`, in order.

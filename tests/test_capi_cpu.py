@@ -199,6 +199,40 @@ def test_planner_infeasible_cap_and_bad_args():
     assert "rs_plan" in R.rs_last_error()
 
 
+def test_size_limits_keep_int64_arithmetic_exact():
+    """Sizes whose products or sums could overflow int64 are rejected:
+    fewer than 2^40 elements per tensor, granule and group, at most 2^18
+    ranks, an alignment of at most 2^20, S at most 2^41."""
+    ok = [W.TensorSpec("a", 1 << 20, 1 << 19, 0)]          # 2^39 elements: accepted
+    offs, info = R.rs_plan(ok, 1 << 18, 1 << 20)
+    assert info["S"] >= (1 << 39) >> 18
+    bad = [
+        ([W.TensorSpec("a", 1 << 20, 1 << 20, 0)], 2, 1),            # 2^40 elements
+        ([W.TensorSpec("a", 2, 3, 1 << 62)], 2, 1),                   # granule overflows
+        ([W.TensorSpec("a", 1 << 62, 4, 0)], 2, 1),                   # rows * cols overflows
+        ([W.TensorSpec("a", 1 << 20, 1 << 19, 0)] * 2, 2, 1),         # group of 2^40
+        ([W.TensorSpec("a", 4, 4, 0)], (1 << 18) + 1, 1),             # ranks
+        ([W.TensorSpec("a", 4, 4, 0)], 2, (1 << 20) + 1),             # alignment
+    ]
+    for specs, m, align in bad:
+        with pytest.raises(R.RsError) as e:
+            R.rs_plan(specs, m, align)
+        assert e.value.status == -1
+        with pytest.raises(R.RsError) as e:
+            R.rs_plan_ordered(specs, m, align, "best")
+        assert e.value.status == -1
+    small = [W.TensorSpec("a", 4, 4, 0)]
+    for specs, m, S, offs in [
+        (small, (1 << 18) + 1, 16, [0]),                             # ranks
+        (small, 2, (1 << 41) + 1, [0]),                              # S
+        (small, 2, 16, [(1 << 62)]),                                 # offset: l + E overflows
+        ([W.TensorSpec("a", 1 << 62, 4, 0)], 2, 16, [0]),            # rows * cols overflows
+    ]:
+        with pytest.raises(R.RsError) as e:
+            R.rs_layout_create(specs, m, S, offs)
+        assert e.value.status == -1, R.rs_last_error()
+
+
 def test_plan_order_entry_points_reject_bad_args():
     specs = [W.TensorSpec("a", 12, 1, 4), W.TensorSpec("b", 4, 2, 1)]
     with pytest.raises(R.RsError) as e:
