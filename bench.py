@@ -398,7 +398,8 @@ def main():
 
     timed = dict(per_op, **per_extra)
     dom = "scale_add" if "scale_add" in timed else next(iter(timed))
-    roof = {"kernel": "scale_add_kernel<fp32>" if dom == "scale_add" else dom,
+    # the dominant kernel as rocprofv3 names it (template argument 0: x in fp32)
+    roof = {"kernel": "scale_add_kernel<0>" if dom == "scale_add" else dom,
             "bound": "hbm", "achieved": timed[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": timed[dom]["frac_peak"],
             "traffic": read_counters(w.name) if dom == "scale_add" else None,
