@@ -70,6 +70,15 @@ static_assert(sizeof(QuantWork) == 64, "QuantWork layout");
 
 constexpr int kMaxTileElems = 16384;  // 256 lanes x 64 elements held in registers
 
+// Tiles of at most kNarrowTileElems elements are "narrow": a team of at most
+// 256 lanes holds one with at most kNarrowSlots four-element slots per lane.
+// Wider tiles take 256 lanes with up to kWideSlots slots per lane.  The tile
+// kernels are compiled for each class, so narrow tiles carry no registers or
+// loop iterations for slots they never have.
+constexpr int kNarrowTileElems = 4096;
+constexpr int kNarrowSlots = 4;
+constexpr int kWideSlots = kMaxTileElems / 4 / 256;
+
 // Size limits that keep every product and sum of sizes inside int64: fewer
 // than 2^40 elements per tensor, per granule and per group, at most 2^20
 // tensors, 2^18 ranks and an alignment of 2^20 elements.  Then S <= 2^41
@@ -109,10 +118,13 @@ struct rs_layout {
   std::vector<rs::QuantWork> work;
 
   // per-rank begin indices, size m + 1
-  std::vector<int64_t> rank_chunk, rank_cchunk, rank_frag, rank_work;
-  std::vector<int32_t> rank_min_tile_rows;  // per rank; INT32_MAX when it has no tile
-  std::vector<int64_t> rank_small_tiles;    // per rank: tiles taken by fewer than 256 lanes
-  std::vector<int64_t> rank_big_tiles;      // per rank: tiles taken by 256 lanes
+  std::vector<int64_t> rank_chunk, rank_cchunk, rank_frag;
+  // The work table holds the narrow tiles' items (class 0), then the wide
+  // tiles' items (class 1), each list in buffer order.  rank_work[c][k] is
+  // rank k's first item of class c as an index into the whole table, and
+  // rank_work[c][m] ends the list.
+  std::vector<int64_t> rank_work[2];
+  std::vector<int32_t> rank_min_tile_rows[2];  // per class and rank; INT32_MAX without tiles
 
   // byte offsets of each table inside the device blob
   size_t off_tensors = 0, off_frags = 0, off_chunks = 0, off_cchunks = 0,

@@ -72,9 +72,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    it helps the pure streams (copies, the norm read,
 //                    quantisation input) and hurts read-modify-write
 //                    (scale/add, zero, the fp32 optimizers)
-//   RS_QUANT_F,      256-lane sub-blocks per quantisation work item, for
-//   RS_QUANT_F_SMALL launches of at least / fewer than RS_QUANT_SMALL_ITEMS
-//                    work items (one sub-block where most tiles are small)
+//   RS_QUANT_F,      256-lane sub-blocks per quantisation work item of wide
+//   RS_QUANT_F_SMALL tiles, for launches of at least / fewer than
+//                    RS_QUANT_SMALL_ITEMS work items (narrow tiles: one)
 //   RS_SQNORM_FINE_BELOW  the norm reads fine chunks when the range has
 //                    fewer coarse chunks than this (too few workgroups)
 //   RS_FILL_BYTES    bytes per workgroup of the unmasked zero: one 16-byte
@@ -83,9 +83,10 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    AdamW / SGD steps, beside their read-modify-write streams
 //   RS_ADAMW_SPLIT,  workgroups per chunk of the AdamW / SGD steps
 //   RS_SGD_SPLIT
-//   RS_DEQ_SPLIT     row bands (workgroups) per dequantised tile
+//   RS_DEQ_SPLIT     row bands (workgroups) per dequantised tile, where every
+//                    tile of the class and range has that many rows
 //   RS_DEQ_LDS       stage a tile's codes in LDS before decoding
-//   RS_ADAM8_F       256-lane sub-blocks per 8-bit Adam work item
+//   RS_ADAM8_F       256-lane sub-blocks per 8-bit Adam work item of wide tiles
 //   RS_ADAM8_BATCH   8-bit Adam slots loaded ahead of their arithmetic
 #ifndef RS_UNROLL
 #define RS_UNROLL 2
@@ -663,12 +664,12 @@ __device__ __forceinline__ Tile tile_of(const QuantWork& w, int j) {
 
 // Each workgroup takes `count` consecutive tiles; tile j of the item is
 // handled by lanes [j*team, (j+1)*team) of each of F sub-blocks of kThreads
-// lanes, sub-block f taking slots [f*16/F, (f+1)*16/F) of the lane's 16
-// four-element slots.  On the 16-byte path a lane keeps its (at most 64/F)
-// elements in registers between the absmax and the encode pass, so x is
-// read once; the other path reads x twice.  F > 1 finishes each tile
-// sooner, for launches with few tiles.
-template <int FMT, int F>
+// lanes, sub-block f taking slots [f*NS, (f+1)*NS) of the lane's F*NS
+// four-element slots (narrow tiles: F = 1, NS = 4; wide tiles: F*NS = 16).
+// On the 16-byte path a lane keeps its 4*NS elements in registers between
+// the absmax and the encode pass, so x is read once; the other path reads x
+// twice.  F > 1 finishes each wide tile sooner, for launches with few tiles.
+template <int FMT, int F, int NS>
 __global__ __launch_bounds__(kThreads* F) void quant_kernel(const QuantWork* __restrict__ work,
                                                             int64_t w0,
                                                             const float* __restrict__ x,
@@ -676,7 +677,6 @@ __global__ __launch_bounds__(kThreads* F) void quant_kernel(const QuantWork* __r
                                                             float* __restrict__ scales,
                                                             uint32_t* __restrict__ found_inf,
                                                             int vec_ok) {
-  constexpr int NS = 16 / F;
   __shared__ uint32_t lds[kThreads * F / kWave];
   __shared__ uint32_t ldt[F][kThreads];
   const QuantWork w = work[w0 + blockIdx.x];
@@ -1127,8 +1127,9 @@ __global__ __launch_bounds__(kThreads) void sgd_kernel(
 // (codes + one fp32 scale per tile, the layout's tile table).  Per tile:
 // dequantise m and v, the AdamW update in fp32, requantise m' and v' with
 // their new absmax scales.  A work item (the quantisation kernel's: `count`
-// tiles of `team` lanes, at most 16 four-element slots per lane) is spread
-// over F sub-blocks of kThreads threads, each taking 16/F of the slots, so a
+// tiles of `team` lanes) is spread over F sub-blocks of kThreads threads,
+// each taking NS of the lane's four-element slots (narrow tiles: F = 1,
+// NS = 4; wide tiles: F*NS = 16), so a
 // lane keeps its m' and v' in registers between the absmax pass and the
 // encode pass (every input is read once) at a modest register count.  The
 // first pass also writes p', which does not depend on the new scales, so
@@ -1206,12 +1207,12 @@ __device__ __forceinline__ float adam_p(float p, float m2, float v2, const AdamC
   return p * k.decay - k.step * (m2 / den);
 }
 
-template <int FMT, int F>
+template <int FMT, int F, int NS>
 __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
     const QuantWork* __restrict__ work, int64_t w0, float* __restrict__ p, const float* __restrict__ g, uint8_t* __restrict__ mc,
     float* __restrict__ ms, uint8_t* __restrict__ vc, float* __restrict__ vs, AdamConst k,
     const uint32_t* __restrict__ found_inf, int m_ranks, int vec_ok) {
-  constexpr int NS = 16 / F;  // slots per lane
+  // NS slots per lane and sub-block (narrow tiles: F = 1, NS = 4)
   __shared__ uint32_t ldw[2][kThreads * F / kWave];
   __shared__ uint32_t ldt[2][F][kThreads];
   if (skip_step(found_inf, m_ranks)) return;
@@ -1576,43 +1577,38 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
   // the 16-byte path needs x 16-byte aligned and codes 4-byte aligned
   const int vec_ok = (reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(codes) % 4 == 0) ? 1 : 0;
-  const int64_t w0 = L->rank_work[k0], nw = L->rank_work[k1] - w0;
-  if (nw == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
-  // Big tiles (256 lanes each) are spread over sub-blocks, more of them in
-  // launches with few work items; ranges where most tiles are small (a few
-  // lanes each, whose absmax stays within a wave) keep one sub-block.
-  int64_t small_tiles = 0, big_tiles = 0;
-  for (int32_t k = k0; k < k1; ++k) {
-    small_tiles += L->rank_small_tiles[k];
-    big_tiles += L->rank_big_tiles[k];
-  }
-  const int F = small_tiles > big_tiles ? 1
-                : nw < RS_QUANT_SMALL_ITEMS ? RS_QUANT_F_SMALL
-                                            : RS_QUANT_F;
-  const dim3 b(kThreads * F);
-  const int64_t per = max_groups(kThreads * F);
-  for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one work item per workgroup
-    const dim3 g(static_cast<unsigned>(std::min(per, w0 + nw - w1)));
+  // One launch per tile class present in the range.  Narrow tiles: one
+  // sub-block, 4 slots per lane.  Wide tiles: 256-lane tiles spread over F
+  // sub-blocks, more of them in launches with few work items.
+  for (int c = 0; c < 2; ++c) {
+    const int64_t w0 = L->rank_work[c][k0], nw = L->rank_work[c][k1] - w0;
+    if (nw == 0) continue;
+    const int F = c == 0 ? 1 : nw < RS_QUANT_SMALL_ITEMS ? RS_QUANT_F_SMALL : RS_QUANT_F;
+    const dim3 b(kThreads * F);
+    const int64_t per = max_groups(kThreads * F);
+    for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one work item per workgroup
+      const dim3 g(static_cast<unsigned>(std::min(per, w0 + nw - w1)));
 #define RS_QUANT_LAUNCH(FM)                                                                    \
   do {                                                                                         \
-    if (F == 1)                                                                                \
-      hipLaunchKernelGGL((quant_kernel<FM, 1>), g, b, 0, s, wk, w1, x, codes, scales,          \
-                         found_inf, vec_ok);                                                   \
-    else if (F == RS_QUANT_F_SMALL)                                                            \
-      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F_SMALL>), g, b, 0, s, wk, w1, x, codes,   \
+    if (c == 0)                                                                                \
+      hipLaunchKernelGGL((quant_kernel<FM, 1, kNarrowSlots>), g, b, 0, s, wk, w1, x, codes,    \
                          scales, found_inf, vec_ok);                                           \
+    else if (F == RS_QUANT_F_SMALL)                                                            \
+      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F_SMALL, kWideSlots / RS_QUANT_F_SMALL>),  \
+                         g, b, 0, s, wk, w1, x, codes, scales, found_inf, vec_ok);             \
     else                                                                                       \
-      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F>), g, b, 0, s, wk, w1, x, codes, scales, \
-                         found_inf, vec_ok);                                                   \
+      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F, kWideSlots / RS_QUANT_F>), g, b, 0, s,  \
+                         wk, w1, x, codes, scales, found_inf, vec_ok);                         \
   } while (0)
-    if (fmt == RS_Q_FP8_E4M3)
-      RS_QUANT_LAUNCH(RS_Q_FP8_E4M3);
-    else
-      RS_QUANT_LAUNCH(RS_Q_INT8);
+      if (fmt == RS_Q_FP8_E4M3)
+        RS_QUANT_LAUNCH(RS_Q_FP8_E4M3);
+      else
+        RS_QUANT_LAUNCH(RS_Q_INT8);
 #undef RS_QUANT_LAUNCH
-    RS_TRY(after_launch(fn));
+      RS_TRY(after_launch(fn));
+    }
   }
   return RS_OK;
 }
@@ -1631,19 +1627,21 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
   const uintptr_t ca = reinterpret_cast<uintptr_t>(codes), ya = reinterpret_cast<uintptr_t>(y);
   int vec_ok = (ca % 4 == 0 && ya % (y_dt == RS_F32 ? 16 : 8) == 0) ? 1 : 0;
   if (vec_ok && ca % 16 == 0) vec_ok = 2;
-  const int64_t w0 = L->rank_work[k0], nw = L->rank_work[k1] - w0;
-  if (nw == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // row bands per work item when every tile of the range has that many rows
-  int32_t min_rows = INT32_MAX;
-  for (int32_t k = k0; k < k1; ++k) min_rows = std::min(min_rows, L->rank_min_tile_rows[k]);
-  const bool split = RS_DEQ_SPLIT > 1 && min_rows >= RS_DEQ_SPLIT;
-  const int64_t bands = split ? RS_DEQ_SPLIT : 1;
-  const dim3 b(kThreads);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
-  const int64_t per = std::max<int64_t>(1, max_groups(kThreads) / bands);  // items per launch
-  for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one workgroup per band of a work item
-    const dim3 g(static_cast<unsigned>(std::min(per, w0 + nw - w1) * bands));
+  for (int c = 0; c < 2; ++c) {  // one launch per tile class present in the range
+    const int64_t w0 = L->rank_work[c][k0], nw = L->rank_work[c][k1] - w0;
+    if (nw == 0) continue;
+    // row bands per work item when every tile of the class and range has
+    // that many rows
+    int32_t min_rows = INT32_MAX;
+    for (int32_t k = k0; k < k1; ++k) min_rows = std::min(min_rows, L->rank_min_tile_rows[c][k]);
+    const bool split = RS_DEQ_SPLIT > 1 && min_rows >= RS_DEQ_SPLIT;
+    const int64_t bands = split ? RS_DEQ_SPLIT : 1;
+    const dim3 b(kThreads);
+    const int64_t per = std::max<int64_t>(1, max_groups(kThreads) / bands);  // items per launch
+    for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one workgroup per band of a work item
+      const dim3 g(static_cast<unsigned>(std::min(per, w0 + nw - w1) * bands));
 #define RS_DEQ_LAUNCH(FM, YK)                                                                  \
   do {                                                                                         \
     if (split)                                                                                 \
@@ -1653,16 +1651,17 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
       hipLaunchKernelGGL((dequant_kernel<FM, YK, 1>), g, b, 0, s, wk, w1, codes, scales, y,      \
                          vec_ok);                                                              \
   } while (0)
-    if (fmt == RS_Q_FP8_E4M3 && y_dt == RS_F32)
-      RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 0);
-    else if (fmt == RS_Q_FP8_E4M3)
-      RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 1);
-    else if (y_dt == RS_F32)
-      RS_DEQ_LAUNCH(RS_Q_INT8, 0);
-    else
-      RS_DEQ_LAUNCH(RS_Q_INT8, 1);
+      if (fmt == RS_Q_FP8_E4M3 && y_dt == RS_F32)
+        RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 0);
+      else if (fmt == RS_Q_FP8_E4M3)
+        RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 1);
+      else if (y_dt == RS_F32)
+        RS_DEQ_LAUNCH(RS_Q_INT8, 0);
+      else
+        RS_DEQ_LAUNCH(RS_Q_INT8, 1);
 #undef RS_DEQ_LAUNCH
-    RS_TRY(after_launch(fn));
+      RS_TRY(after_launch(fn));
+    }
   }
   return RS_OK;
 }
@@ -1761,21 +1760,35 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
                       reinterpret_cast<uintptr_t>(g) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(m_codes) % 4 == 0 &&
                       reinterpret_cast<uintptr_t>(v_codes) % 4 == 0) ? 1 : 0;
-  const int64_t w0 = L->rank_work[k0], nw = L->rank_work[k1] - w0;
-  if (nw == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 b(kThreads * RS_ADAM8_F);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
-  const int64_t per = max_groups(kThreads * RS_ADAM8_F);
-  for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one work item per workgroup
-    const dim3 gr(static_cast<unsigned>(std::min(per, w0 + nw - w1)));
-    if (fmt == RS_Q_FP8_E4M3)
-      hipLaunchKernelGGL((adamw8_kernel<RS_Q_FP8_E4M3, RS_ADAM8_F>), gr, b, 0, s, wk, w1, p, g,
-                         m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
-    else
-      hipLaunchKernelGGL((adamw8_kernel<RS_Q_INT8, RS_ADAM8_F>), gr, b, 0, s, wk, w1, p, g,
-                         m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);
-    RS_TRY(after_launch(fn));
+  // one launch per tile class present in the range: narrow tiles with one
+  // sub-block of 4 slots per lane, wide tiles over RS_ADAM8_F sub-blocks
+  for (int c = 0; c < 2; ++c) {
+    const int64_t w0 = L->rank_work[c][k0], nw = L->rank_work[c][k1] - w0;
+    if (nw == 0) continue;
+    const int F = c == 0 ? 1 : RS_ADAM8_F;
+    const dim3 b(kThreads * F);
+    const int64_t per = max_groups(kThreads * F);
+    for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one work item per workgroup
+      const dim3 gr(static_cast<unsigned>(std::min(per, w0 + nw - w1)));
+#define RS_ADAM8_LAUNCH(FM)                                                                     \
+  do {                                                                                          \
+    if (c == 0)                                                                                 \
+      hipLaunchKernelGGL((adamw8_kernel<FM, 1, kNarrowSlots>), gr, b, 0, s, wk, w1, p, g,       \
+                         m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);     \
+    else                                                                                        \
+      hipLaunchKernelGGL((adamw8_kernel<FM, RS_ADAM8_F, kWideSlots / RS_ADAM8_F>), gr, b, 0, s, \
+                         wk, w1, p, g, m_codes, m_scales, v_codes, v_scales, k, found_inf,      \
+                         L->m, vec_ok);                                                         \
+  } while (0)
+      if (fmt == RS_Q_FP8_E4M3)
+        RS_ADAM8_LAUNCH(RS_Q_FP8_E4M3);
+      else
+        RS_ADAM8_LAUNCH(RS_Q_INT8);
+#undef RS_ADAM8_LAUNCH
+      RS_TRY(after_launch(fn));
+    }
   }
   return RS_OK;
 }

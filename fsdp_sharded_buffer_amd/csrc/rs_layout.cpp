@@ -19,10 +19,13 @@ int64_t granule_of(const rs_tensor_spec& s) { return s.gran_rows > 0 ? s.gran_ro
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Lanes per tile: enough that no lane holds more than 64 elements.
+// Lanes per tile: a narrow tile takes the smallest power of two from 8
+// lanes up that holds it at 16 elements (4 slots) per lane; a wide tile
+// takes 256 lanes (up to 64 elements each).
 int team_for(int64_t elems) {
+  if (elems > kNarrowTileElems) return 256;
   int team = 8;
-  while (team < 256 && int64_t(team) * 64 < elems) team *= 2;
+  while (team < 256 && int64_t(team) * 4 * kNarrowSlots < elems) team *= 2;
   return team;
 }
 
@@ -95,10 +98,10 @@ rs_status build(rs_layout* L) {
   L->work.clear();
   L->num_tiles = 0;
   L->rank_frag.assign(m + 1, 0);
-  L->rank_work.assign(m + 1, 0);
-  L->rank_min_tile_rows.assign(m, INT32_MAX);
-  L->rank_small_tiles.assign(m, 0);
-  L->rank_big_tiles.assign(m, 0);
+  for (int c = 0; c < 2; ++c) {
+    L->rank_work[c].assign(m + 1, 0);
+    L->rank_min_tile_rows[c].assign(m, INT32_MAX);
+  }
 
   build_chunks(L, L->chunk_elems, L->chunks, L->rank_chunk, true);
   build_chunks(L, L->chunk_elems * kCoarseFactor, L->cchunks, L->rank_cchunk, false);
@@ -121,11 +124,13 @@ rs_status build(rs_layout* L) {
 
   // quantisation tiles, tensor by tensor, row-major (ranks are
   // non-decreasing in this order because tensors and tile rows are), cut
-  // into runs of consecutive tiles of one tensor and rank with the same team
-  // size and vector flag
+  // into runs of consecutive tiles of one tensor and rank with the same
+  // class, team size and vector flag; each class keeps its own list
   int64_t scale_idx = 0;
   bool open = false;
+  int cur_cls = 0;
   QuantWork cur{};
+  std::vector<QuantWork> lists[2];
   for (int32_t t = 0; t < n; ++t) {
     const rs_tensor_spec& s = L->specs[t];
     if (s.q_rows <= 0) continue;
@@ -141,18 +146,20 @@ rs_status build(rs_layout* L) {
                       "rs_layout_create: a quantisation tile of tensor " + std::to_string(t) +
                           " crosses a shard boundary");
         const int32_t rank = int32_t(first / S);
+        const int cls = rows * cols > kNarrowTileElems ? 1 : 0;
         const int32_t team = team_for(rows * cols);
         const int32_t vec = (cols % 4 == 0 && s.cols % 4 == 0 && first % 4 == 0) ? 1 : 0;
         const int64_t idx = tr * ntc + tc;
         if (scale_idx >= INT32_MAX)
           return fail(RS_ERR_INVALID_ARG, "rs_layout_create: more than 2^31 quantisation tiles");
-        L->rank_min_tile_rows[rank] = std::min(L->rank_min_tile_rows[rank], int32_t(rows));
-        ++(team < 256 ? L->rank_small_tiles : L->rank_big_tiles)[rank];
-        if (open && cur.rank == rank && cur.team == team && cur.vec == vec &&
+        L->rank_min_tile_rows[cls][rank] =
+            std::min(L->rank_min_tile_rows[cls][rank], int32_t(rows));
+        if (open && cur_cls == cls && cur.rank == rank && cur.team == team && cur.vec == vec &&
             cur.count < 256 / team && cur.base == l && int64_t(cur.t0) + cur.count == idx) {
           ++cur.count;
         } else {
-          if (open) L->work.push_back(cur);
+          if (open) lists[cur_cls].push_back(cur);
+          cur_cls = cls;
           cur = QuantWork{};
           cur.base = l;
           cur.t0 = int32_t(idx);
@@ -172,15 +179,17 @@ rs_status build(rs_layout* L) {
       }
     }
   }
-  if (open) L->work.push_back(cur);
+  if (open) lists[cur_cls].push_back(cur);
   L->num_tiles = scale_idx;
-  // each rank's first work item
-  {
+  // the narrow list, then the wide list; each rank's first item of each
+  for (int c = 0; c < 2; ++c) {
+    const int64_t base = int64_t(L->work.size());
     size_t i = 0;
     for (int32_t k = 0; k <= m; ++k) {
-      while (i < L->work.size() && L->work[i].rank < k) ++i;
-      L->rank_work[k] = int64_t(i);
+      while (i < lists[c].size() && lists[c][i].rank < k) ++i;
+      L->rank_work[c][k] = base + int64_t(i);
     }
+    L->work.insert(L->work.end(), lists[c].begin(), lists[c].end());
   }
 
   size_t off = 0;
