@@ -36,7 +36,7 @@ def _random_workload(seed):
         kind = rng.integers(0, 3)
         if kind == 0:                                   # vector, element granular
             ts.append(W.TensorSpec(f"v{i}", 1, int(rng.integers(1, 3000)), 0))
-        elif kind == 2 and rng.random() < 0.35:        # big tiles: teams of 64-256 lanes
+        elif kind == 2 and rng.random() < 0.35:        # big tiles: narrow (128-256 lanes) and wide
             g = int(rng.choice([32, 64, 128]))
             cols = int(rng.choice([128, 256, 384]))
             qc = int(rng.choice([64, 128]))
