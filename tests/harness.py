@@ -188,6 +188,15 @@ def _tiny():
     return W.Workload("tiny", ts, m=3, qfmt="int8", block=5)
 
 
+def _tall():
+    """Tall, thin tiles: 4096x1 (narrow, one 256-lane team) and 16384x1
+    (wide, the largest tile) on the element path, and 512x4 (narrow, one
+    16-byte slot per row), on 2 ranks."""
+    ts = (W.TensorSpec("a", 8192, 3, 4096, 4096, 1), W.TensorSpec("b", 16384, 2, 16384, 16384, 1),
+          W.TensorSpec("c", 1024, 4, 512, 512, 4))
+    return W.Workload("tall", ts, m=2, qfmt="fp8_e4m3", block=1)
+
+
 def _no_quant():
     """Vectors only: no quantisation tiles at all."""
     ts = (W.TensorSpec("v1", 1, 1000, 0), W.TensorSpec("v2", 1, 77, 0))
@@ -210,6 +219,7 @@ SMALL = {
     "pad_ranks": lambda: (_pad_ranks(), 1, 64),
     "tiny": lambda: (_tiny(), 1, 64),
     "no_quant": lambda: (_no_quant(), 16, 128),
+    "tall": lambda: (_tall(), 16, 0),
     "toy_chunk_max": lambda: (W.toy_unit(), 16, 1 << 22),   # largest chunk: one per fragment
 }
 
