@@ -197,6 +197,8 @@ def ptr_table(tensors, device=None):
     tensor -> buffer mapping that rs_pack / rs_unpack read."""
     import torch
     ptrs = [t.data_ptr() for t in tensors]
+    if device is None and not ptrs:
+        raise ValueError("ptr_table: no tensors and no device")
     dev = device if device is not None else tensors[0].device
     return torch.tensor(ptrs, dtype=torch.int64, device=dev)
 
@@ -211,10 +213,15 @@ class Layout:
         self.specs = list(specs)
         self.m, self.S, self.offsets = m, S, list(offsets)
         self.handle = rs_layout_create(self.specs, m, S, self.offsets, chunk_elems)
-        self.info = rs_layout_get_info(self.handle)
-        self.table = torch.empty(self.info["device_bytes"], dtype=torch.uint8, device=device)
-        rs_layout_upload(self.handle, self.table, stream)
-        self.ws = torch.zeros(max(self.info["workspace_bytes"], 8), dtype=torch.uint8, device=device)
+        try:
+            self.info = rs_layout_get_info(self.handle)
+            self.table = torch.empty(self.info["device_bytes"], dtype=torch.uint8, device=device)
+            rs_layout_upload(self.handle, self.table, stream)
+            self.ws = torch.zeros(max(self.info["workspace_bytes"], 8), dtype=torch.uint8,
+                                  device=device)
+        except BaseException:
+            self.close()  # the host tables are freed; the torch buffers go with self
+            raise
 
     @classmethod
     def plan(cls, specs, m: int, align: int = 16, chunk_elems: int = 0, device="cuda",
