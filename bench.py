@@ -432,6 +432,21 @@ def main():
         med, _, _ = event_ms(opt.step, 5)
         ref["fused_sgd_64M"] = round(20 * k / (med * 1e-3) / 1e9, 1)
         del prm, opt
+        if args.per_rank:
+            # one rank's share (S contiguous fp32 elements), cycling over m
+            # slices of one buffer as the per-rank launches do: context for
+            # the fixed per-launch costs at that size
+            A = torch.empty((m, S), dtype=torch.float32, device=dev).normal_()
+            B = torch.empty_like(A).normal_()
+            share = {"elements": S}
+            for name, f, per in (("copy", lambda k: B[k].copy_(A[k]), 8),
+                                 ("axpy_inplace", lambda k: B[k].add_(A[k], alpha=0.5), 12),
+                                 ("fill", lambda k: B[k].zero_(), 4),
+                                 ("l2_norm", lambda k: torch.linalg.vector_norm(A[k]), 4)):
+                med, _, _ = event_ms(lambda f=f: [f(k) for k in range(m)], 5)
+                share[name] = round(per * S * m / (med * 1e-3) / 1e9, 1)
+            ref["rank_share"] = share
+            del A, B
         ref["unit"] = "GB/s"
         log(f"torch reference: {ref}")
 
