@@ -1,8 +1,11 @@
 """GPU parity on seeded random groups: random tensor counts, shapes, row and
-block granules, tile shapes (odd widths, and big tiles taken by 64-256
-lanes), rank counts, alignments and chunk sizes.  Every operation runs on the whole rank range and on a random
-sub-range and is compared with the oracle (bit-exact; norms within 1e-5
-relative of fp64), with canary guard bands around every output."""
+block granules, tile shapes (odd widths, narrow and wide tiles), rank
+counts, alignments and chunk sizes.  A second generator draws wider groups:
+up to 64 ranks, 1 x k tiles up to 1 x 16384, tall k x 1 tiles up to
+16384 rows, square blocks of 8-128 with partial edges, alignment up to 64
+and chunks up to 4096.  Every operation runs on the whole rank range and on
+a random sub-range and is compared with the oracle (bit-exact; norms within
+1e-5 relative of fp64), with canary guard bands around every output."""
 import numpy as np
 import pytest
 
@@ -19,6 +22,7 @@ F32_CANARY = 0x7FA5A5A5
 BF16_CANARY = 0x7FA5
 U8_CANARY = 0xAB
 N_GROUPS = 120
+N_WIDE = 40
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -61,15 +65,51 @@ def _random_workload(seed):
                       seed=seed), A, chunk, rng
 
 
+def _wide_workload(seed):
+    rng = np.random.default_rng(99000 + seed)
+    ts = []
+    budget = 1_500_000
+    for i in range(int(rng.integers(1, 10))):
+        kind = int(rng.integers(0, 5))
+        if kind == 0:                                   # vector, element granular
+            ts.append(W.TensorSpec(f"v{i}", 1, int(rng.integers(1, 50000)), 0))
+        elif kind == 1:                                 # 1 x k tiles, row granular
+            cols = int(rng.choice([128, 256, 1000, 4096, 16384]))
+            qc = min(cols, int(rng.choice([64, 128, 512, 4096, 16384])))
+            rows = int(rng.integers(1, max(2, min(64, budget // cols))))
+            ts.append(W.TensorSpec(f"e{i}", rows, cols, 1, 1, qc))
+        elif kind == 2:                                 # tall k x 1 tiles
+            cols = int(rng.choice([1, 2, 3, 5]))
+            qr = int(rng.choice([256, 1024, 4096, 16384]))
+            rows = qr * int(rng.integers(1, 3)) + (int(rng.integers(0, qr)) if rng.random() < 0.5 else 0)
+            ts.append(W.TensorSpec(f"t{i}", rows, cols, qr, qr, 1))
+        elif kind == 3:                                 # square blocks with partial edges
+            b = int(rng.choice([8, 16, 32, 64, 128]))
+            cols = int(rng.integers(b // 2, 5 * b))
+            rows = int(rng.integers(1, 5)) * b + (int(rng.integers(0, b)) if rng.random() < 0.5 else 0)
+            ts.append(W.TensorSpec(f"b{i}", rows, cols, b, b, b))
+        else:                                           # row granular, not quantised
+            g = int(rng.choice([1, 2, 7]))
+            ts.append(W.TensorSpec(f"r{i}", g * int(rng.integers(1, 40)), int(rng.integers(1, 300)), g))
+    m = int(rng.integers(1, 65))
+    fmt = "fp8_e4m3" if rng.random() < 0.5 else "int8"
+    A = int(rng.choice([1, 4, 16, 64]))
+    chunk = int(rng.choice([64, 128, 2048, 4096]))
+    nf = 0.002 if rng.random() < 0.3 else 0.0
+    return W.Workload(f"wide{seed}", tuple(ts), m=m, qfmt=fmt, block=1, nonfinite_frac=nf,
+                      seed=seed), A, chunk, rng
+
+
 def _sync():
     import torch
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("seed", range(N_GROUPS))
-def test_random_group(seed):
+@pytest.mark.parametrize("gen,seed", [("basic", s) for s in range(N_GROUPS)] +
+                         [("wide", s) for s in range(N_WIDE)])
+def test_random_group(gen, seed):
     import torch
-    w, A, chunk, rng = _random_workload(seed)
+    w, A, chunk, rng = (_random_workload if gen == "basic" else _wide_workload)(seed)
     c = Case(w, A, chunk)
     R = c.R
     h = c.lay.handle
@@ -83,7 +123,7 @@ def test_random_group(seed):
     qf = R.RS_Q_FP8_E4M3 if w.qfmt == "fp8_e4m3" else R.RS_Q_INT8
     srcs = [torch.from_numpy(a).cuda() for a in inp.params]
     for k0, k1 in ranges:
-        what = f"random{seed} (n={len(w.tensors)} m={c.m} A={A} chunk={chunk}) [{k0},{k1})"
+        what = f"{w.name} (n={len(w.tensors)} m={c.m} A={A} chunk={chunk}) [{k0},{k1})"
         log(what)
         # pack fp32 -> bf16
         bw, buf = guarded(c.total, torch.bfloat16, BF16_CANARY)
