@@ -535,14 +535,17 @@ def test_pack_bf16_cast_every_fp32_pattern():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("fmt", ["fp8_e4m3", "int8"])
-def test_quant_every_fp32_up_to_amax(fmt):
-    """Quantisation of every fp32 value x with |x| <= 1344, both signs, in
-    1 x 16384 tiles whose first element is 1344: the scale is then
-    fl(1344/Q) (3 for E4M3, an inexact reciprocal either way), so the codes
-    come through the reciprocal fast path, its safety windows and the exact
-    fallback over the whole code range.  Against the oracle's cast of the
-    fp32 quotient, with the oracle on host threads."""
+@pytest.mark.parametrize("fmt,amax_value", [("fp8_e4m3", 1344.0), ("int8", 1344.0),
+                                            ("fp8_e4m3", 448.0), ("int8", 127.0)])
+def test_quant_every_fp32_up_to_amax(fmt, amax_value):
+    """Quantisation of every fp32 value x with |x| <= amax, both signs, in
+    1 x 16384 tiles whose first element is amax.  With amax = 1344 the scale
+    is fl(1344/Q) (3 for E4M3), an inexact reciprocal, so the codes come
+    through the reciprocal fast path, its safety windows and the exact
+    fallback over the whole code range.  With amax = Q the scale is 1 and
+    every code is the encoder applied to x itself: every fp32 input of the
+    code range, each rounding midpoint included.  Against the oracle's cast
+    of the fp32 quotient, with the oracle on host threads."""
     from concurrent.futures import ThreadPoolExecutor
 
     import torch
@@ -554,7 +557,7 @@ def test_quant_every_fp32_up_to_amax(fmt):
     lay = R.Layout(spec, 1, info["S"], offs)
     qf = R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8
     Q = np.float32(448.0 if fmt == "fp8_e4m3" else 127.0)
-    amax = np.float32(1344.0)
+    amax = np.float32(amax_value)
     scale = np.float32(amax / Q)
     top = int(amax.view(np.uint32))            # every magnitude pattern 0 .. top
     per = N - N // T                           # test values per launch (tile heads hold amax)
