@@ -863,7 +863,8 @@ __device__ __forceinline__ void store4(char* yb, int64_t elem, const float d[4],
 // several times slower.)
 // With F > 1, F workgroups share a work item, each taking one band of
 // about rows/F rows of every tile (more, shorter workgroups); the host uses
-// F = 1 when some tile of the range has fewer than F rows.
+// F = 1 when some tile of the launch (one tile class of the range) has
+// fewer than F rows.
 template <int FMT, int YK, int F>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const QuantWork* __restrict__ work,
                                                            int64_t w0,
