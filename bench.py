@@ -54,8 +54,9 @@ def op_bytes(w, S, n_tiles):
 
 
 def rank_bytes(w, offs, S):
-    """Algorithmic bytes of each operation over one rank's shard [kS, (k+1)S):
-    the tensor elements and quantisation tiles that fall in it."""
+    """Algorithmic bytes of each operation (the step's and those measured
+    beside it) over one rank's shard [kS, (k+1)S): the tensor elements and
+    quantisation tiles that fall in it."""
     m = w.m
     E = np.zeros(m, np.int64)
     Eq = np.zeros(m, np.int64)
@@ -73,7 +74,9 @@ def rank_bytes(w, offs, S):
             tiles += np.bincount((first // S).reshape(-1), minlength=m)
     return [{"pack": 4 * int(E[k]) + 2 * S, "unpack": 4 * int(E[k]), "scale_add": 12 * int(E[k]),
              "sqnorm": 4 * int(E[k]), "block_quant": 5 * int(Eq[k]) + 4 * int(tiles[k]),
-             "zero": 4 * S} for k in range(m)]
+             "zero": 4 * S, "block_dequant": 5 * int(Eq[k]) + 4 * int(tiles[k]),
+             "adamw_step": 28 * int(E[k]), "sgd_step": 20 * int(E[k]),
+             "adamw8_step": 16 * int(Eq[k]) + 16 * int(tiles[k])} for k in range(m)]
 
 
 def extra_bytes(w, S, n_tiles):
@@ -285,16 +288,18 @@ def main():
     codes2 = torch.zeros(total, dtype=torch.uint8, device=dev)
     scales2 = torch.ones(lay.info["num_tiles"], dtype=torch.float32, device=dev)
     var = torch.zeros(total, dtype=torch.float32, device=dev)
-    extra = {
-        "block_dequant": lambda: R.rs_block_dequant(h, codes, qfmt, scales, deq, R.RS_F32, 0, m, sp),
-        "adamw_step": lambda: R.rs_adamw_step(h, deq, acc, mom, var, 1e-4, 0.9, 0.95, 1e-8, 0.1,
-                                              0.5, 0.1, 1.0, None, None, 0, m, sp),
-        "sgd_step": lambda: R.rs_sgd_step(h, deq, acc, mom, 1e-4, 0.9, 0.0, False, 1.0, None, None,
-                                          0, m, sp),
-        "adamw8_step": lambda: R.rs_adamw8_step(h, deq, acc, codes, scales, codes2, scales2, qfmt,
-                                                1e-4, 0.9, 0.95, 1e-8, 0.1, 0.5, 0.1, 1.0, None, 0,
-                                                m, sp),
+    ranged_extra = {
+        "block_dequant": lambda a, b: R.rs_block_dequant(h, codes, qfmt, scales, deq, R.RS_F32, a, b,
+                                                         sp),
+        "adamw_step": lambda a, b: R.rs_adamw_step(h, deq, acc, mom, var, 1e-4, 0.9, 0.95, 1e-8,
+                                                   0.1, 0.5, 0.1, 1.0, None, None, a, b, sp),
+        "sgd_step": lambda a, b: R.rs_sgd_step(h, deq, acc, mom, 1e-4, 0.9, 0.0, False, 1.0, None,
+                                               None, a, b, sp),
+        "adamw8_step": lambda a, b: R.rs_adamw8_step(h, deq, acc, codes, scales, codes2, scales2,
+                                                     qfmt, 1e-4, 0.9, 0.95, 1e-8, 0.1, 0.5, 0.1,
+                                                     1.0, None, a, b, sp),
     }
+    extra = {name: (lambda f=f: f(0, m)) for name, f in ranged_extra.items()}
     xbytes = extra_bytes(w, S, lay.info["num_tiles"])
 
     def step():
@@ -373,7 +378,7 @@ def main():
     if args.per_rank:
         rb = rank_bytes(w, offs, S)
         per_rank = {}
-        for name, f in ranged.items():
+        for name, f in dict(ranged, **ranged_extra).items():
             cycle = lambda f=f: [f(k, k + 1) for k in range(m)]
             med, _, _ = event_ms(cycle, args.samples)
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(m + 1)]

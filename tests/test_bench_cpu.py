@@ -20,9 +20,10 @@ def test_rank_bytes_sum_to_whole_buffer(name):
     else:
         offs, S = pl.offsets, pl.S
     nt = O.num_tiles(w.tensors)
-    whole = Bn.op_bytes(w, S, nt)
+    whole = dict(Bn.op_bytes(w, S, nt), **Bn.extra_bytes(w, S, nt))
     ranks = Bn.rank_bytes(w, offs, S)
     assert len(ranks) == w.m
+    assert set(ranks[0]) == set(whole)
     for op, b in whole.items():
         assert sum(r[op] for r in ranks) == b, op
     E = w.numel
