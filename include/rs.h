@@ -22,9 +22,15 @@
  * at most 2^20 tensors, 2^18 ranks and an alignment of 2^20 elements; S at
  * most 2^41.  Calls outside them return RS_ERR_INVALID_ARG.
  *
- * Launches.  A call enqueues one kernel (the norms: two).  A range with
- * more workgroups than one launch may hold (2^31 lanes) is covered by
- * several launches of the same kernel on `stream`, in order.
+ * Launches.  A call enqueues one kernel (the norms: two; the tile
+ * operations: one per tile class present).  A range with more workgroups
+ * than one launch may hold (2^31 lanes) is covered by several launches of
+ * the same kernel on `stream`, in order.
+ *
+ * Concurrency.  A call reads and writes only its rank range (and the
+ * found_inf flags of those ranks), so calls over disjoint rank ranges may
+ * run at the same time on different streams; rs_ragged_sqnorm calls that
+ * overlap in time need separate workspaces.
  *
  * Errors.  Every call returns an rs_status.  On a non-zero status from
  * argument checking nothing was enqueued, no output was touched, and
