@@ -501,38 +501,92 @@ __global__ __launch_bounds__(kThreads) void sqnorm_partial_kernel(
   }
 }
 
-// Per tensor: fragment sums in rank order, each the fixed-order sum of its
-// chunk partials (fine or coarse chunks, as the partial kernel used);
-// writes partial[k*n + t] for every k of the range.
-__global__ __launch_bounds__(kThreads) void sqnorm_combine_kernel(
+// Per tensor: the squared norm as the sum of its fragment sums in rank
+// order.  Each fragment's chunk partials are summed in a fixed order that
+// depends only on the fragment and the chunk table read, never on the rank
+// range of the call: lanes stride over them with four accumulators, then a
+// butterfly per wave.
+//  * Fine chunks (ranges of few ranks, each fragment holding many chunks):
+//    the whole workgroup sums one fragment at a time, the wave sums added
+//    in wave order.
+//  * Coarse chunks (ranges of many ranks): one wave per fragment, the
+//    workgroup's kCombineWaves waves taking the range's fragments in turn
+//    (sums staged in LDS, kCombineBatch ranks per pass), so a range of many
+//    ranks costs about as much as one of kCombineWaves.
+// Writes partial[k*n + t] for every k of the range.
+constexpr int kCombineWaves = 16;
+constexpr int kCombineBatch = 2048;
+
+// One wave's fixed-order share of a fragment's chunk partials: lane `first`
+// of the lanes that stride by `stride` over [cb, ce), four accumulators, then
+// the sum over the wave (every lane of the wave gets it).
+__device__ __forceinline__ double frag_lane_sum(const double* __restrict__ part, int cb, int ce,
+                                                int first, int stride) {
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  int i = cb + first;
+  for (; i + 3 * stride < ce; i += 4 * stride) {
+    a0 += part[i];
+    a1 += part[i + stride];
+    a2 += part[i + 2 * stride];
+    a3 += part[i + 3 * stride];
+  }
+  for (; i < ce; i += stride) a0 += part[i];
+  double s = (a0 + a1) + (a2 + a3);
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  return s;
+}
+
+__global__ __launch_bounds__(kCombineWaves* kWave) void sqnorm_combine_kernel(
     const TensorDesc* __restrict__ tensors, const FragDesc* __restrict__ frags,
     const double* __restrict__ part, int32_t n, int32_t k0, int32_t k1, double* __restrict__ sq_out,
     double* __restrict__ partial, int fine) {
-  __shared__ double lds[kThreads / kWave];
+  __shared__ double fs[kCombineBatch];
   const int t = blockIdx.x;
   const TensorDesc td = tensors[t];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
   double total = 0.0;
-  for (int k = k0; k < k1; ++k) {
-    const bool has = td.frag_begin >= 0 && k >= td.rank_lo && k < td.rank_hi;
-    double s = 0.0;
-    if (has) {  // uniform across the workgroup
-      const FragDesc fd = frags[td.frag_begin + (k - td.rank_lo)];
-      // lanes stride over the partials; four loads in flight per lane
-      double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-      const int cb = fine ? fd.chunk_begin : fd.cchunk_begin;
-      const int ce = fine ? fd.chunk_end : fd.cchunk_end;
-      int i = cb + threadIdx.x;
-      for (; i + 3 * kThreads < ce; i += 4 * kThreads) {
-        a0 += part[i];
-        a1 += part[i + kThreads];
-        a2 += part[i + 2 * kThreads];
-        a3 += part[i + 3 * kThreads];
+  if (fine) {
+    for (int k = k0; k < k1; ++k) {
+      const bool has = td.frag_begin >= 0 && k >= td.rank_lo && k < td.rank_hi;  // uniform
+      double s = 0.0;
+      if (has) {
+        const FragDesc fd = frags[td.frag_begin + (k - td.rank_lo)];
+        const double w = frag_lane_sum(part, fd.chunk_begin, fd.chunk_end, threadIdx.x,
+                                       kCombineWaves * kWave);
+        if (lane == 0) fs[wave] = w;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          s = fs[0];
+          for (int i = 1; i < kCombineWaves; ++i) s += fs[i];
+          total += s;
+        }
+        __syncthreads();
       }
-      for (; i < ce; i += kThreads) a0 += part[i];
-      s = block_sum((a0 + a1) + (a2 + a3), lds);
-      if (threadIdx.x == 0) total += s;
+      if (partial && threadIdx.x == 0) partial[int64_t(k) * n + t] = s;
     }
-    if (partial && threadIdx.x == 0) partial[int64_t(k) * n + t] = s;
+    if (threadIdx.x == 0) sq_out[t] = total;
+    return;
+  }
+  for (int kb = k0; kb < k1; kb += kCombineBatch) {
+    const int ke = min(k1, kb + kCombineBatch);
+    for (int k = kb + wave; k < ke; k += kCombineWaves) {
+      const bool has = td.frag_begin >= 0 && k >= td.rank_lo && k < td.rank_hi;  // wave-uniform
+      double s = 0.0;
+      if (has) {
+        const FragDesc fd = frags[td.frag_begin + (k - td.rank_lo)];
+        s = frag_lane_sum(part, fd.cchunk_begin, fd.cchunk_end, lane, kWave);
+      }
+      if (lane == 0) {
+        fs[k - kb] = s;
+        if (partial) partial[int64_t(k) * n + t] = s;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int k = kb; k < ke; ++k) total += fs[k - kb];
+    __syncthreads();
   }
   if (threadIdx.x == 0) sq_out[t] = total;
 }
@@ -1558,7 +1612,7 @@ extern "C" rs_status rs_ragged_sqnorm(const rs_layout* L, const float* x, double
     hipLaunchKernelGGL(sqnorm_partial_kernel, chunk_grid(nc), dim3(kThreads), 0, s,
                        table<ChunkDesc>(L, fine ? L->off_chunks : L->off_cchunks), c0, nc, x, part,
                        found_inf);
-  hipLaunchKernelGGL(sqnorm_combine_kernel, dim3(unsigned(L->n)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(sqnorm_combine_kernel, dim3(unsigned(L->n)), dim3(kCombineWaves * kWave), 0, s,
                      table<TensorDesc>(L, L->off_tensors), table<FragDesc>(L, L->off_frags), part,
                      L->n, k0, k1, sq_out, partial, fine);
   return after_launch(fn);
