@@ -1,0 +1,49 @@
+"""The Python example of README.md runs as written, and its results hold:
+the packed buffer holds each tensor's bf16 values at its offset, the norms
+are the squared norms of the unscaled grads, and rank 0's codes decode to
+its grads within the quantisation bound."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import casts as OC
+from harness import to_np
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_readme_example():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    text = open(os.path.join(ROOT, "README.md")).read()
+    blocks = re.findall(r"```python\n(.*?)```", text, flags=re.S)
+    assert blocks, "no python example in README.md"
+    ns = {}
+    exec(compile(blocks[0], "README.md", "exec"), ns)
+    R, lay, w = ns["R"], ns["lay"], ns["w"]
+    buf, params, grad, sq = to_np(ns["buf"]), ns["params"], ns["grad"], to_np(ns["sq"])
+    for t, (spec, l) in enumerate(zip(lay.specs, lay.offsets)):
+        exp = OC.bf16_bits_from_f32(to_np(params[t]).reshape(-1))
+        assert np.array_equal(buf[l:l + exp.size], exp), f"tensor {t}"
+    g = to_np(grad).astype(np.float64)
+    for t, (spec, l) in enumerate(zip(lay.specs, lay.offsets)):
+        e = float(np.sum(g[l:l + spec.rows * spec.cols] ** 2))
+        assert abs(sq[t] - e) <= 1e-9 * e, f"norm {t}"
+    # rank 0's first quantised tile decodes within half a code step of the grads
+    t0 = next(t for t, s in enumerate(lay.specs) if s.q_rows)
+    s0, l0 = lay.specs[t0], lay.offsets[t0]
+    assert l0 < lay.S
+    pos = l0 + (np.arange(s0.q_rows)[:, None] * s0.cols + np.arange(s0.q_cols)[None, :])
+    scale = float(to_np(ns["scales"])[0])
+    dec = OC.e4m3fn_to_f64(to_np(ns["codes"])[pos]) * scale
+    x = g[pos]
+    q = np.abs(x) / scale
+    step = np.maximum(2.0 ** np.floor(np.log2(np.maximum(q, 2.0 ** -6))) / 8, 2.0 ** -9)
+    ulp_q = np.spacing(q.astype(np.float32)).astype(np.float64)   # the fp32 quotient's rounding
+    assert np.all(np.abs(dec - x) <= scale * (step + ulp_q) / 2 * (1 + 1e-6))
+    lay.close()
