@@ -346,3 +346,91 @@ def test_full_adamw8(fx):
     assert np.array_equal(gp[~quantised].view(np.uint32), fx.param_host[~quantised].view(np.uint32))
     assert np.array_equal(to_np(mc)[~quantised], mc0[~quantised])
     del p, g, mc, vc, ms, vs
+
+
+def _tiles_of_rank(fx, k):
+    """Global indices of the quantisation tiles whose elements lie in rank k."""
+    out, base = [], 0
+    for s, l in zip(fx.w.tensors, fx.offsets):
+        if not s.q_rows:
+            continue
+        ntr, ntc = O.tile_counts(s)
+        r0 = np.arange(ntr, dtype=np.int64) * s.q_rows
+        c0 = np.arange(ntc, dtype=np.int64) * s.q_cols
+        first = l + r0[:, None] * s.cols + c0[None, :]
+        out.append(base + np.flatnonzero((first // fx.S).reshape(-1) == k))
+        base += ntr * ntc
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+@pytest.mark.timeout(900)
+def test_full_rank_shares(fx):
+    """One rank's share at full size, in the launch configuration of the
+    bench's per-rank timing (range [k, k+1): fine chunks for the norms,
+    four sub-blocks per wide quantisation tile where the rank has fewer than
+    1024 work items): scale/add with found-inf, norms with partials,
+    quantisation and dequantisation for the first, a middle and the last
+    rank, against the oracle over that rank."""
+    import torch
+    R = fx.R
+    rng = np.random.default_rng(29)
+    fmt = fx.w.qfmt
+    qf = R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8
+    nt = fx.lay.info["num_tiles"]
+    n = len(fx.w.tensors)
+    for k in sorted({0, fx.m // 2, fx.m - 1}):
+        log(f"full rank share {fx.w.name} rank {k}")
+        lo, hi = k * fx.S, (k + 1) * fx.S
+        # scale/add and found-inf
+        y = torch.from_numpy(fx.param_host).cuda()
+        x = torch.from_numpy(fx.grad_host).cuda()
+        fi = torch.zeros(fx.m, dtype=torch.int32, device="cuda")
+        R.rs_group_scale_add(fx.lay.handle, y, x, R.RS_F32, 0.5, -2.0, None, fi, k, k + 1)
+        _sync()
+        ey, ef = O.scale_add(fx.param_host, fx.grad_host, 0.5, -2.0, fx.items, fx.offsets, fx.S,
+                             fx.m, k, k + 1)
+        gy = to_np(y)
+        assert_f32_equal_nan_class(gy[lo:hi], ey[lo:hi], f"rank {k} scale_add")
+        assert np.array_equal(gy[:lo].view(np.uint32), fx.param_host[:lo].view(np.uint32))
+        assert np.array_equal(gy[hi:].view(np.uint32), fx.param_host[hi:].view(np.uint32))
+        assert np.array_equal(to_np(fi).astype(np.uint32), ef)
+        # norms over the rank: per-tensor sums and the partial row of rank k
+        sq = torch.empty(n, dtype=torch.float64, device="cuda")
+        part = torch.zeros(fx.m * n, dtype=torch.float64, device="cuda")
+        R.rs_ragged_sqnorm(fx.lay.handle, x, sq, part, None, fx.lay.ws, k, k + 1)
+        _sync()
+        esq = O.sqnorm(fx.grad_host, fx.items, fx.offsets, fx.S, fx.m, k, k + 1)[0]
+        got = to_np(sq)
+        prow = to_np(part).reshape(fx.m, n)[k]
+        for g_, what in ((got, "sq"), (prow, "partial")):
+            assert np.array_equal(np.isnan(g_), np.isnan(esq)), what
+            assert np.array_equal(np.isinf(g_), np.isinf(esq)), what
+            f = np.isfinite(esq)
+            rel = np.abs(g_[f] - esq[f]) / np.maximum(np.abs(esq[f]), 1e-300)
+            assert np.all(rel <= 1e-5), f"rank {k} {what}: {rel.max()}"
+        # quantisation and dequantisation of the rank's tiles (a sample on big groups)
+        tiles = _tiles_of_rank(fx, k)
+        if tiles.size:
+            if tiles.size > 3000:
+                tiles = np.sort(rng.choice(tiles, size=3000, replace=False))
+            codes = torch.full((fx.total,), 0xAB, dtype=torch.uint8, device="cuda")
+            scales = torch.full((nt,), -1.0, dtype=torch.float32, device="cuda")
+            R.rs_block_quant(fx.lay.handle, x, qf, codes, scales, k, k + 1)
+            _sync()
+            ec, es = O.block_quant(fx.grad_host, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, k, k + 1,
+                                   np.zeros(fx.total, np.uint8), np.zeros(nt, np.float32),
+                                   only_tiles=tiles)
+            gc_, gs = to_np(codes), to_np(scales)
+            assert_bits_equal(gs[tiles], es[tiles], f"rank {k} scales")
+            pos = _tile_positions(fx, list(tiles))
+            assert_bits_equal(gc_[pos], ec[pos], f"rank {k} codes")
+            assert np.all(gc_[:lo] == 0xAB) and np.all(gc_[hi:] == 0xAB)
+            yq = torch.full((fx.total,), float("nan"), dtype=torch.float32, device="cuda")
+            R.rs_block_dequant(fx.lay.handle, codes, qf, scales, yq, R.RS_F32, k, k + 1)
+            _sync()
+            eq = O.block_dequant(gc_, gs, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, k, k + 1,
+                                 np.zeros(fx.total, np.float32), "f32", only_tiles=list(tiles))
+            assert_f32_equal_nan_class(to_np(yq)[pos], eq[pos], f"rank {k} dequant")
+            assert np.all(np.isnan(to_np(yq)[:lo])) and np.all(np.isnan(to_np(yq)[hi:]))
+            del codes, scales, yq
+        del y, x
