@@ -195,6 +195,13 @@ def test_planner_infeasible_cap_and_bad_args():
     with pytest.raises(R.RsError):
         R.rs_plan([W.TensorSpec("a", 0, 4, 0)], 2, 1)
     assert "rs_plan" in R.rs_last_error()
+    # an empty group is rejected, by the planner and by the layout builder
+    with pytest.raises(R.RsError) as e:
+        R.rs_plan([], 2, 1)
+    assert e.value.status == -1
+    with pytest.raises(R.RsError) as e:
+        R.rs_layout_create([], 2, 16, [])
+    assert e.value.status == -1
 
 
 def test_size_limits_keep_int64_arithmetic_exact():
