@@ -318,3 +318,33 @@ def test_hot_calls_reject_before_launch():
     R.rs_layout_destroy(h)
     assert R.rs_status_str(-5) == "rank range out of bounds"
     assert R.rs_status_str(0) == "ok"
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """The binding's ctypes structs have the sizes and field offsets of the
+    structs in include/rs.h, compiled as C by the host compiler."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = [_lib.rs_tensor_spec, _lib.rs_plan_info, _lib.rs_layout_info, _lib.rs_adamw_params,
+               _lib.rs_sgd_params]
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "rs.h"', "int main(void) {"]
+    for st in structs:
+        name = st.__name__
+        lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
+        for f, _ in st._fields_:
+            lines.append(f'  printf("{name}.{f} %zu\\n", offsetof({name}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layouts.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layouts"
+    subprocess.run([cc, "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                       text=True).stdout.splitlines())
+    for st in structs:
+        name = st.__name__
+        assert int(got[name]) == ctypes.sizeof(st), name
+        for f, _ in st._fields_:
+            assert int(got[f"{name}.{f}"]) == getattr(st, f).offset, f"{name}.{f}"
