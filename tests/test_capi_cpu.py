@@ -348,3 +348,19 @@ def test_struct_layouts_match_header(tmp_path):
         assert int(got[name]) == ctypes.sizeof(st), name
         for f, _ in st._fields_:
             assert int(got[f"{name}.{f}"]) == getattr(st, f).offset, f"{name}.{f}"
+
+
+def test_signatures_match_header_parameter_counts():
+    """Each ctypes signature has as many arguments as the declaration in
+    include/rs.h, and returns a value exactly when the declaration does."""
+    txt = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decls = re.findall(r"\b([a-z_]+\s*\**)\s*\b(rs_[a-z_0-9]+)\s*\(([^;{]*?)\)\s*;", txt, flags=re.S)
+    seen = set()
+    for ret, name, params in decls:
+        params = " ".join(params.split())
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        restype, argtypes = _lib.SIGNATURES[name]
+        assert len(argtypes) == n, f"{name}: {len(argtypes)} ctypes arguments, {n} in rs.h"
+        assert (restype is None) == (ret.strip() == "void"), name
+        seen.add(name)
+    assert seen == set(_lib.SIGNATURES)
