@@ -88,6 +88,11 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //   RS_DEQ_LDS       stage a tile's codes in LDS before decoding
 //   RS_ADAM8_F       256-lane sub-blocks per 8-bit Adam work item of wide tiles
 //   RS_ADAM8_BATCH   8-bit Adam slots loaded ahead of their arithmetic
+//   RS_NT_STORE_BELOW  launches of quantisation, dequantisation and the
+//                    unmasked zero that write fewer bytes than this (one
+//                    rank's share, say) use nontemporal stores: a short
+//                    launch then leaves less to write back from L2 at its
+//                    end; long launches store faster without the hint
 #ifndef RS_UNROLL
 #define RS_UNROLL 2
 #endif
@@ -145,9 +150,13 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #ifndef RS_ADAM8_NT
 #define RS_ADAM8_NT 1
 #endif
+#ifndef RS_NT_STORE_BELOW
+#define RS_NT_STORE_BELOW (192ll << 20)
+#endif
 
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // one 128-bit global load / store (global_load_dwordx4 / global_store_dwordx4)
 template <bool NT>
@@ -425,13 +434,14 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(const ChunkDesc* __restr
 
 // Unmasked zero of a contiguous, 16-byte aligned byte range: RS_FILL_BYTES
 // per workgroup.
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(char* __restrict__ base,
                                                              int64_t nbytes) {
   const int64_t lo = int64_t(blockIdx.x) * RS_FILL_BYTES;
   const int64_t n16 = (nbytes - lo < RS_FILL_BYTES ? nbytes - lo : RS_FILL_BYTES) / 16;
   const u32x4 z = {0u, 0u, 0u, 0u};
   char* d = base + lo;
-  for (int64_t v = threadIdx.x; v < n16; v += kThreads) st16<RS_ZERO_NT>(d + v * 16, z);
+  for (int64_t v = threadIdx.x; v < n16; v += kThreads) st16<NT || RS_ZERO_NT>(d + v * 16, z);
 }
 
 // ----------------------------------------------------------------- sqnorm
@@ -723,7 +733,7 @@ __device__ __forceinline__ Tile tile_of(const QuantWork& w, int j) {
 // On the 16-byte path a lane keeps its 4*NS elements in registers between
 // the absmax and the encode pass, so x is read once; the other path reads x
 // twice.  F > 1 finishes each wide tile sooner, for launches with few tiles.
-template <int FMT, int F, int NS>
+template <int FMT, int F, int NS, bool NTS>
 __global__ __launch_bounds__(kThreads* F) void quant_kernel(const QuantWork* __restrict__ work,
                                                             int64_t w0,
                                                             const float* __restrict__ x,
@@ -848,10 +858,14 @@ __global__ __launch_bounds__(kThreads* F) void quant_kernel(const QuantWork* __r
           word = int8_from_rint(r[0]) | (int8_from_rint(r[1]) << 8) | (int8_from_rint(r[2]) << 16) |
                  (int8_from_rint(r[3]) << 24);
         }
-        if (safe)
-          *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
-        else
+        if (safe) {
+          if constexpr (NTS)
+            __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(cbase + sw.off));
+          else
+            *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
+        } else {
           slow |= 1u << i;
+        }
       }
       sw.next();
     }
@@ -894,7 +908,7 @@ __device__ __forceinline__ void decode4(uint32_t word, float d[4]) {
   }
 }
 
-template <int YK>
+template <int YK, bool NTS>
 __device__ __forceinline__ void store4(char* yb, int64_t elem, const float d[4], float scale) {
   if constexpr (YK == 0) {
     u32x4 o;
@@ -902,12 +916,15 @@ __device__ __forceinline__ void store4(char* yb, int64_t elem, const float d[4],
     o.y = u32(d[1] * scale);
     o.z = u32(d[2] * scale);
     o.w = u32(d[3] * scale);
-    st16<false>(yb + elem * 4, o);
+    st16<NTS>(yb + elem * 4, o);
   } else {
-    uint2 o;
+    u32x2 o;
     o.x = bf16_rne(d[0] * scale) | (bf16_rne(d[1] * scale) << 16);
     o.y = bf16_rne(d[2] * scale) | (bf16_rne(d[3] * scale) << 16);
-    *reinterpret_cast<uint2*>(yb + elem * 2) = o;
+    if constexpr (NTS)
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(yb + elem * 2));
+    else
+      *reinterpret_cast<u32x2*>(yb + elem * 2) = o;
   }
 }
 
@@ -919,7 +936,7 @@ __device__ __forceinline__ void store4(char* yb, int64_t elem, const float d[4],
 // about rows/F rows of every tile (more, shorter workgroups); the host uses
 // F = 1 when some tile of the launch (one tile class of the range) has
 // fewer than F rows.
-template <int FMT, int YK, int F>
+template <int FMT, int YK, int F, bool NTS>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const QuantWork* __restrict__ work,
                                                            int64_t w0,
                                                            const uint8_t* __restrict__ codes,
@@ -968,7 +985,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const QuantWork* __re
       const int c = f - r * c4;
       float d[4];
       decode4<FMT>(tl[(r * td.cols) / 4 + c], d);
-      store4<YK>(yb, int64_t(r) * td.ld + c * 4, d, scale);
+      store4<YK, NTS>(yb, int64_t(r) * td.ld + c * 4, d, scale);
     }
     return;
   }
@@ -991,7 +1008,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const QuantWork* __re
       if (lane + i * team < nf) {
         float d[4];
         decode4<FMT>(q[i], d);
-        store4<YK>(yb, off[i], d, scale);
+        store4<YK, NTS>(yb, off[i], d, scale);
       }
     }
   } else {
@@ -1575,8 +1592,12 @@ extern "C" rs_status rs_group_zero(const rs_layout* L, void* y, rs_dtype dt,
     for (int64_t o = 0; o < nbytes; o += per) {
       const int64_t nb = std::min(per, nbytes - o);
       const int64_t g = (nb + RS_FILL_BYTES - 1) / RS_FILL_BYTES;
-      hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s,
-                         lo + o, nb);
+      if (nbytes < RS_NT_STORE_BELOW)
+        hipLaunchKernelGGL(fill_zero_kernel<true>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
+                           s, lo + o, nb);
+      else
+        hipLaunchKernelGGL(fill_zero_kernel<false>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
+                           s, lo + o, nb);
       RS_TRY(after_launch(fn));
     }
     return RS_OK;
@@ -1637,6 +1658,8 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
   // One launch per tile class present in the range.  Narrow tiles: one
   // sub-block, 4 slots per lane.  Wide tiles: 256-lane tiles spread over F
   // sub-blocks, more of them in launches with few work items.
+  // nontemporal code stores for launches that write little (see RS_NT_STORE_BELOW)
+  const bool nts = int64_t(k1 - k0) * L->S < RS_NT_STORE_BELOW;
   for (int c = 0; c < 2; ++c) {
     const int64_t w0 = L->rank_work[c][k0], nw = L->rank_work[c][k1] - w0;
     if (nw == 0) continue;
@@ -1645,22 +1668,26 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
     const int64_t per = max_groups(kThreads * F);
     for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one work item per workgroup
       const dim3 g(static_cast<unsigned>(std::min(per, w0 + nw - w1)));
-#define RS_QUANT_LAUNCH(FM)                                                                    \
-  do {                                                                                         \
-    if (c == 0)                                                                                \
-      hipLaunchKernelGGL((quant_kernel<FM, 1, kNarrowSlots>), g, b, 0, s, wk, w1, x, codes,    \
-                         scales, found_inf, vec_ok);                                           \
-    else if (F == RS_QUANT_F_SMALL)                                                            \
-      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F_SMALL, kWideSlots / RS_QUANT_F_SMALL>),  \
-                         g, b, 0, s, wk, w1, x, codes, scales, found_inf, vec_ok);             \
-    else                                                                                       \
-      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F, kWideSlots / RS_QUANT_F>), g, b, 0, s,  \
-                         wk, w1, x, codes, scales, found_inf, vec_ok);                         \
+#define RS_QUANT_LAUNCH(FM, NT)                                                                 \
+  do {                                                                                          \
+    if (c == 0)                                                                                 \
+      hipLaunchKernelGGL((quant_kernel<FM, 1, kNarrowSlots, NT>), g, b, 0, s, wk, w1, x, codes, \
+                         scales, found_inf, vec_ok);                                            \
+    else if (F == RS_QUANT_F_SMALL)                                                             \
+      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F_SMALL, kWideSlots / RS_QUANT_F_SMALL, NT>), \
+                         g, b, 0, s, wk, w1, x, codes, scales, found_inf, vec_ok);              \
+    else                                                                                        \
+      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F, kWideSlots / RS_QUANT_F, NT>), g, b, 0,  \
+                         s, wk, w1, x, codes, scales, found_inf, vec_ok);                       \
   } while (0)
-      if (fmt == RS_Q_FP8_E4M3)
-        RS_QUANT_LAUNCH(RS_Q_FP8_E4M3);
+      if (fmt == RS_Q_FP8_E4M3 && nts)
+        RS_QUANT_LAUNCH(RS_Q_FP8_E4M3, true);
+      else if (fmt == RS_Q_FP8_E4M3)
+        RS_QUANT_LAUNCH(RS_Q_FP8_E4M3, false);
+      else if (nts)
+        RS_QUANT_LAUNCH(RS_Q_INT8, true);
       else
-        RS_QUANT_LAUNCH(RS_Q_INT8);
+        RS_QUANT_LAUNCH(RS_Q_INT8, false);
 #undef RS_QUANT_LAUNCH
       RS_TRY(after_launch(fn));
     }
@@ -1684,6 +1711,8 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
   if (vec_ok && ca % 16 == 0) vec_ok = 2;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const QuantWork* wk = table<QuantWork>(L, L->off_work);
+  // nontemporal stores for launches that write little (see RS_NT_STORE_BELOW)
+  const bool nts = int64_t(k1 - k0) * L->S * (y_dt == RS_F32 ? 4 : 2) < RS_NT_STORE_BELOW;
   for (int c = 0; c < 2; ++c) {  // one launch per tile class present in the range
     const int64_t w0 = L->rank_work[c][k0], nw = L->rank_work[c][k1] - w0;
     if (nw == 0) continue;
@@ -1697,14 +1726,21 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
     const int64_t per = std::max<int64_t>(1, max_groups(kThreads) / bands);  // items per launch
     for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one workgroup per band of a work item
       const dim3 g(static_cast<unsigned>(std::min(per, w0 + nw - w1) * bands));
-#define RS_DEQ_LAUNCH(FM, YK)                                                                  \
+#define RS_DEQ_LAUNCH2(FM, YK, NT)                                                             \
   do {                                                                                         \
     if (split)                                                                                 \
-      hipLaunchKernelGGL((dequant_kernel<FM, YK, RS_DEQ_SPLIT>), g, b, 0, s, wk, w1, codes,      \
+      hipLaunchKernelGGL((dequant_kernel<FM, YK, RS_DEQ_SPLIT, NT>), g, b, 0, s, wk, w1, codes,  \
                          scales, y, vec_ok);                                                   \
     else                                                                                       \
-      hipLaunchKernelGGL((dequant_kernel<FM, YK, 1>), g, b, 0, s, wk, w1, codes, scales, y,      \
+      hipLaunchKernelGGL((dequant_kernel<FM, YK, 1, NT>), g, b, 0, s, wk, w1, codes, scales, y,  \
                          vec_ok);                                                              \
+  } while (0)
+#define RS_DEQ_LAUNCH(FM, YK)          \
+  do {                                 \
+    if (nts)                           \
+      RS_DEQ_LAUNCH2(FM, YK, true);    \
+    else                               \
+      RS_DEQ_LAUNCH2(FM, YK, false);   \
   } while (0)
       if (fmt == RS_Q_FP8_E4M3 && y_dt == RS_F32)
         RS_DEQ_LAUNCH(RS_Q_FP8_E4M3, 0);
@@ -1715,6 +1751,7 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
       else
         RS_DEQ_LAUNCH(RS_Q_INT8, 1);
 #undef RS_DEQ_LAUNCH
+#undef RS_DEQ_LAUNCH2
       RS_TRY(after_launch(fn));
     }
   }
