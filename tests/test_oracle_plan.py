@@ -266,3 +266,37 @@ def test_coarser_granule_never_shrinks_S():
         m = int(rng.integers(1, 6))
         S = [P.plan(P.items_from_specs(W.regranulated(specs, r)), m, 1).S for r in (1, 2, 4)]
         assert S[0] <= S[1] <= S[2], (specs, m, S)
+
+
+@pytest.mark.parametrize("name,A", [("llama3_8b_layer", 16), ("llama3_8b_layer", 1),
+                                    ("llama70b_layer", 16)])
+def test_s_star_closed_form_of_llama_layers(name, A):
+    """S* of the Llama layer groups from a hand argument.  Every tensor at
+    least twice as long as a candidate S holds two shard boundaries S apart,
+    so S must be a multiple of its granule.  In the 8B layer, Wgate, Wup
+    and Wdown (58,720,256 elements each, granules 128*4096 and 128*14336)
+    are that long for every S below 29,360,128 = 8 * lcm(524288, 1835008),
+    and 7 * 3,670,016 lies below ceil(E/8); in the 70B layer
+    the same holds at 7,340,032 = lcm(128*8192, 128*28672).  So S* is the
+    smallest lcm multiple at or above the lower bound, provided a layout
+    exists there, which the oracle's plan shows."""
+    w = W.WORKLOADS[name]
+    items = P.items_from_specs(w.tensors)
+    E = sum(it.numel for it in items)
+    lb = -(-E // w.m)
+    long_ = [it for it in items if it.granule > 1]
+    L = 1
+    for it in long_:
+        L = math.lcm(L, it.granule)
+    cand = -(-lb // L) * L
+    # every S in [lb, cand) leaves the long tensors longer than 2S
+    big = [it for it in long_ if 2 * (cand - 1) < it.numel]
+    L_big = 1
+    for it in big:
+        L_big = math.lcm(L_big, it.granule)
+    assert L_big == L and cand % A == 0
+    expect = {"llama3_8b_layer": 29_360_128, "llama70b_layer": 7_340_032}[name]
+    assert cand == expect
+    p = P.plan(items, w.m, A)
+    assert p.S == cand
+    _independent_check(items, p.offsets, p.S, w.m, A)
