@@ -11,7 +11,7 @@ needs the built library and a GPU.
 from __future__ import annotations
 
 import ctypes
-from ctypes import POINTER, byref, c_double, c_float, c_int32, c_int64, c_void_p
+from ctypes import byref, c_int32, c_int64, c_void_p
 from typing import Dict, List, Optional, Sequence, Tuple
 
 from ._lib import lib, RsError, check  # noqa: F401

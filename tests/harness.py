@@ -2,16 +2,13 @@
 C-ABI on seeded inputs and run the oracle on the same bytes."""
 from __future__ import annotations
 
-import os
 import sys
 from dataclasses import dataclass
-from typing import List, Optional
+from typing import List
 
 import numpy as np
 
 import workloads as W
-from oracle import casts as OC
-from oracle import ops as O
 from oracle import plan as P
 
 GUARD = 64  # canary elements before and after every device output

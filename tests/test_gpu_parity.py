@@ -16,10 +16,9 @@ import pytest
 import workloads as W
 from oracle import casts as OC
 from oracle import ops as O
-from oracle import plan as P
 
-from harness import (GUARD, SMALL, Case, assert_bits_equal, assert_f32_equal_nan_class, case,
-                     check_guards, from_np, guarded, log, to_np)
+from harness import (SMALL, assert_bits_equal, assert_f32_equal_nan_class, case, check_guards,
+                     from_np, guarded, log, to_np)
 
 pytestmark = pytest.mark.gpu
 

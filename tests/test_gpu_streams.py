@@ -4,7 +4,6 @@ ranks' work would on their own devices).  Each operation is issued as two
 half-range calls on two default-priority streams without waiting between
 them, and the results must equal one whole-range call bit for bit.  The
 norms use one workspace per stream and compare the per-rank partials."""
-import numpy as np
 import pytest
 
 from harness import case, from_np, log, to_np

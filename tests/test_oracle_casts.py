@@ -9,7 +9,6 @@ import json
 import os
 
 import numpy as np
-import pytest
 import torch
 
 from oracle import casts as C
