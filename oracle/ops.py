@@ -122,9 +122,10 @@ def scale_add(y: np.ndarray, x: np.ndarray, alpha: float, beta: float,
             continue
         xs = x[lo:hi]
         xs = casts.bf16_to_f32(xs) if xs.dtype == np.uint16 else xs.astype(F32)
-        u = a * out[lo:hi]            # fp32 products and sum, each rounded
-        v = b * xs
-        w = (u + v).astype(F32)
+        with np.errstate(invalid="ignore", over="ignore"):   # Inf/NaN inputs are expected
+            u = a * out[lo:hi]            # fp32 products and sum, each rounded
+            v = b * xs
+            w = (u + v).astype(F32)
         out[lo:hi] = w
         if not np.all(np.isfinite(w)):
             found[k] = 1
