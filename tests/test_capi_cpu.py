@@ -364,3 +364,20 @@ def test_signatures_match_header_parameter_counts():
         assert (restype is None) == (ret.strip() == "void"), name
         seen.add(name)
     assert seen == set(_lib.SIGNATURES)
+
+
+def test_layout_rejects_a_tile_across_a_shard_boundary():
+    """Row granules with 4-row tiles: on 4 ranks S = 8 cuts the first 4x4
+    tile of an 8x4 tensor in half, so the layout is refused (such a tile
+    could not be quantised without communication); on 2 ranks the cut falls
+    between tiles and the layout is accepted."""
+    specs = [W.TensorSpec("a", 8, 4, 1, 4, 4)]
+    offs, info = R.rs_plan(specs, 4, 1)
+    assert info["S"] == 8
+    with pytest.raises(R.RsError) as e:
+        R.rs_layout_create(specs, 4, info["S"], offs)
+    assert e.value.status == -1 and "crosses a shard boundary" in R.rs_last_error()
+    offs, info = R.rs_plan(specs, 2, 1)
+    h = R.rs_layout_create(specs, 2, info["S"], offs)
+    assert R.rs_layout_get_info(h)["num_tiles"] == 2
+    R.rs_layout_destroy(h)
