@@ -78,7 +78,10 @@ enum { RS_Q_FP8_E4M3 = 0, RS_Q_INT8 = 1 };
  *   otherwise the granule is gran_rows*cols elements.
  * q_rows, q_cols: block-quantisation tile (veScale-FSDP, section 6.3); 0,0
  *   means the tensor is not quantised.  q_rows*q_cols <= 16384 and
- *   q_rows*cols < 2^31. */
+ *   q_rows*cols < 2^31.  The planner places granules, not tiles: make
+ *   gran_rows a multiple of q_rows (usually equal) so that no tile can
+ *   straddle a shard boundary; rs_layout_create refuses a layout where one
+ *   does. */
 typedef struct {
   int64_t rows;
   int64_t cols;
