@@ -342,3 +342,16 @@ def test_quant_found_inf():
     x[v + 2] = np.nan
     f = O.quant_found_inf(x, w.tensors, p.offsets, p.S, w.m, 0, w.m)
     assert f.tolist() == [1 if k == (l + 7) // p.S else 0 for k in range(w.m)]
+
+
+def test_quant_tiles_match_hand_worked_values():
+    """tests/golden/quant_tiles.json: tiles quantised by hand from the OCP
+    E4M3FN and INT8 definitions (scale, every code, ties to even, subnormals,
+    a zero tile)."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quant_tiles.json")))
+    for t in g["tiles"]:
+        scale, codes = O.quant_tile(np.array(t["x"], np.float32), t["fmt"])
+        assert float(scale) == t["scale"], t["why"]
+        assert [int(c) for c in codes.reshape(-1)] == [int(c, 16) for c in t["codes"]], t["why"]
