@@ -1,10 +1,13 @@
 // Test-only program: the C-ABI used from C++ with no Python in the process.
 // Plans a small group, builds and uploads its layout, packs fp32 tensors into
 // a bf16 buffer, unpacks them back to fp32, takes the per-tensor squared
-// norms of the fp32 tensors packed into an fp32 buffer, and checks all of it
-// on the host.  Prints "capi demo ok" and exits 0 on success.
+// norms of the fp32 tensors packed into an fp32 buffer, scales and adds a
+// second buffer into it with found-inf, and quantises it to FP8 and back
+// (every decoded value within half a code step of its input), checking all
+// of it on the host.  Prints "capi demo ok" and exits 0 on success.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -114,6 +117,66 @@ int main() {
     for (float v : host[t]) e += double(v) * double(v);
     if (std::fabs(gsq[t] - e) > 1e-9 * e) ++bad;
   }
+  // y <- 0.5*y + 2*x over every fragment: fl(fl(0.5*y) + fl(2*x)), padding untouched
+  std::vector<float> y(size_t(info.total)), x(size_t(info.total));
+  HIP_CHECK(hipMemcpy(y.data(), buf32, y.size() * 4, hipMemcpyDeviceToHost));
+  for (size_t i = 0; i < x.size(); ++i) x[i] = float(int(i % 17) - 8) * 0.125f;
+  void* xdev = nullptr;
+  uint32_t* found = nullptr;
+  HIP_CHECK(hipMalloc(&xdev, x.size() * 4));
+  HIP_CHECK(hipMalloc(&found, size_t(m) * 4));
+  HIP_CHECK(hipMemcpy(xdev, x.data(), x.size() * 4, hipMemcpyHostToDevice));
+  HIP_CHECK(hipMemset(found, 0, size_t(m) * 4));
+  RS_CHECK(rs_group_scale_add(L, static_cast<float*>(buf32), xdev, RS_F32, 0.5f, 2.0f, nullptr,
+                              found, 0, m, nullptr));
+  std::vector<float> y2(y.size());
+  HIP_CHECK(hipDeviceSynchronize());
+  HIP_CHECK(hipMemcpy(y2.data(), buf32, y2.size() * 4, hipMemcpyDeviceToHost));
+  std::vector<char> in_tensor(y.size(), 0);
+  for (int t = 0; t < n; ++t)
+    for (int64_t i = 0; i < specs[t].rows * specs[t].cols; ++i) in_tensor[size_t(offs[t] + i)] = 1;
+  for (size_t i = 0; i < y.size(); ++i) {
+    const volatile float u = 0.5f * y[i];  // volatile: two separate fp32 roundings, no FMA
+    const volatile float v = 2.0f * x[i];
+    const float e = in_tensor[i] ? float(u + v) : y[i];
+    if (std::memcmp(&e, &y2[i], 4) != 0) ++bad;
+  }
+  std::vector<uint32_t> fh(static_cast<size_t>(m));
+  HIP_CHECK(hipMemcpy(fh.data(), found, fh.size() * 4, hipMemcpyDeviceToHost));
+  for (uint32_t f : fh) bad += f != 0u;  // every value is finite
+
+  // FP8 quantisation and back: each decoded value within half a code step
+  uint8_t* codes = nullptr;
+  float* scales = nullptr;
+  float* deq = nullptr;
+  HIP_CHECK(hipMalloc(&codes, size_t(info.total)));
+  HIP_CHECK(hipMalloc(&scales, size_t(info.num_tiles) * 4));
+  HIP_CHECK(hipMalloc(&deq, size_t(info.total) * 4));
+  RS_CHECK(rs_block_quant(L, static_cast<const float*>(buf32), RS_Q_FP8_E4M3, codes, scales,
+                          nullptr, 0, m, nullptr));
+  RS_CHECK(rs_block_dequant(L, codes, RS_Q_FP8_E4M3, scales, deq, RS_F32, 0, m, nullptr));
+  std::vector<float> d(y.size()), sc(size_t(info.num_tiles));
+  HIP_CHECK(hipDeviceSynchronize());
+  HIP_CHECK(hipMemcpy(d.data(), deq, d.size() * 4, hipMemcpyDeviceToHost));
+  HIP_CHECK(hipMemcpy(sc.data(), scales, sc.size() * 4, hipMemcpyDeviceToHost));
+  int64_t tile = 0;
+  for (int t = 0; t < n; ++t) {
+    const rs_tensor_spec& s = specs[t];
+    if (s.q_rows == 0) continue;
+    for (int64_t r0 = 0; r0 < s.rows; r0 += s.q_rows)
+      for (int64_t c0 = 0; c0 < s.cols; c0 += s.q_cols, ++tile)
+        for (int64_t r = r0; r < std::min(s.rows, r0 + s.q_rows); ++r)
+          for (int64_t c = c0; c < std::min(s.cols, c0 + s.q_cols); ++c) {
+            const size_t p = size_t(offs[t] + r * s.cols + c);
+            const double q = std::fabs(double(y2[p])) / sc[size_t(tile)];
+            // E4M3 code spacing at q: 2^(floor(log2 q) - 3) for q >= 2^-6, else 2^-9
+            const double step = q < 0x1p-6 ? 0x1p-9 : std::ldexp(1.0, std::ilogb(q) - 3);
+            const double tol = sc[size_t(tile)] * (step / 2 + std::ldexp(1.0, std::ilogb(q) - 23)) + 1e-30;
+            if (std::fabs(double(d[p]) - double(y2[p])) > tol) ++bad;
+          }
+  }
+  if (tile != info.num_tiles) ++bad;
+
   // an invalid call reports its error and launches nothing
   if (rs_pack(L, dsrc, RS_F32, buf16, RS_BF16, 2, 1, nullptr) != RS_ERR_RANGE) ++bad;
 
@@ -126,6 +189,11 @@ int main() {
   (void)hipFree(buf16);
   (void)hipFree(buf32);
   (void)hipFree(sq);
+  (void)hipFree(xdev);
+  (void)hipFree(found);
+  (void)hipFree(codes);
+  (void)hipFree(scales);
+  (void)hipFree(deq);
   (void)hipFree(ws);
   (void)hipFree(table);
   rs_layout_destroy(L);
