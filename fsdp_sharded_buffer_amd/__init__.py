@@ -18,6 +18,7 @@ from ._lib import lib, RsError, check  # noqa: F401
 from ._lib import rs_tensor_spec, rs_plan_info, rs_layout_info, rs_adamw_params, rs_sgd_params
 
 RS_F32, RS_BF16, RS_U8 = 0, 1, 2
+RS_ERR_NOMEM = -8
 RS_Q_FP8_E4M3, RS_Q_INT8 = 0, 1
 RS_ORDER_GIVEN, RS_ORDER_BLOCK, RS_ORDER_SHAPE, RS_ORDER_BEST = 0, 1, 2, 3
 ORDERS = {"given": RS_ORDER_GIVEN, "block": RS_ORDER_BLOCK, "shape": RS_ORDER_SHAPE,
@@ -26,7 +27,8 @@ ORDERS = {"given": RS_ORDER_GIVEN, "block": RS_ORDER_BLOCK, "shape": RS_ORDER_SH
 __all__ = [
     "RS_F32", "RS_BF16", "RS_U8", "RS_Q_FP8_E4M3", "RS_Q_INT8", "RsError",
     "RS_ORDER_GIVEN", "RS_ORDER_BLOCK", "RS_ORDER_SHAPE", "RS_ORDER_BEST", "ORDERS",
-    "rs_plan", "rs_plan_order", "rs_plan_ordered", "rs_layout_create", "rs_layout_get_info", "rs_layout_upload",
+    "rs_plan", "rs_plan_order", "rs_plan_ordered", "rs_layout_create", "rs_layout_get_info",
+    "rs_layout_device_bytes", "rs_workspace_bytes", "rs_layout_upload",
     "rs_layout_destroy", "rs_pack", "rs_unpack", "rs_group_scale_add", "rs_group_zero",
     "rs_ragged_sqnorm", "rs_block_quant", "rs_block_dequant", "rs_adamw_step", "rs_adamw8_step",
     "rs_sgd_step",
@@ -109,6 +111,14 @@ def rs_layout_get_info(layout) -> Dict:
     info = rs_layout_info()
     check(lib().rs_layout_get_info(layout, byref(info)))
     return {f: getattr(info, f) for f, _ in rs_layout_info._fields_}
+
+
+def rs_layout_device_bytes(layout) -> int:
+    return int(lib().rs_layout_device_bytes(layout))
+
+
+def rs_workspace_bytes(layout) -> int:
+    return int(lib().rs_workspace_bytes(layout))
 
 
 def rs_layout_upload(layout, dev_table, stream=None) -> None:

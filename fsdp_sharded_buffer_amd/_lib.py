@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_char_p, c_double, c_float, c_int32, c_int64, c_void_p
+from ctypes import POINTER, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librs.so")
@@ -57,6 +57,8 @@ SIGNATURES = {
     "rs_layout_get_info": (c_int32, [c_void_p, POINTER(rs_layout_info)]),
     "rs_layout_upload": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "rs_layout_destroy": (None, [c_void_p]),
+    "rs_layout_device_bytes": (c_size_t, [c_void_p]),
+    "rs_workspace_bytes": (c_size_t, [c_void_p]),
     "rs_pack": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32,
                           c_void_p]),
     "rs_unpack": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32,

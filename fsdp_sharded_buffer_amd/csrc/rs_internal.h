@@ -140,4 +140,8 @@ namespace rs {
 // Records a message for rs_last_error() and returns `st`.
 rs_status fail(rs_status st, const std::string& msg);
 void clear_error();
+// Maps the exception in flight to a status for a C entry point (called from
+// its catch block): std::bad_alloc and thread start failures give
+// RS_ERR_NOMEM, anything else RS_ERR_INVALID_ARG; records the message.
+rs_status on_exception(const char* fn) noexcept;
 }  // namespace rs

@@ -16,6 +16,8 @@
 #include <cstdint>
 #include <cstdlib>
 #include <string>
+#include <tuple>
+#include <utility>
 
 #include "rs_internal.h"
 
@@ -403,9 +405,8 @@ __device__ __forceinline__ void scale_add_run(float* yp, const char* xp, int n, 
 
 template <int XK>
 __global__ __launch_bounds__(kThreads) void scale_add_kernel(
-    const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* __restrict__ y,
-    const void* __restrict__ x, float alpha, float beta, const uint8_t* __restrict__ mask,
-    uint32_t* __restrict__ found_inf) {
+    const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* y, const void* x,
+    float alpha, float beta, const uint8_t* __restrict__ mask, uint32_t* __restrict__ found_inf) {
   for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
     const ChunkDesc c = chunks[c0 + i];
     if (c.tensor < 0) continue;
@@ -476,7 +477,9 @@ __device__ __forceinline__ void sq4(u32x4 r, double& acc, bool& bad) {
   bad |= !(finite_bits(r.x) && finite_bits(r.y) && finite_bits(r.z) && finite_bits(r.w));
 }
 
-// Per (coarse) chunk: fp64 sum of squares into part[chunk].
+// Per (fine or coarse) chunk ci of the range [c0, c0 + nc): fp64 sum of
+// squares into part[ci - c0], so the scratch holds one partial per chunk of
+// the range.
 __global__ __launch_bounds__(kThreads) void sqnorm_partial_kernel(
     const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, const float* __restrict__ x,
     double* __restrict__ part, uint32_t* __restrict__ found_inf) {
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void sqnorm_partial_kernel(
     }
     flag_rank(bad, found_inf, c.rank);
     const double s = block_sum(acc, lds);
-    if (threadIdx.x == 0) part[ci] = s;
+    if (threadIdx.x == 0) part[ii] = s;
   }
 }
 
@@ -547,12 +550,29 @@ __device__ __forceinline__ double frag_lane_sum(const double* __restrict__ part,
   return s;
 }
 
+// One workgroup per tensor present in the range (tensors [t_lo, t_hi) in
+// buffer order), plus, when some tensor is absent, one last workgroup that
+// writes the zeros of the absent tensors' sq and partial entries.  part[i]
+// is the partial of chunk c0 + i of the table read.
 __global__ __launch_bounds__(kCombineWaves* kWave) void sqnorm_combine_kernel(
     const TensorDesc* __restrict__ tensors, const FragDesc* __restrict__ frags,
-    const double* __restrict__ part, int32_t n, int32_t k0, int32_t k1, double* __restrict__ sq_out,
-    double* __restrict__ partial, int fine) {
+    const double* __restrict__ part, int64_t c0, int32_t n, int32_t k0, int32_t k1, int32_t t_lo,
+    int32_t t_hi, double* __restrict__ sq_out, double* __restrict__ partial, int fine) {
   __shared__ double fs[kCombineBatch];
-  const int t = blockIdx.x;
+  if (int(blockIdx.x) == t_hi - t_lo) {
+    for (int t = threadIdx.x; t < n; t += blockDim.x)
+      if (t < t_lo || t >= t_hi) sq_out[t] = 0.0;
+    if (partial) {
+      const int absent = n - (t_hi - t_lo);
+      for (int64_t i = threadIdx.x; i < int64_t(k1 - k0) * absent; i += blockDim.x) {
+        const int64_t k = k0 + i / absent;
+        const int j = int(i % absent);
+        partial[k * n + (j < t_lo ? j : j + (t_hi - t_lo))] = 0.0;
+      }
+    }
+    return;
+  }
+  const int t = t_lo + int(blockIdx.x);
   const TensorDesc td = tensors[t];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -563,8 +583,8 @@ __global__ __launch_bounds__(kCombineWaves* kWave) void sqnorm_combine_kernel(
       double s = 0.0;
       if (has) {
         const FragDesc fd = frags[td.frag_begin + (k - td.rank_lo)];
-        const double w = frag_lane_sum(part, fd.chunk_begin, fd.chunk_end, threadIdx.x,
-                                       kCombineWaves * kWave);
+        const double w = frag_lane_sum(part, int(fd.chunk_begin - c0), int(fd.chunk_end - c0),
+                                       threadIdx.x, kCombineWaves * kWave);
         if (lane == 0) fs[wave] = w;
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -586,7 +606,7 @@ __global__ __launch_bounds__(kCombineWaves* kWave) void sqnorm_combine_kernel(
       double s = 0.0;
       if (has) {
         const FragDesc fd = frags[td.frag_begin + (k - td.rank_lo)];
-        s = frag_lane_sum(part, fd.cchunk_begin, fd.cchunk_end, lane, kWave);
+        s = frag_lane_sum(part, int(fd.cchunk_begin - c0), int(fd.cchunk_end - c0), lane, kWave);
       }
       if (lane == 0) {
         fs[k - kb] = s;
@@ -1441,12 +1461,32 @@ __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
 
 // ------------------------------------------------------------- host glue
 
+// The status of each launch is its own hipLaunchKernel return code, never
+// hipGetLastError(), which could report an error left by unrelated earlier
+// work.  launch() keeps the first failure of the current call; check_common
+// clears it when a call starts and after_launch reports and clears it.
+thread_local hipError_t t_launch_err = hipSuccess;
+
+template <typename... P, typename... A>
+void launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, A&&... a) {
+  std::tuple<P...> args(std::forward<A>(a)...);
+  const hipError_t e = std::apply(
+      [&](auto&... v) {
+        void* ptrs[] = {static_cast<void*>(&v)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, s);
+      },
+      args);
+  if (e != hipSuccess && t_launch_err == hipSuccess) t_launch_err = e;
+}
+
+
 template <typename T>
 const T* table(const rs_layout* L, size_t off) {
   return reinterpret_cast<const T*>(static_cast<const char*>(L->dev) + off);
 }
 
 rs_status check_common(const rs_layout* L, int32_t k0, int32_t k1, const char* fn) {
+  t_launch_err = hipSuccess;
   if (!L) return fail(RS_ERR_INVALID_ARG, std::string(fn) + ": null layout");
   if (!L->dev) return fail(RS_ERR_STATE, std::string(fn) + ": layout not uploaded");
   if (k0 < 0 || k1 > L->m || k0 >= k1)
@@ -1482,7 +1522,8 @@ dim3 chunk_grid(int64_t n) {
 }
 
 rs_status after_launch(const char* fn) {
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = t_launch_err;
+  t_launch_err = hipSuccess;
   if (e != hipSuccess) return fail(RS_ERR_HIP, std::string(fn) + ": " + hipGetErrorString(e));
   clear_error();
   return RS_OK;
@@ -1502,7 +1543,7 @@ bool float_kind(rs_dtype d) { return d == RS_F32 || d == RS_BF16; }
 using namespace rs;
 
 extern "C" rs_status rs_pack(const rs_layout* L, const void* const* src, rs_dtype src_dt, void* buf,
-                             rs_dtype buf_dt, int32_t k0, int32_t k1, void* stream) {
+                             rs_dtype buf_dt, int32_t k0, int32_t k1, void* stream) try {
   const char* fn = "rs_pack";
   RS_TRY(check_common(L, k0, k1, fn));
   if (!float_kind(src_dt) || !float_kind(buf_dt))
@@ -1515,19 +1556,21 @@ extern "C" rs_status rs_pack(const rs_layout* L, const void* const* src, rs_dtyp
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
   const dim3 g = chunk_grid(nc), b(kThreads);
   if (src_dt == RS_F32 && buf_dt == RS_BF16)
-    hipLaunchKernelGGL((pack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, src, buf);
+    launch((pack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, src, buf);
   else if (src_dt == RS_F32 && buf_dt == RS_F32)
-    hipLaunchKernelGGL((pack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, src, buf);
+    launch((pack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, src, buf);
   else if (src_dt == RS_BF16 && buf_dt == RS_BF16)
-    hipLaunchKernelGGL((pack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, src, buf);
+    launch((pack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, src, buf);
   else
-    hipLaunchKernelGGL((pack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, src, buf);
+    launch((pack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, src, buf);
   return after_launch(fn);
+} catch (...) {
+  return rs::on_exception("rs_pack");
 }
 
 extern "C" rs_status rs_unpack(const rs_layout* L, const void* buf, rs_dtype buf_dt,
                                void* const* dst, rs_dtype dst_dt, int32_t k0, int32_t k1,
-                               void* stream) {
+                               void* stream) try {
   const char* fn = "rs_unpack";
   RS_TRY(check_common(L, k0, k1, fn));
   if (!float_kind(dst_dt) || !float_kind(buf_dt))
@@ -1540,20 +1583,22 @@ extern "C" rs_status rs_unpack(const rs_layout* L, const void* buf, rs_dtype buf
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
   const dim3 g = chunk_grid(nc), b(kThreads);
   if (buf_dt == RS_BF16 && dst_dt == RS_BF16)
-    hipLaunchKernelGGL((unpack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, buf, dst);
+    launch((unpack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, buf, dst);
   else if (buf_dt == RS_BF16 && dst_dt == RS_F32)
-    hipLaunchKernelGGL((unpack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, buf, dst);
+    launch((unpack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, buf, dst);
   else if (buf_dt == RS_F32 && dst_dt == RS_F32)
-    hipLaunchKernelGGL((unpack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, buf, dst);
+    launch((unpack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, buf, dst);
   else
-    hipLaunchKernelGGL((unpack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, buf, dst);
+    launch((unpack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, buf, dst);
   return after_launch(fn);
+} catch (...) {
+  return rs::on_exception("rs_unpack");
 }
 
 extern "C" rs_status rs_group_scale_add(const rs_layout* L, float* y, const void* x,
                                         rs_dtype x_dt, float alpha, float beta,
                                         const uint8_t* tensor_mask, uint32_t* found_inf,
-                                        int32_t k0, int32_t k1, void* stream) {
+                                        int32_t k0, int32_t k1, void* stream) try {
   const char* fn = "rs_group_scale_add";
   RS_TRY(check_common(L, k0, k1, fn));
   if (!float_kind(x_dt)) return fail(RS_ERR_DTYPE, "rs_group_scale_add: x must be RS_F32 or RS_BF16");
@@ -1566,17 +1611,19 @@ extern "C" rs_status rs_group_scale_add(const rs_layout* L, float* y, const void
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
   const dim3 g = chunk_grid(nc), b(kThreads);
   if (x_dt == RS_F32)
-    hipLaunchKernelGGL((scale_add_kernel<0>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
+    launch((scale_add_kernel<0>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
                        found_inf);
   else
-    hipLaunchKernelGGL((scale_add_kernel<1>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
+    launch((scale_add_kernel<1>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
                        found_inf);
   return after_launch(fn);
+} catch (...) {
+  return rs::on_exception("rs_group_scale_add");
 }
 
 extern "C" rs_status rs_group_zero(const rs_layout* L, void* y, rs_dtype dt,
                                    const uint8_t* tensor_mask, int32_t k0, int32_t k1,
-                                   void* stream) {
+                                   void* stream) try {
   const char* fn = "rs_group_zero";
   RS_TRY(check_common(L, k0, k1, fn));
   if (!float_kind(dt)) return fail(RS_ERR_DTYPE, "rs_group_zero: dt must be RS_F32 or RS_BF16");
@@ -1593,10 +1640,10 @@ extern "C" rs_status rs_group_zero(const rs_layout* L, void* y, rs_dtype dt,
       const int64_t nb = std::min(per, nbytes - o);
       const int64_t g = (nb + RS_FILL_BYTES - 1) / RS_FILL_BYTES;
       if (nbytes < RS_NT_STORE_BELOW)
-        hipLaunchKernelGGL(fill_zero_kernel<true>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
+        launch(fill_zero_kernel<true>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
                            s, lo + o, nb);
       else
-        hipLaunchKernelGGL(fill_zero_kernel<false>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
+        launch(fill_zero_kernel<false>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
                            s, lo + o, nb);
       RS_TRY(after_launch(fn));
     }
@@ -1607,15 +1654,53 @@ extern "C" rs_status rs_group_zero(const rs_layout* L, void* y, rs_dtype dt,
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_cchunks);
   const dim3 g = chunk_grid(nc), b(kThreads);
   if (dt == RS_F32)
-    hipLaunchKernelGGL((zero_kernel<0>), g, b, 0, s, ch, c0, nc, y, tensor_mask);
+    launch((zero_kernel<0>), g, b, 0, s, ch, c0, nc, y, tensor_mask);
   else
-    hipLaunchKernelGGL((zero_kernel<1>), g, b, 0, s, ch, c0, nc, y, tensor_mask);
+    launch((zero_kernel<1>), g, b, 0, s, ch, c0, nc, y, tensor_mask);
+  return after_launch(fn);
+} catch (...) {
+  return rs::on_exception("rs_group_zero");
+}
+
+namespace rs {
+namespace {
+
+// The norms of ranks [k0, k1) with chunk partials in `part` (at least
+// sqnorm_partials() doubles): the partial kernel over the range's chunks,
+// then the combine over the tensors present in the range.
+int64_t sqnorm_partials(const rs_layout* L, int32_t k0, int32_t k1, int* fine) {
+  // coarse chunks, unless the range has too few of them to fill the chip
+  *fine = (L->rank_cchunk[k1] - L->rank_cchunk[k0]) < RS_SQNORM_FINE_BELOW ? 1 : 0;
+  const std::vector<int64_t>& rb = *fine ? L->rank_chunk : L->rank_cchunk;
+  return rb[k1] - rb[k0];
+}
+
+rs_status sqnorm_launch(const rs_layout* L, const float* x, double* sq_out, double* partial,
+                        uint32_t* found_inf, double* part, int32_t k0, int32_t k1,
+                        hipStream_t s, const char* fn) {
+  int fine = 0;
+  const int64_t nc = sqnorm_partials(L, k0, k1, &fine);
+  const int64_t c0 = (fine ? L->rank_chunk : L->rank_cchunk)[k0];
+  if (nc > 0)
+    launch(sqnorm_partial_kernel, chunk_grid(nc), dim3(kThreads), 0, s,
+           table<ChunkDesc>(L, fine ? L->off_chunks : L->off_cchunks), c0, nc, x, part, found_inf);
+  // tensors with a fragment in the range: a contiguous run in buffer order
+  const int64_t f0 = L->rank_frag[k0], f1 = L->rank_frag[k1];
+  const int32_t t_lo = f1 > f0 ? L->frags[f0].tensor : 0;
+  const int32_t t_hi = f1 > f0 ? L->frags[f1 - 1].tensor + 1 : 0;
+  const unsigned groups = unsigned(t_hi - t_lo) + (t_hi - t_lo < L->n ? 1u : 0u);
+  launch(sqnorm_combine_kernel, dim3(groups), dim3(kCombineWaves * kWave), 0, s,
+         table<TensorDesc>(L, L->off_tensors), table<FragDesc>(L, L->off_frags), part, c0, L->n,
+         k0, k1, t_lo, t_hi, sq_out, partial, fine);
   return after_launch(fn);
 }
 
+}  // namespace
+}  // namespace rs
+
 extern "C" rs_status rs_ragged_sqnorm(const rs_layout* L, const float* x, double* sq_out,
                                       double* partial, uint32_t* found_inf, void* ws, int32_t k0,
-                                      int32_t k1, void* stream) {
+                                      int32_t k1, void* stream) try {
   const char* fn = "rs_ragged_sqnorm";
   RS_TRY(check_common(L, k0, k1, fn));
   RS_TRY(check_ptr(x, 4, fn, "x"));
@@ -1623,25 +1708,15 @@ extern "C" rs_status rs_ragged_sqnorm(const rs_layout* L, const float* x, double
   RS_TRY(check_ptr(ws, 8, fn, "ws"));
   if (partial) RS_TRY(check_ptr(partial, 8, fn, "partial"));
   if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // coarse chunks, unless the range has too few of them to fill the chip
-  const int fine = (L->rank_cchunk[k1] - L->rank_cchunk[k0]) < RS_SQNORM_FINE_BELOW ? 1 : 0;
-  const std::vector<int64_t>& rb = fine ? L->rank_chunk : L->rank_cchunk;
-  const int64_t c0 = rb[k0], nc = rb[k1] - c0;
-  double* part = static_cast<double*>(ws);
-  if (nc > 0)
-    hipLaunchKernelGGL(sqnorm_partial_kernel, chunk_grid(nc), dim3(kThreads), 0, s,
-                       table<ChunkDesc>(L, fine ? L->off_chunks : L->off_cchunks), c0, nc, x, part,
-                       found_inf);
-  hipLaunchKernelGGL(sqnorm_combine_kernel, dim3(unsigned(L->n)), dim3(kCombineWaves * kWave), 0, s,
-                     table<TensorDesc>(L, L->off_tensors), table<FragDesc>(L, L->off_frags), part,
-                     L->n, k0, k1, sq_out, partial, fine);
-  return after_launch(fn);
+  return sqnorm_launch(L, x, sq_out, partial, found_inf, static_cast<double*>(ws), k0, k1,
+                       static_cast<hipStream_t>(stream), fn);
+} catch (...) {
+  return rs::on_exception("rs_ragged_sqnorm");
 }
 
 extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt fmt,
                                     uint8_t* codes, float* scales, uint32_t* found_inf, int32_t k0,
-                                    int32_t k1, void* stream) {
+                                    int32_t k1, void* stream) try {
   const char* fn = "rs_block_quant";
   RS_TRY(check_common(L, k0, k1, fn));
   if (fmt != RS_Q_FP8_E4M3 && fmt != RS_Q_INT8)
@@ -1671,13 +1746,13 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
 #define RS_QUANT_LAUNCH(FM, NT)                                                                 \
   do {                                                                                          \
     if (c == 0)                                                                                 \
-      hipLaunchKernelGGL((quant_kernel<FM, 1, kNarrowSlots, NT>), g, b, 0, s, wk, w1, x, codes, \
+      launch((quant_kernel<FM, 1, kNarrowSlots, NT>), g, b, 0, s, wk, w1, x, codes, \
                          scales, found_inf, vec_ok);                                            \
     else if (F == RS_QUANT_F_SMALL)                                                             \
-      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F_SMALL, kWideSlots / RS_QUANT_F_SMALL, NT>), \
+      launch((quant_kernel<FM, RS_QUANT_F_SMALL, kWideSlots / RS_QUANT_F_SMALL, NT>), \
                          g, b, 0, s, wk, w1, x, codes, scales, found_inf, vec_ok);              \
     else                                                                                        \
-      hipLaunchKernelGGL((quant_kernel<FM, RS_QUANT_F, kWideSlots / RS_QUANT_F, NT>), g, b, 0,  \
+      launch((quant_kernel<FM, RS_QUANT_F, kWideSlots / RS_QUANT_F, NT>), g, b, 0,  \
                          s, wk, w1, x, codes, scales, found_inf, vec_ok);                       \
   } while (0)
       if (fmt == RS_Q_FP8_E4M3 && nts)
@@ -1693,11 +1768,13 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
     }
   }
   return RS_OK;
+} catch (...) {
+  return rs::on_exception("rs_block_quant");
 }
 
 extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, rs_qfmt fmt,
                                       const float* scales, void* y, rs_dtype y_dt, int32_t k0,
-                                      int32_t k1, void* stream) {
+                                      int32_t k1, void* stream) try {
   const char* fn = "rs_block_dequant";
   RS_TRY(check_common(L, k0, k1, fn));
   if (fmt != RS_Q_FP8_E4M3 && fmt != RS_Q_INT8)
@@ -1729,10 +1806,10 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
 #define RS_DEQ_LAUNCH2(FM, YK, NT)                                                             \
   do {                                                                                         \
     if (split)                                                                                 \
-      hipLaunchKernelGGL((dequant_kernel<FM, YK, RS_DEQ_SPLIT, NT>), g, b, 0, s, wk, w1, codes,  \
+      launch((dequant_kernel<FM, YK, RS_DEQ_SPLIT, NT>), g, b, 0, s, wk, w1, codes,  \
                          scales, y, vec_ok);                                                   \
     else                                                                                       \
-      hipLaunchKernelGGL((dequant_kernel<FM, YK, 1, NT>), g, b, 0, s, wk, w1, codes, scales, y,  \
+      launch((dequant_kernel<FM, YK, 1, NT>), g, b, 0, s, wk, w1, codes, scales, y,  \
                          vec_ok);                                                              \
   } while (0)
 #define RS_DEQ_LAUNCH(FM, YK)          \
@@ -1756,12 +1833,14 @@ extern "C" rs_status rs_block_dequant(const rs_layout* L, const uint8_t* codes, 
     }
   }
   return RS_OK;
+} catch (...) {
+  return rs::on_exception("rs_block_dequant");
 }
 
 extern "C" rs_status rs_adamw_step(const rs_layout* L, float* p, const float* g, float* m, float* v,
                                    const rs_adamw_params* hp, const uint8_t* tensor_mask,
                                    const uint32_t* found_inf, int32_t k0, int32_t k1,
-                                   void* stream) {
+                                   void* stream) try {
   const char* fn = "rs_adamw_step";
   RS_TRY(check_common(L, k0, k1, fn));
   if (!hp) return fail(RS_ERR_INVALID_ARG, "rs_adamw_step: null hyperparameters");
@@ -1785,15 +1864,17 @@ extern "C" rs_status rs_adamw_step(const rs_layout* L, float* p, const float* g,
   k.inv = 1.0f / hp->grad_scale;
   const int64_t c0 = L->rank_chunk[k0], nc = L->rank_chunk[k1] - c0;
   if (nc == 0) return RS_OK;
-  hipLaunchKernelGGL(adamw_kernel<RS_ADAMW_SPLIT>, chunk_grid(nc * RS_ADAMW_SPLIT), dim3(kThreads), 0,
+  launch(adamw_kernel<RS_ADAMW_SPLIT>, chunk_grid(nc * RS_ADAMW_SPLIT), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), table<ChunkDesc>(L, L->off_chunks), c0, nc,
                      p, g, m, v, k, tensor_mask, found_inf, L->m);
   return after_launch(fn);
+} catch (...) {
+  return rs::on_exception("rs_adamw_step");
 }
 
 extern "C" rs_status rs_sgd_step(const rs_layout* L, float* p, const float* g, float* buf,
                                  const rs_sgd_params* hp, const uint8_t* tensor_mask,
-                                 const uint32_t* found_inf, int32_t k0, int32_t k1, void* stream) {
+                                 const uint32_t* found_inf, int32_t k0, int32_t k1, void* stream) try {
   const char* fn = "rs_sgd_step";
   RS_TRY(check_common(L, k0, k1, fn));
   if (!hp) return fail(RS_ERR_INVALID_ARG, "rs_sgd_step: null hyperparameters");
@@ -1810,17 +1891,19 @@ extern "C" rs_status rs_sgd_step(const rs_layout* L, float* p, const float* g, f
   k.nesterov = hp->nesterov ? 1 : 0;
   const int64_t c0 = L->rank_chunk[k0], nc = L->rank_chunk[k1] - c0;
   if (nc == 0) return RS_OK;
-  hipLaunchKernelGGL(sgd_kernel<RS_SGD_SPLIT>, chunk_grid(nc * RS_SGD_SPLIT), dim3(kThreads), 0,
+  launch(sgd_kernel<RS_SGD_SPLIT>, chunk_grid(nc * RS_SGD_SPLIT), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), table<ChunkDesc>(L, L->off_chunks), c0, nc,
                      p, g, buf, k, tensor_mask, found_inf, L->m);
   return after_launch(fn);
+} catch (...) {
+  return rs::on_exception("rs_sgd_step");
 }
 
 extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g, uint8_t* m_codes,
                                     float* m_scales, uint8_t* v_codes, float* v_scales,
                                     rs_qfmt fmt, const rs_adamw_params* hp,
                                     const uint32_t* found_inf, int32_t k0, int32_t k1,
-                                    void* stream) {
+                                    void* stream) try {
   const char* fn = "rs_adamw8_step";
   RS_TRY(check_common(L, k0, k1, fn));
   if (!hp) return fail(RS_ERR_INVALID_ARG, "rs_adamw8_step: null hyperparameters");
@@ -1867,10 +1950,10 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
 #define RS_ADAM8_LAUNCH(FM)                                                                     \
   do {                                                                                          \
     if (c == 0)                                                                                 \
-      hipLaunchKernelGGL((adamw8_kernel<FM, 1, kNarrowSlots>), gr, b, 0, s, wk, w1, p, g,       \
+      launch((adamw8_kernel<FM, 1, kNarrowSlots>), gr, b, 0, s, wk, w1, p, g,       \
                          m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);     \
     else                                                                                        \
-      hipLaunchKernelGGL((adamw8_kernel<FM, RS_ADAM8_F, kWideSlots / RS_ADAM8_F>), gr, b, 0, s, \
+      launch((adamw8_kernel<FM, RS_ADAM8_F, kWideSlots / RS_ADAM8_F>), gr, b, 0, s, \
                          wk, w1, p, g, m_codes, m_scales, v_codes, v_scales, k, found_inf,      \
                          L->m, vec_ok);                                                         \
   } while (0)
@@ -1883,4 +1966,7 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
     }
   }
   return RS_OK;
+} catch (...) {
+  return rs::on_exception("rs_adamw8_step");
 }
+

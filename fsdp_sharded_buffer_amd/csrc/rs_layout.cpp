@@ -103,6 +103,14 @@ rs_status build(rs_layout* L) {
     L->rank_min_tile_rows[c].assign(m, INT32_MAX);
   }
 
+  // Chunk indices are int32 in the device tables.  The fine table holds at
+  // most ceil(m*S / chunk) chunks plus one partial chunk per run, and the
+  // runs (fragments and padding gaps) number at most 2(n + m); refuse before
+  // building rather than after.
+  const int64_t max_chunks = (int64_t(m) * S + L->chunk_elems - 1) / L->chunk_elems + 2 * (int64_t(n) + m);
+  if (max_chunks > int64_t(INT32_MAX))
+    return fail(RS_ERR_INVALID_ARG,
+                "rs_layout_create: more than 2^31 work chunks (m*S / chunk_elems); raise chunk_elems");
   build_chunks(L, L->chunk_elems, L->chunks, L->rank_chunk, true);
   build_chunks(L, L->chunk_elems * kCoarseFactor, L->cchunks, L->rank_cchunk, false);
   if (L->chunks.size() > size_t(INT32_MAX) || L->frags.size() > size_t(INT32_MAX))
@@ -215,7 +223,7 @@ rs_status build(rs_layout* L) {
 
 extern "C" rs_status rs_layout_create(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t S,
                                       const int64_t* offsets, int64_t chunk_elems,
-                                      rs_layout** out) {
+                                      rs_layout** out) try {
   if (!specs || !offsets || !out || n <= 0 || m <= 0 || S <= 0)
     return fail(RS_ERR_INVALID_ARG, "rs_layout_create: null pointer or non-positive n/m/S");
   if (n > kMaxTensors || m > kMaxRanks || S > 2 * kMaxElems)
@@ -267,9 +275,11 @@ extern "C" rs_status rs_layout_create(const rs_tensor_spec* specs, int32_t n, in
   *out = L;
   clear_error();
   return RS_OK;
+} catch (...) {
+  return rs::on_exception("rs_layout_create");
 }
 
-extern "C" rs_status rs_layout_get_info(const rs_layout* L, rs_layout_info* info) {
+extern "C" rs_status rs_layout_get_info(const rs_layout* L, rs_layout_info* info) try {
   if (!L || !info) return fail(RS_ERR_INVALID_ARG, "rs_layout_get_info: null pointer");
   info->n = L->n;
   info->m = L->m;
@@ -283,9 +293,15 @@ extern "C" rs_status rs_layout_get_info(const rs_layout* L, rs_layout_info* info
   info->device_bytes = int64_t(L->device_bytes);
   info->workspace_bytes = int64_t(L->workspace_bytes);
   return RS_OK;
+} catch (...) {
+  return rs::on_exception("rs_layout_get_info");
 }
 
-extern "C" rs_status rs_layout_upload(rs_layout* L, void* dev_table, void* stream) {
+extern "C" size_t rs_layout_device_bytes(const rs_layout* L) { return L ? L->device_bytes : 0; }
+
+extern "C" size_t rs_workspace_bytes(const rs_layout* L) { return L ? L->workspace_bytes : 0; }
+
+extern "C" rs_status rs_layout_upload(rs_layout* L, void* dev_table, void* stream) try {
   if (!L || !dev_table) return fail(RS_ERR_INVALID_ARG, "rs_layout_upload: null pointer");
   if (reinterpret_cast<uintptr_t>(dev_table) % 256)
     return fail(RS_ERR_ALIGN, "rs_layout_upload: dev_table must be 256-byte aligned");
@@ -306,6 +322,8 @@ extern "C" rs_status rs_layout_upload(rs_layout* L, void* dev_table, void* strea
   L->dev = dev_table;
   clear_error();
   return RS_OK;
+} catch (...) {
+  return rs::on_exception("rs_layout_upload");
 }
 
 extern "C" void rs_layout_destroy(rs_layout* L) { delete L; }

@@ -17,6 +17,7 @@
 #include <chrono>
 #include <cstdlib>
 #include <cstring>
+#include <new>
 #include <numeric>
 #include <system_error>
 #include <thread>
@@ -35,6 +36,27 @@ rs_status fail(rs_status st, const std::string& msg) {
 }
 
 void clear_error() { g_last_error.clear(); }
+
+rs_status on_exception(const char* fn) noexcept {
+  rs_status st = RS_ERR_INVALID_ARG;
+  const char* what = "unexpected host exception";
+  try {
+    throw;
+  } catch (const std::bad_alloc&) {
+    st = RS_ERR_NOMEM;
+    what = "out of host memory";
+  } catch (const std::system_error&) {
+    st = RS_ERR_NOMEM;
+    what = "could not start a host thread";
+  } catch (...) {
+  }
+  try {
+    g_last_error = std::string(fn) + ": " + what;
+  } catch (...) {
+    g_last_error.clear();
+  }
+  return st;
+}
 
 namespace {
 
@@ -246,7 +268,7 @@ void order_perm(const rs_tensor_spec* specs, int32_t n, rs_order kind, int32_t* 
 }  // namespace rs
 
 extern "C" rs_status rs_plan(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t align,
-                             int64_t S_cap, int64_t* offsets, rs_plan_info* info) {
+                             int64_t S_cap, int64_t* offsets, rs_plan_info* info) try {
   using namespace rs;
   const auto t0 = std::chrono::steady_clock::now();
   if (!specs || !offsets || n <= 0 || m <= 0 || align <= 0)
@@ -264,10 +286,12 @@ extern "C" rs_status rs_plan(const rs_tensor_spec* specs, int32_t n, int32_t m, 
   fill_info(info, items, m, S, lb, t0);
   clear_error();
   return RS_OK;
+} catch (...) {
+  return rs::on_exception("rs_plan");
 }
 
 extern "C" rs_status rs_plan_order(const rs_tensor_spec* specs, int32_t n, rs_order kind,
-                                   int32_t* perm) {
+                                   int32_t* perm) try {
   using namespace rs;
   if (!specs || !perm || n <= 0)
     return fail(RS_ERR_INVALID_ARG, "rs_plan_order: null pointer or non-positive n");
@@ -276,11 +300,13 @@ extern "C" rs_status rs_plan_order(const rs_tensor_spec* specs, int32_t n, rs_or
   order_perm(specs, n, kind, perm);
   clear_error();
   return RS_OK;
+} catch (...) {
+  return rs::on_exception("rs_plan_order");
 }
 
 extern "C" rs_status rs_plan_ordered(const rs_tensor_spec* specs, int32_t n, int32_t m,
                                      int64_t align, int64_t S_cap, rs_order kind, int32_t* perm,
-                                     int64_t* offsets, rs_plan_info* info) {
+                                     int64_t* offsets, rs_plan_info* info) try {
   using namespace rs;
   const auto t0 = std::chrono::steady_clock::now();
   if (!specs || !perm || !offsets || n <= 0 || m <= 0 || align <= 0)
@@ -328,6 +354,8 @@ extern "C" rs_status rs_plan_ordered(const rs_tensor_spec* specs, int32_t n, int
   fill_info(info, items, m, best_S, best_lb, t0);
   clear_error();
   return RS_OK;
+} catch (...) {
+  return rs::on_exception("rs_plan_ordered");
 }
 
 extern "C" const char* rs_status_str(rs_status st) {
@@ -340,6 +368,7 @@ extern "C" const char* rs_status_str(rs_status st) {
     case RS_ERR_RANGE: return "rank range out of bounds";
     case RS_ERR_HIP: return "HIP runtime error";
     case RS_ERR_STATE: return "layout not uploaded";
+    case RS_ERR_NOMEM: return "out of host resources";
     default: return "unknown status";
   }
 }

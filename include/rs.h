@@ -29,14 +29,20 @@
  *
  * Concurrency.  A call reads and writes only its rank range (and the
  * found_inf flags of those ranks), so calls over disjoint rank ranges may
- * run at the same time on different streams; rs_ragged_sqnorm calls that
- * overlap in time need separate workspaces.
+ * run at the same time on different streams.  rs_ragged_sqnorm is the
+ * exception: it writes sq[t] for every tensor, so calls that overlap in time
+ * need separate sq arrays as well as separate workspaces.
+ *
+ * Aliasing.  Outputs must not overlap inputs or other outputs, except where a
+ * call says so (rs_group_scale_add: x may be y).
  *
  * Errors.  Every call returns an rs_status.  On a non-zero status from
  * argument checking nothing was enqueued, no output was touched, and
  * rs_last_error() returns a message for the calling thread.  RS_ERR_HIP
- * reports a failed launch (hipGetLastError after each launch); launches of
- * the same call before the failed one stay enqueued.
+ * reports a launch that failed (that launch's own hipLaunchKernel status,
+ * not an error left by earlier work); launches of the same call before the
+ * failed one stay enqueued.  RS_ERR_NOMEM reports a host allocation or host
+ * thread that failed in a set-up call; no C++ exception leaves the library.
  *
  * Alignment.  Kernels use 128-bit accesses where a fragment's buffer and
  * tensor addresses are 16-byte aligned, and element accesses elsewhere, so
@@ -62,7 +68,8 @@ enum {
   RS_ERR_INFEASIBLE = -4,  /* no layout with S <= S_cap */
   RS_ERR_RANGE = -5,       /* rank range outside 0 <= k0 < k1 <= m */
   RS_ERR_HIP = -6,         /* HIP runtime error */
-  RS_ERR_STATE = -7        /* layout not uploaded */
+  RS_ERR_STATE = -7,       /* layout not uploaded */
+  RS_ERR_NOMEM = -8        /* a host allocation or host thread failed */
 };
 
 typedef int32_t rs_dtype;
@@ -187,6 +194,15 @@ rs_status rs_layout_create(const rs_tensor_spec* specs, int32_t n, int32_t m, in
                            const int64_t* offsets, int64_t chunk_elems, rs_layout** out);
 rs_status rs_layout_get_info(const rs_layout* layout, rs_layout_info* info);
 
+/* rs_layout_device_bytes - bytes the caller allocates on the device for the
+ * layout's tables (info.device_bytes); 0 for a NULL layout.  Host only. */
+size_t rs_layout_device_bytes(const rs_layout* layout);
+
+/* rs_workspace_bytes - bytes of device scratch rs_ragged_sqnorm needs (one
+ * fp64 partial per work chunk; info.workspace_bytes); 0 for a NULL layout.
+ * Host only. */
+size_t rs_workspace_bytes(const rs_layout* layout);
+
 /* rs_layout_upload - copy the tables into dev_table (device, at least
  * info.device_bytes, 256-byte aligned) on `stream` and wait for the copy.
  * The layout then uses dev_table in every call; the caller keeps it alive
@@ -228,7 +244,12 @@ rs_status rs_unpack(const rs_layout* layout, const void* buf, rs_dtype buf_dt,
  *   tensor elements in [k0*S, k1*S) whose tensor_mask[t] != 0 (all tensors
  *   when tensor_mask is NULL); padding is never written.
  *   y          device fp32, m*S elements
- *   x          device, m*S elements of x_dt (RS_F32 or RS_BF16)
+ *   x          device, m*S elements of x_dt (RS_F32 or RS_BF16).  x may be
+ *              y itself (x_dt RS_F32), as in the sharded gradient scaler's
+ *              in-place unscale (beta = 0): then y <- fl(fl(alpha*y) +
+ *              fl(beta*y)) element by element, each element read before it
+ *              is written by the same lane.  Any other overlap of x and y
+ *              is undefined.
  *   tensor_mask device uint8 [n] or NULL
  *   found_inf  device uint32 [m] or NULL: found_inf[k] is set to 1 when a
  *              written value in rank k is not finite; never cleared (the
@@ -252,7 +273,8 @@ rs_status rs_group_zero(const rs_layout* layout, void* y, rs_dtype dt,
  * NaN, otherwise an infinite input makes it +Inf.
  *   x          device fp32, m*S elements
  *   sq         device double [n] out: written for every tensor (0 when the
- *              tensor has no element in the range)
+ *              tensor has no element in the range), so calls that overlap
+ *              in time must not share it
  *   partial    device double [m*n] or NULL: partial[k*n + t] = the sum over
  *              tensor t's fragment in rank k, written for k in [k0, k1)
  *              (0 where the rank holds none of t) - the value each rank

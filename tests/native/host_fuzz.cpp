@@ -60,6 +60,22 @@ int main(int argc, char** argv) {
     offs[U(0, n - 1)] += U(-5, 5);
     if (rs_layout_create(sp.data(), n, m, info.S, offs.data(), chunk, &L) == RS_OK) rs_layout_destroy(L);
   }
+  // A layout inside the size limits whose chunk table could not be indexed
+  // (2^42 positions in 2048-element chunks) is refused before any table is
+  // built, with a status rather than an exception.
+  {
+    rs_tensor_spec one{1, 4, 0, 0, 0};
+    const int64_t off = 0;
+    rs_layout* L = nullptr;
+    const rs_status st = rs_layout_create(&one, 1, 4, int64_t(1) << 40, &off, 0, &L);
+    if (st != RS_ERR_INVALID_ARG || L != nullptr) {
+      std::printf("large S: status %d (%s)\n", int(st), rs_last_error()); return 1;
+    }
+    if (rs_layout_create(&one, 1, 4, int64_t(1) << 40, &off, 1 << 22, &L) != RS_OK) {
+      std::printf("large S with 2^22-element chunks refused: %s\n", rs_last_error()); return 1;
+    }
+    rs_layout_destroy(L);
+  }
   std::printf("fuzz ok: %d layouts built, %d rejected\n", ok, rej);
   return 0;
 }

@@ -381,3 +381,34 @@ def test_layout_rejects_a_tile_across_a_shard_boundary():
     h = R.rs_layout_create(specs, 2, info["S"], offs)
     assert R.rs_layout_get_info(h)["num_tiles"] == 2
     R.rs_layout_destroy(h)
+
+
+def test_size_getters_match_layout_info():
+    """rs_layout_device_bytes / rs_workspace_bytes give the sizes the caller
+    allocates, equal to the layout info's, and 0 for a NULL layout."""
+    w = W.llama8b_layer()
+    offs, info = R.rs_plan(w.tensors, w.m, 16)
+    h = R.rs_layout_create(w.tensors, w.m, info["S"], offs)
+    li = R.rs_layout_get_info(h)
+    assert R.rs_layout_device_bytes(h) == li["device_bytes"] > 0
+    assert R.rs_workspace_bytes(h) == li["workspace_bytes"] >= 8 * li["num_chunks"]
+    R.rs_layout_destroy(h)
+    assert R.rs_layout_device_bytes(None) == 0 and R.rs_workspace_bytes(None) == 0
+
+
+def test_layout_refuses_unindexable_chunk_tables_before_building():
+    """A layout within the size limits whose fine chunk table would exceed
+    int32 indices is refused with RS_ERR_INVALID_ARG, quickly and without
+    building it; larger chunks make the same layout acceptable."""
+    import time
+    one = [W.TensorSpec("a", 1, 4, 0)]
+    t0 = time.perf_counter()
+    with pytest.raises(R.RsError) as e:
+        R.rs_layout_create(one, 4, 1 << 40, [0])
+    assert e.value.status == -1 and "chunks" in R.rs_last_error()
+    assert time.perf_counter() - t0 < 1.0
+    h = R.rs_layout_create(one, 4, 1 << 40, [0], chunk_elems=1 << 22)
+    # the 4-element tensor splits the first chunk in two
+    assert R.rs_layout_get_info(h)["num_chunks"] == ((4 << 40) >> 22) + 1
+    R.rs_layout_destroy(h)
+    assert R.rs_status_str(R.RS_ERR_NOMEM) == "out of host resources"
