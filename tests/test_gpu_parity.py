@@ -196,6 +196,31 @@ def test_scale_add_found_inf_ors():
     assert_f32_equal_nan_class(to_np(y), ey, "scale_add nonfinite")
 
 
+@pytest.mark.parametrize("name", ["toy", "ragged_a1_c64", "mixed_div", "moe_div8", "tiny", "tall"])
+def test_scale_add_in_place(name):
+    """x is y itself, as in the sharded gradient scaler's in-place unscale:
+    y' = fl(fl(alpha*y) + fl(beta*y)) per element, bit-exact against the
+    oracle run on two separate copies of the same values."""
+    import torch
+    c = case(name)
+    R = c.R
+    inp = c.inputs()
+    y0 = c.flat(inp.grads, fill=np.float32(12345.0))
+    for (alpha, beta) in [(1.0 / 65536, 0.0), (1.0, 1.0), (0.75, -1.5), (0.0, 3.0e38)]:
+        for k0, k1 in c.ranges()[:3]:
+            log(f"scale_add in place {name} a={alpha} b={beta} [{k0},{k1})")
+            whole, y = guarded(c.total, torch.float32, F32_CANARY)
+            y.copy_(torch.from_numpy(y0))
+            fi = torch.zeros(c.m, dtype=torch.int32, device="cuda")
+            R.rs_group_scale_add(c.lay.handle, y, y, R.RS_F32, alpha, beta, None, fi, k0, k1)
+            _sync()
+            ey, ef = O.scale_add(y0, y0.copy(), alpha, beta, c.items, c.offsets, c.S, c.m, k0, k1)
+            what = f"scale_add in place {name} a={alpha} b={beta} [{k0},{k1})"
+            assert_f32_equal_nan_class(to_np(y), ey, what)
+            assert np.array_equal(to_np(fi).astype(np.uint32), ef), what + " found_inf"
+            check_guards(whole, F32_CANARY, "scale_add in place y")
+
+
 # ------------------------------------------------------------------ zero
 
 

@@ -1,6 +1,7 @@
 """The Python example of README.md runs as written, and its results hold:
-the packed buffer holds each tensor's bf16 values at its offset, the norms
-are the squared norms of the unscaled grads, and rank 0's codes decode to
+the packed buffer holds each tensor's bf16 values at its offset, the
+in-place unscale (x is y) equals the oracle's scale/add bit for bit, the
+norms are the squared norms of the unscaled grads, and rank 0's codes decode to
 its grads within the quantisation bound."""
 import os
 import re
@@ -9,6 +10,8 @@ import numpy as np
 import pytest
 
 from oracle import casts as OC
+from oracle import ops as O
+from oracle import plan as P
 from harness import to_np
 
 pytestmark = pytest.mark.gpu
@@ -23,13 +26,33 @@ def test_readme_example():
     text = open(os.path.join(ROOT, "README.md")).read()
     blocks = re.findall(r"```python\n(.*?)```", text, flags=re.S)
     assert blocks, "no python example in README.md"
-    ns = {}
-    exec(compile(blocks[0], "README.md", "exec"), ns)
+    import fsdp_sharded_buffer_amd as pkg
+    # record the grads as the example's in-place unscale receives them
+    seen = []
+    real = pkg.rs_group_scale_add
+
+    def spy(layout, y, x, *args, **kw):
+        seen.append((to_np(y).copy(), x is y, args[:3]))
+        return real(layout, y, x, *args, **kw)
+
+    pkg.rs_group_scale_add = spy
+    try:
+        ns = {}
+        exec(compile(blocks[0], "README.md", "exec"), ns)
+    finally:
+        pkg.rs_group_scale_add = real
     R, lay, w = ns["R"], ns["lay"], ns["w"]
     buf, params, grad, sq = to_np(ns["buf"]), ns["params"], ns["grad"], to_np(ns["sq"])
     for t, (spec, l) in enumerate(zip(lay.specs, lay.offsets)):
         exp = OC.bf16_bits_from_f32(to_np(params[t]).reshape(-1))
         assert np.array_equal(buf[l:l + exp.size], exp), f"tensor {t}"
+    # the unscaled grads equal the oracle's scale/add of the grads it was given
+    (g0, aliased, (x_dt, alpha, beta)), = seen
+    assert aliased and x_dt == R.RS_F32
+    items = P.items_from_specs(lay.specs)
+    ey, ef = O.scale_add(g0, g0.copy(), alpha, beta, items, lay.offsets, lay.S, lay.m, 0, lay.m)
+    assert np.array_equal(to_np(grad).view(np.uint32), ey.view(np.uint32)), "unscale"
+    assert not ef.any()
     g = to_np(grad).astype(np.float64)
     for t, (spec, l) in enumerate(zip(lay.specs, lay.offsets)):
         e = float(np.sum(g[l:l + spec.rows * spec.cols] ** 2))

@@ -3,8 +3,14 @@ two calls over disjoint rank ranges may run concurrently on two streams (as
 ranks' work would on their own devices).  Each operation is issued as two
 half-range calls on two default-priority streams without waiting between
 them, and the results must equal one whole-range call bit for bit.  The
-norms use one workspace per stream and compare the per-rank partials."""
+norms use one workspace and one sq array per stream (rs_ragged_sqnorm
+writes sq for every tensor); the per-rank partials must equal the
+whole-range call's, and each stream's sq must equal the oracle's sums over
+that stream's ranks and a later call over the same ranks on one stream."""
+import numpy as np
 import pytest
+
+from oracle import ops as O
 
 from harness import case, from_np, log, to_np
 
@@ -43,6 +49,7 @@ def test_disjoint_rank_ranges_on_two_streams(name):
             "outs": [torch.zeros(s.numel, dtype=torch.float32, device="cuda") for s in c.w.tensors],
             "y": y0.clone(), "found": torch.zeros(m, dtype=torch.int32, device="cuda"),
             "sq": torch.zeros(n, dtype=torch.float64, device="cuda"),
+            "sq2": torch.zeros(n, dtype=torch.float64, device="cuda"),
             "part": torch.zeros(m * n, dtype=torch.float64, device="cuda"),
             "codes": torch.full((c.total,), 0xAB, dtype=torch.uint8, device="cuda"),
             "scales": torch.zeros(nt, dtype=torch.float32, device="cuda"),
@@ -54,12 +61,12 @@ def test_disjoint_rank_ranges_on_two_streams(name):
         b["otab"] = R.ptr_table(b["outs"])  # device pointer table, built before any stream work
         return b
 
-    def run(b, k0, k1, stream, ws):
+    def run(b, k0, k1, stream, ws, sq="sq"):
         s = stream.cuda_stream
         R.rs_pack(h, ptab, R.RS_F32, b["buf"], R.RS_BF16, k0, k1, s)
         R.rs_unpack(h, b["buf"], R.RS_BF16, b["otab"], R.RS_F32, k0, k1, s)
         R.rs_group_scale_add(h, b["y"], x0, R.RS_F32, 0.5, 2.0, None, b["found"], k0, k1, s)
-        R.rs_ragged_sqnorm(h, b["y"], b["sq"], b["part"], None, ws, k0, k1, s)
+        R.rs_ragged_sqnorm(h, b["y"], b[sq], b["part"], None, ws, k0, k1, s)
         R.rs_block_quant(h, b["y"], qf, b["codes"], b["scales"], k0, k1, s)
         R.rs_block_dequant(h, b["codes"], qf, b["scales"], b["deq"], R.RS_F32, k0, k1, s)
         R.rs_group_zero(h, b["z"], R.RS_F32, None, k0, k1, s)
@@ -77,13 +84,13 @@ def test_disjoint_rank_ranges_on_two_streams(name):
     s2.wait_stream(torch.cuda.current_stream())
     for _ in range(3):  # several rounds, each pair issued without waiting between the streams
         run(split, 0, half, s1, c.lay.ws)
-        run(split, half, m, s2, ws2)
+        run(split, half, m, s2, ws2, "sq2")
     torch.cuda.synchronize()
     # the repeated rounds are idempotent except the accumulating ones: redo
     # those once more from a fresh state, concurrently
     once = buffers()
     run(once, 0, half, s1, c.lay.ws)
-    run(once, half, m, s2, ws2)
+    run(once, half, m, s2, ws2, "sq2")
     torch.cuda.synchronize()
     log(f"{name}: m={m}, ranges [0,{half}) and [{half},{m}) on two streams")
 
@@ -100,3 +107,16 @@ def test_disjoint_rank_ranges_on_two_streams(name):
         assert same(split[key], whole[key]), f"{name} repeated {key}"
     for t, (a, b) in enumerate(zip(split["outs"], whole["outs"])):
         assert same(a, b), f"{name} repeated unpack t{t}"
+    # each stream's own sq: the oracle's sums over its ranks (of the y both
+    # streams produced), and bit-equal to a later single-stream call
+    yh = to_np(once["y"])
+    for key, (k0, k1) in (("sq", (0, half)), ("sq2", (half, m))):
+        got = to_np(once[key])
+        esq = O.sqnorm(yh, c.items, c.offsets, c.S, m, k0, k1)[0]
+        assert np.array_equal(np.isnan(got), np.isnan(esq)), f"{name} {key}"
+        f = np.isfinite(esq)
+        assert np.all(np.abs(got[f] - esq[f]) <= 1e-5 * np.abs(esq[f])), f"{name} {key}"
+        ref = torch.zeros(n, dtype=torch.float64, device="cuda")
+        R.rs_ragged_sqnorm(h, once["y"], ref, None, None, c.lay.ws, k0, k1)
+        torch.cuda.synchronize()
+        assert same(once[key], ref), f"{name} {key} against one stream"
