@@ -30,7 +30,7 @@ __all__ = [
     "rs_plan", "rs_plan_order", "rs_plan_ordered", "rs_layout_create", "rs_layout_get_info",
     "rs_layout_device_bytes", "rs_workspace_bytes", "rs_layout_upload",
     "rs_layout_destroy", "rs_pack", "rs_unpack", "rs_group_scale_add", "rs_group_zero",
-    "rs_ragged_sqnorm", "rs_block_quant", "rs_block_dequant", "rs_adamw_step", "rs_adamw8_step",
+    "rs_ragged_sqnorm", "rs_ragged_sqnorm_noalloc", "rs_block_quant", "rs_block_dequant", "rs_adamw_step", "rs_adamw8_step",
     "rs_sgd_step",
     "rs_status_str", "rs_last_error",
     "Layout", "ptr_table", "dtype_code", "specs_array",
@@ -151,6 +151,12 @@ def rs_ragged_sqnorm(layout, x, sq, partial=None, found_inf=None, ws=None, k0: i
                      stream=None) -> None:
     check(lib().rs_ragged_sqnorm(layout, _ptr(x), _ptr(sq), _ptr(partial), _ptr(found_inf), _ptr(ws),
                                  k0, k1, _stream(stream)))
+
+
+def rs_ragged_sqnorm_noalloc(layout, x, sq, partial=None, found_inf=None, k0: int = 0,
+                             k1: int = 1, stream=None) -> None:
+    check(lib().rs_ragged_sqnorm_noalloc(layout, _ptr(x), _ptr(sq), _ptr(partial), _ptr(found_inf),
+                                         k0, k1, _stream(stream)))
 
 
 def rs_block_quant(layout, x, fmt: int, codes, scales, k0: int, k1: int, stream=None,

@@ -69,6 +69,8 @@ SIGNATURES = {
                                 c_void_p]),
     "rs_ragged_sqnorm": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_int32, c_int32, c_void_p]),
+    "rs_ragged_sqnorm_noalloc": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_int32, c_int32, c_void_p]),
     "rs_block_quant": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                  c_int32, c_int32, c_void_p]),
     "rs_block_dequant": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,

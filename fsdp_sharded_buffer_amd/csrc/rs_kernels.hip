@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <utility>
@@ -1970,3 +1971,63 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
   return rs::on_exception("rs_adamw8_step");
 }
 
+// ------------------------------------------------------ no-allocation norms
+//
+// rs_ragged_sqnorm_noalloc keeps the chunk partials in this file-scope device
+// array instead of a caller workspace.  Each GPU the library runs on holds
+// its own copy until the process ends.  Host code never passes the array's
+// name to a kernel: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in g_scratch_ptr.
+constexpr int64_t kStaticPartials = 131072;  // 1 MiB of fp64 partials
+static __device__ __align__(256) double scratch[kStaticPartials];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the device's first call).
+rs_status static_scratch(const char* fn, double** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RS_ERR_HIP, std::string(fn) + ": " + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(RS_ERR_INVALID_ARG, std::string(fn) + ": device index beyond 255");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(RS_ERR_HIP, std::string(fn) + ": hipGetSymbolAddress: " + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<double*>(g_scratch_ptr[dev]);
+  return RS_OK;
+}
+
+}  // namespace
+
+extern "C" rs_status rs_ragged_sqnorm_noalloc(const rs_layout* L, const float* x, double* sq_out,
+                                              double* partial, uint32_t* found_inf, int32_t k0,
+                                              int32_t k1, void* stream) try {
+  const char* fn = "rs_ragged_sqnorm_noalloc";
+  RS_TRY(check_common(L, k0, k1, fn));
+  RS_TRY(check_ptr(x, 4, fn, "x"));
+  RS_TRY(check_ptr(sq_out, 8, fn, "sq"));
+  if (partial) RS_TRY(check_ptr(partial, 8, fn, "partial"));
+  if (found_inf) RS_TRY(check_ptr(found_inf, 4, fn, "found_inf"));
+  int fine = 0;
+  const int64_t need = sqnorm_partials(L, k0, k1, &fine);
+  if (need > kStaticPartials)
+    return fail(RS_ERR_INVALID_ARG,
+                std::string(fn) + ": the rank range has " + std::to_string(need) +
+                    " work chunks and the static scratch holds " + std::to_string(kStaticPartials) +
+                    " partials; use rs_ragged_sqnorm with a workspace or a smaller range");
+  double* part = nullptr;
+  RS_TRY(static_scratch(fn, &part));
+  return sqnorm_launch(L, x, sq_out, partial, found_inf, part, k0, k1,
+                       static_cast<hipStream_t>(stream), fn);
+} catch (...) {
+  return rs::on_exception("rs_ragged_sqnorm_noalloc");
+}

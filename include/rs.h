@@ -286,6 +286,25 @@ rs_status rs_group_zero(const rs_layout* layout, void* y, rs_dtype dt,
 rs_status rs_ragged_sqnorm(const rs_layout* layout, const float* x, double* sq, double* partial,
                            uint32_t* found_inf, void* ws, int32_t k0, int32_t k1, void* stream);
 
+/* rs_ragged_sqnorm_noalloc - rs_ragged_sqnorm without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same kernels, same
+ * results bit for bit; the chunk partials go to a static device array of the
+ * library (1 MiB per GPU, held until the process ends), so the call makes no
+ * hipMalloc, hipFree or other allocating call.  The array's device address
+ * is looked up once per device, on the first call with that device current.
+ *   limit    the rank range may hold at most 131072 work chunks: any range
+ *            of fewer than 256 coarse chunks, and up to about 8.6e9
+ *            elements with the default chunk size; a larger range returns
+ *            RS_ERR_INVALID_ARG before anything is enqueued
+ *   others   as rs_ragged_sqnorm (x, sq, partial, found_inf, k0, k1, stream)
+ * Every call on one GPU shares that GPU's array, and a call overwrites the
+ * partials it reads before reading them (nothing needs clearing): calls that
+ * overlap in time on one GPU race, so order them on one stream. */
+rs_status rs_ragged_sqnorm_noalloc(const rs_layout* layout, const float* x, double* sq,
+                                   double* partial, uint32_t* found_inf, int32_t k0, int32_t k1,
+                                   void* stream);
+
 /* rs_block_quant - absmax block quantisation of every tile of every
  * quantised tensor that lies in [k0*S, k1*S).  Tiles never cross a shard
  * boundary (rs_layout_create rejects such layouts), so each rank quantises
