@@ -229,7 +229,7 @@ def tile_bounds(spec, local: int) -> Tuple[int, int, int, int]:
 
 def block_quant(x: np.ndarray, specs, offsets: Sequence[int], S: int, m: int, fmt: str,
                 k0: int, k1: int, codes: np.ndarray, scales: np.ndarray,
-                only_tiles=None) -> Tuple[np.ndarray, np.ndarray]:
+                only_tiles=None, inplace: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """Quantise every tile of every quantised tensor that lies in ranks [k0, k1).
 
     codes: uint8 array parallel to the buffer (codes[p] encodes buffer
@@ -238,9 +238,11 @@ def block_quant(x: np.ndarray, specs, offsets: Sequence[int], S: int, m: int, fm
     Positions and scales of other tiles are kept.  Every tile must lie inside
     one rank; an exception is raised otherwise.  only_tiles, when given, is a
     collection of global tile indices to compute (a sample of a large group).
+    With inplace, codes and scales themselves are written and returned.
     """
-    codes = codes.copy()
-    scales = scales.copy()
+    if not inplace:
+        codes = codes.copy()
+        scales = scales.copy()
     wanted = None if only_tiles is None else set(int(i) for i in only_tiles)
     base = 0
     for spec, l in zip(specs, offsets):
@@ -285,16 +287,18 @@ def decode_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
 
 def block_dequant(codes: np.ndarray, scales: np.ndarray, specs, offsets: Sequence[int], S: int,
                   m: int, fmt: str, k0: int, k1: int, y: np.ndarray, y_dtype: str,
-                  only_tiles=None) -> np.ndarray:
+                  only_tiles=None, inplace: bool = False) -> np.ndarray:
     """Inverse of block_quant: y[p] = fl32(decode(codes[p]) * scale) for every
     element of every quantised tile in ranks [k0, k1); y holds fp32 values
     ("f32") or bf16 bit patterns ("bf16", the fp32 product rounded to
-    nearest even).  Other positions of y are kept.
+    nearest even).  Other positions of y are kept; with inplace, y itself is
+    written and returned.
 
     This is the dequantisation step of an 8-bit optimizer's state
     (veScale-FSDP: Flexible and High-Performance FSDP at Scale, section 6.3).
     """
-    y = y.copy()
+    if not inplace:
+        y = y.copy()
     wanted = None if only_tiles is None else set(int(i) for i in only_tiles)
     base = 0
     for spec, l in zip(specs, offsets):

@@ -105,7 +105,7 @@ def sgd_step(p, g, b, items: Sequence[Item], offsets, S, m_ranks, k0, k1, lr, mo
 
 
 def adamw8_step(p, g, m_codes, m_scales, v_codes, v_scales, specs, offsets, S, m_ranks, k0, k1,
-                fmt: str, hp: dict, found_inf=None, only_tiles=None):
+                fmt: str, hp: dict, found_inf=None, only_tiles=None, inplace: bool = False):
     """AdamW with block-quantised moments (8-bit Adam, veScale-FSDP section
     6.3): for every tile of every quantised tensor in ranks [k0, k1):
 
@@ -114,13 +114,15 @@ def adamw8_step(p, g, m_codes, m_scales, v_codes, v_scales, specs, offsets, S, m
         m codes, m scale = block_quant(m');  v codes, v scale = block_quant(v')
 
     Non-quantised tensors are not touched (their fp32 moments are stepped
-    with adamw_step).  Returns new (p, m_codes, m_scales, v_codes, v_scales).
+    with adamw_step).  Returns new (p, m_codes, m_scales, v_codes, v_scales),
+    or the given arrays, written, with inplace.
     """
     from . import ops as O
 
-    p = p.copy()
-    m_codes, v_codes = m_codes.copy(), v_codes.copy()
-    m_scales, v_scales = m_scales.copy(), v_scales.copy()
+    if not inplace:
+        p = p.copy()
+        m_codes, v_codes = m_codes.copy(), v_codes.copy()
+        m_scales, v_scales = m_scales.copy(), v_scales.copy()
     if _skip(found_inf):
         return p, m_codes, m_scales, v_codes, v_scales
     k = adamw_constants(**hp)
