@@ -1,11 +1,20 @@
 """GPU parity at the full sizes of the four large groups, in the launch
 configuration bench.py times (align 16, default chunks, the whole rank
-range).  Whole-buffer outputs are compared with the oracle run rank by rank;
-quantisation is compared on a sample of tiles (every tile of the 8B layer)
-that includes the first and last tile of each tensor and every tile holding
-an injected non-finite value.
+range).  Whole-buffer outputs are compared with the oracle run rank by rank.
+
+The tile operations (quantisation, dequantisation, 8-bit AdamW) are compared
+on every tile of every group, fragment by fragment (one quantised tensor's
+tiles inside one rank), with digests of the oracle's outputs written by
+tests/golden/make_fullsize_digests.py, which runs only the oracle; a
+fragment whose digest differs is recomputed here by the oracle to name the
+first differing element.  The one exception is the mixed group's embedding
+(4.1M one-row tiles): it is compared with the oracle on a sample of tiles
+(random ones, the first and last of every rank, and tiles holding injected
+non-finite values).
 """
 import gc
+import json
+import os
 
 import numpy as np
 import pytest
@@ -14,11 +23,13 @@ import workloads as W
 from oracle import ops as O
 from oracle import plan as P
 
+import fullsize_cases as FC
 from harness import assert_bits_equal, assert_f32_equal_nan_class, log, to_np
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["llama3_8b_layer", "moe_experts", "llama70b_layer", "ragged_mixed"]
+FULL = list(FC.GROUPS)
+DIGESTS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fullsize_digests.json")
 
 
 class Full:
@@ -200,79 +211,117 @@ def test_full_sgd(fx):
     del p, g, b
 
 
-def _tile_sample(fx, rng, n_random):
-    specs = fx.w.tensors
-    nt = O.num_tiles(specs)
-    pick = set(int(i) for i in rng.choice(nt, size=min(n_random, nt), replace=False))
-    base = 0
-    starts = []
-    for s, l in zip(specs, fx.offsets):
+def _digests(fx):
+    """The oracle's digests for this group; the layout must be the one they
+    were computed on."""
+    d = json.load(open(DIGESTS))[fx.w.name]
+    assert d["S"] == fx.S and d["offsets"] == list(fx.offsets), "digests are for another layout"
+    assert d["num_tiles"] == fx.lay.info["num_tiles"]
+    return d
+
+
+def _embedding_sample(fx, rng, n_random, ranks=None):
+    """Global tile indices of a sample of each tensor with more than
+    FC.SAMPLE_ABOVE tiles: n_random random tiles, the first and last tile of
+    every rank, and up to 200 tiles holding injected non-finite values
+    (restricted to `ranks` when given)."""
+    out, base = [], 0
+    flat_starts = np.cumsum([0] + [s.numel for s in fx.w.tensors])
+    bad = fx.inp.nonfinite_positions
+    for t, (s, l) in enumerate(zip(fx.w.tensors, fx.offsets)):
         if not s.q_rows:
             continue
-        ntr, ntc = O.tile_counts(s)
-        pick.update((base, base + ntr * ntc - 1))
-        starts.append((base, s, l))
-        base += ntr * ntc
-    # tiles holding injected non-finite grads
-    if fx.inp.nonfinite_positions.size:
-        flat_starts = np.cumsum([0] + [s.numel for s in specs])
-        tbase = {}
-        b = 0
-        for s in specs:
-            if s.q_rows:
-                tbase[s.name] = b
-                ntr, ntc = O.tile_counts(s)
-                b += ntr * ntc
-        for p in rng.choice(fx.inp.nonfinite_positions, size=200, replace=False):
-            t = int(np.searchsorted(flat_starts, p, side="right") - 1)
-            s = specs[t]
-            if not s.q_rows:
-                continue
-            e = int(p - flat_starts[t])
-            r, c = divmod(e, s.cols)
-            _, ntc = O.tile_counts(s)
-            pick.add(tbase[s.name] + (r // s.q_rows) * ntc + c // s.q_cols)
-    return sorted(pick)
+        rk = FC.tile_ranks(s, l, fx.S)
+        if rk.size > FC.SAMPLE_ABOVE:
+            keep = np.ones(rk.size, bool) if ranks is None else np.isin(rk, ranks)
+            idx = np.flatnonzero(keep)
+            pick = set(int(i) for i in rng.choice(idx, size=min(n_random, idx.size), replace=False))
+            for k in np.unique(rk[keep]):
+                on = np.flatnonzero(rk == k)
+                pick.update((int(on[0]), int(on[-1])))
+            mine = bad[(bad >= flat_starts[t]) & (bad < flat_starts[t + 1])] - flat_starts[t]
+            if mine.size:
+                r, c = np.divmod(mine, s.cols)
+                _, ntc = O.tile_counts(s)
+                ti = (r // s.q_rows) * ntc + c // s.q_cols
+                ti = ti[keep[ti]]
+                pick.update(int(i) for i in rng.choice(ti, size=min(200, ti.size), replace=False))
+            out.append(base + np.array(sorted(pick), np.int64))
+        base += rk.size
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
 
 
-@pytest.mark.timeout(600)
+def _compare_fragments(fx, frags, got, expected, oracle_frag, what):
+    """Digest of each fragment's device outputs against the oracle's; on a
+    difference, the oracle recomputes that fragment (oracle_frag(frag) ->
+    list of (device array, expected array, name)) to report the element."""
+    bad = [f for f, e in zip(frags, expected) if got(f) != e]
+    if bad:
+        t, k, lo, hi, a, b = bad[0]
+        for dev, exp, name in oracle_frag(bad[0]):
+            if exp.dtype == np.float32:
+                assert_f32_equal_nan_class(dev, exp, f"{what}: tensor {t} rank {k} {name}")
+            else:
+                assert_bits_equal(dev, exp, f"{what}: tensor {t} rank {k} {name}")
+        raise AssertionError(f"{what}: {len(bad)} fragments differ from the oracle's digests, "
+                             f"first tensor {t} rank {k}, yet its outputs match on recomputation")
+
+
+@pytest.mark.timeout(900)
 def test_full_block_quant(fx):
+    """Quantisation of the params and the grads buffers over the whole range
+    and dequantisation of the device's codes, every fragment against the
+    oracle's digests (the embedding against the oracle on a tile sample)."""
     import torch
     R = fx.R
+    dig = _digests(fx)
+    frags = [tuple(f) for f in dig["frags"]]
     rng = np.random.default_rng(23)
     fmt = fx.w.qfmt
+    qf = R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8
     nt = fx.lay.info["num_tiles"]
+    sample = _embedding_sample(fx, rng, 3000)
+    spos = _tile_positions(fx, list(sample)) if sample.size else np.zeros(0, np.int64)
+    quantised = np.zeros(fx.total, bool)
+    for s, l in zip(fx.w.tensors, fx.offsets):
+        if s.q_rows:
+            quantised[l:l + s.numel] = True
     for src, host in (("params", fx.param_host), ("grads", fx.grad_host)):
-        log(f"full quant {fx.w.name} {src}")
+        log(f"full quant {fx.w.name} {src}: {len(frags)} fragments, {sample.size} sampled tiles")
         x = torch.from_numpy(host).cuda()
         codes = torch.full((fx.total,), 0xAB, dtype=torch.uint8, device="cuda")
         scales = torch.empty(nt, dtype=torch.float32, device="cuda")
-        R.rs_block_quant(fx.lay.handle, x, R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8,
-                         codes, scales, 0, fx.m)
-        _sync()
-        tiles = list(range(nt)) if nt <= 20000 else _tile_sample(fx, rng, 3000)
-        ecodes, escales = O.block_quant(host, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, 0, fx.m,
-                                        np.zeros(fx.total, np.uint8), np.zeros(nt, np.float32),
-                                        only_tiles=tiles)
-        gc_, gs = to_np(codes), to_np(scales)
-        assert_bits_equal(gs[tiles], escales[tiles], f"full quant {fx.w.name} {src} scales")
-        pos = _tile_positions(fx, tiles)
-        assert_bits_equal(gc_[pos], ecodes[pos], f"full quant {fx.w.name} {src} codes")
-        # padding and non-quantised positions keep the canary
-        quantised = np.zeros(fx.total, bool)
-        for s, l in zip(fx.w.tensors, fx.offsets):
-            if s.q_rows:
-                quantised[l:l + s.numel] = True
-        assert np.all(gc_[~quantised] == 0xAB)
-        # dequantise the device codes back to fp32 and check the same tiles
+        R.rs_block_quant(fx.lay.handle, x, qf, codes, scales, 0, fx.m)
         y = torch.full((fx.total,), float("nan"), dtype=torch.float32, device="cuda")
-        R.rs_block_dequant(fx.lay.handle, codes, R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8,
-                           scales, y, R.RS_F32, 0, fx.m)
+        R.rs_block_dequant(fx.lay.handle, codes, qf, scales, y, R.RS_F32, 0, fx.m)
         _sync()
-        ey = O.block_dequant(gc_, gs, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, 0, fx.m,
-                             np.zeros(fx.total, np.float32), "f32", only_tiles=tiles)
-        assert_f32_equal_nan_class(to_np(y)[pos], ey[pos], f"full dequant {fx.w.name} {src}")
-        del x, codes, y
+        gc_, gs, gy = to_np(codes), to_np(scales), to_np(y)
+
+        def oracle_frag(f, host=host):
+            t, k, lo, hi, a, b = f
+            ec, es = np.zeros(fx.total, np.uint8), np.zeros(nt, np.float32)
+            O.block_quant(host, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, k, k + 1, ec, es,
+                          only_tiles=range(a, b), inplace=True)
+            ey = O.block_dequant(ec, es, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, k, k + 1,
+                                 np.zeros(fx.total, np.float32), "f32", only_tiles=range(a, b))
+            return [(gc_[lo:hi], ec[lo:hi], "codes"), (gs[a:b], es[a:b], "scales"),
+                    (gy[lo:hi], ey[lo:hi], "dequant")]
+
+        _compare_fragments(fx, frags, lambda f: FC.digest(gc_[f[2]:f[3]], gs[f[4]:f[5]], gy[f[2]:f[3]]),
+                           dig["quant_" + src], oracle_frag, f"full quant {fx.w.name} {src}")
+        if sample.size:
+            ec, es = np.zeros(fx.total, np.uint8), np.zeros(nt, np.float32)
+            O.block_quant(host, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, 0, fx.m, ec, es,
+                          only_tiles=sample, inplace=True)
+            assert_bits_equal(gs[sample], es[sample], f"full quant {fx.w.name} {src} sampled scales")
+            assert_bits_equal(gc_[spos], ec[spos], f"full quant {fx.w.name} {src} sampled codes")
+            ey = O.block_dequant(gc_, gs, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, 0, fx.m,
+                                 np.zeros(fx.total, np.float32), "f32", only_tiles=sample)
+            assert_f32_equal_nan_class(gy[spos], ey[spos], f"full dequant {fx.w.name} {src} sampled")
+        # padding and non-quantised positions keep their canaries
+        assert np.all(gc_[~quantised] == 0xAB)
+        assert np.all(np.isnan(gy[~quantised]))
+        del x, codes, y, gc_, gy
 
 
 def _tile_positions(fx, tiles):
@@ -289,36 +338,23 @@ def _tile_positions(fx, tiles):
     return np.concatenate(pos)
 
 
-def _random_codes(rng, n, fmt, signed):
-    """Seeded valid codes: INT8 in [-127, 127] (or [0, 127]); E4M3FN without
-    the NaN codes (and without the sign bit when unsigned)."""
-    if fmt == "int8":
-        lo = -127 if signed else 0
-        return rng.integers(lo, 128, size=n, dtype=np.int16).astype(np.int8).view(np.uint8)
-    c = rng.integers(0, 0x7F, size=n, dtype=np.uint8)          # 0x00..0x7E
-    if signed:
-        c |= (rng.integers(0, 2, size=n, dtype=np.uint8) << 7)
-    return c
-
-
 @pytest.mark.timeout(900)
 def test_full_adamw8(fx):
-    """8-bit AdamW over the whole buffer in one launch; compared on sampled
-    tiles (every tile of the 8B layer), non-quantised elements untouched."""
+    """8-bit AdamW over the whole buffer in one launch, from the seeded
+    moment state of fullsize_cases; every fragment against the oracle's
+    digests (the embedding on a tile sample), non-quantised elements
+    untouched."""
     import torch
     from oracle import optim as OP
     R = fx.R
-    log(f"full adamw8 {fx.w.name}")
-    rng = np.random.default_rng(31)
+    dig = _digests(fx)
+    frags = [tuple(f) for f in dig["frags"]]
+    log(f"full adamw8 {fx.w.name}: {len(frags)} fragments")
+    rng = np.random.default_rng(37)
     fmt = fx.w.qfmt
     nt = fx.lay.info["num_tiles"]
-    qmax = 448.0 if fmt == "fp8_e4m3" else 127.0
-    mc0 = _random_codes(rng, fx.total, fmt, True)
-    vc0 = _random_codes(rng, fx.total, fmt, False)
-    ms0 = (np.abs(rng.standard_normal(nt)) * 1e-4 / qmax).astype(np.float32)
-    vs0 = (np.abs(rng.standard_normal(nt)) * 1e-6 / qmax).astype(np.float32)
-    hp = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1, bc1=1 - 0.9 ** 5,
-              bc2=1 - 0.95 ** 5, grad_scale=1.0)
+    hp = FC.ADAMW8_HP
+    mc0, vc0, ms0, vs0 = FC.adamw8_state(fx.total, nt, fmt)
     p = torch.from_numpy(fx.param_host).cuda()
     g = torch.from_numpy(fx.grad_host).cuda()
     mc, vc = torch.from_numpy(mc0).cuda(), torch.from_numpy(vc0).cuda()
@@ -327,40 +363,40 @@ def test_full_adamw8(fx):
     R.rs_adamw8_step(fx.lay.handle, p, g, mc, ms, vc, vs, qf, hp["lr"], hp["beta1"], hp["beta2"],
                      hp["eps"], hp["wd"], hp["bc1"], hp["bc2"], hp["grad_scale"], None, 0, fx.m)
     _sync()
-    tiles = list(range(nt)) if nt <= 20000 else _tile_sample(fx, rng, 2000)
-    ep, emc, ems, evc, evs = OP.adamw8_step(fx.param_host, fx.grad_host, mc0, ms0, vc0, vs0,
-                                            fx.w.tensors, fx.offsets, fx.S, fx.m, 0, fx.m, fmt, hp,
-                                            only_tiles=tiles)
-    pos = _tile_positions(fx, tiles)
+    gp, gmc, gvc, gms, gvs = to_np(p), to_np(mc), to_np(vc), to_np(ms), to_np(vs)
+
+    def oracle_frag(f):
+        t, k, lo, hi, a, b = f
+        ep, emc, ems, evc, evs = OP.adamw8_step(fx.param_host, fx.grad_host, mc0, ms0, vc0, vs0,
+                                                fx.w.tensors, fx.offsets, fx.S, fx.m, k, k + 1, fmt,
+                                                hp, only_tiles=range(a, b))
+        return [(gp[lo:hi], ep[lo:hi], "p"), (gmc[lo:hi], emc[lo:hi], "m codes"),
+                (gvc[lo:hi], evc[lo:hi], "v codes"), (gms[a:b], ems[a:b], "m scales"),
+                (gvs[a:b], evs[a:b], "v scales")]
+
     what = f"full adamw8 {fx.w.name}"
-    gp = to_np(p)
-    assert_f32_equal_nan_class(gp[pos], ep[pos], what + " p")
-    assert_bits_equal(to_np(mc)[pos], emc[pos], what + " m codes")
-    assert_bits_equal(to_np(vc)[pos], evc[pos], what + " v codes")
-    assert_bits_equal(to_np(ms)[tiles], ems[tiles], what + " m scales")
-    assert_bits_equal(to_np(vs)[tiles], evs[tiles], what + " v scales")
+    _compare_fragments(fx, frags, lambda f: FC.digest(gp[f[2]:f[3]], gmc[f[2]:f[3]], gvc[f[2]:f[3]],
+                                                      gms[f[4]:f[5]], gvs[f[4]:f[5]]),
+                       dig["adamw8"], oracle_frag, what)
+    sample = _embedding_sample(fx, rng, 2000)
+    if sample.size:
+        ep, emc, evc = fx.param_host.copy(), mc0.copy(), vc0.copy()
+        ems, evs = ms0.copy(), vs0.copy()
+        OP.adamw8_step(ep, fx.grad_host, emc, ems, evc, evs, fx.w.tensors, fx.offsets, fx.S, fx.m, 0,
+                       fx.m, fmt, hp, only_tiles=sample, inplace=True)
+        pos = _tile_positions(fx, list(sample))
+        assert_f32_equal_nan_class(gp[pos], ep[pos], what + " sampled p")
+        assert_bits_equal(gmc[pos], emc[pos], what + " sampled m codes")
+        assert_bits_equal(gvc[pos], evc[pos], what + " sampled v codes")
+        assert_bits_equal(gms[sample], ems[sample], what + " sampled m scales")
+        assert_bits_equal(gvs[sample], evs[sample], what + " sampled v scales")
     quantised = np.zeros(fx.total, bool)
     for s, l in zip(fx.w.tensors, fx.offsets):
         if s.q_rows:
             quantised[l:l + s.numel] = True
     assert np.array_equal(gp[~quantised].view(np.uint32), fx.param_host[~quantised].view(np.uint32))
-    assert np.array_equal(to_np(mc)[~quantised], mc0[~quantised])
+    assert np.array_equal(gmc[~quantised], mc0[~quantised])
     del p, g, mc, vc, ms, vs
-
-
-def _tiles_of_rank(fx, k):
-    """Global indices of the quantisation tiles whose elements lie in rank k."""
-    out, base = [], 0
-    for s, l in zip(fx.w.tensors, fx.offsets):
-        if not s.q_rows:
-            continue
-        ntr, ntc = O.tile_counts(s)
-        r0 = np.arange(ntr, dtype=np.int64) * s.q_rows
-        c0 = np.arange(ntc, dtype=np.int64) * s.q_cols
-        first = l + r0[:, None] * s.cols + c0[None, :]
-        out.append(base + np.flatnonzero((first // fx.S).reshape(-1) == k))
-        base += ntr * ntc
-    return np.concatenate(out) if out else np.zeros(0, np.int64)
 
 
 @pytest.mark.timeout(900)
@@ -369,8 +405,8 @@ def test_full_rank_shares(fx):
     bench's per-rank timing (range [k, k+1): fine chunks for the norms,
     four sub-blocks per wide quantisation tile where the rank has fewer than
     1024 work items): scale/add with found-inf, norms with partials,
-    quantisation and dequantisation for the first, a middle and the last
-    rank, against the oracle over that rank."""
+    quantisation and dequantisation (every tile, against the oracle's
+    digests) for the first, a middle and the last rank."""
     import torch
     R = fx.R
     rng = np.random.default_rng(29)
@@ -378,6 +414,7 @@ def test_full_rank_shares(fx):
     qf = R.RS_Q_FP8_E4M3 if fmt == "fp8_e4m3" else R.RS_Q_INT8
     nt = fx.lay.info["num_tiles"]
     n = len(fx.w.tensors)
+    dig = _digests(fx)
     for k in sorted({0, fx.m // 2, fx.m - 1}):
         log(f"full rank share {fx.w.name} rank {k}")
         lo, hi = k * fx.S, (k + 1) * fx.S
@@ -408,29 +445,44 @@ def test_full_rank_shares(fx):
             f = np.isfinite(esq)
             rel = np.abs(g_[f] - esq[f]) / np.maximum(np.abs(esq[f]), 1e-300)
             assert np.all(rel <= 1e-5), f"rank {k} {what}: {rel.max()}"
-        # quantisation and dequantisation of the rank's tiles (a sample on big groups)
-        tiles = _tiles_of_rank(fx, k)
-        if tiles.size:
-            if tiles.size > 3000:
-                tiles = np.sort(rng.choice(tiles, size=3000, replace=False))
-            codes = torch.full((fx.total,), 0xAB, dtype=torch.uint8, device="cuda")
-            scales = torch.full((nt,), -1.0, dtype=torch.float32, device="cuda")
-            R.rs_block_quant(fx.lay.handle, x, qf, codes, scales, k, k + 1)
-            _sync()
-            ec, es = O.block_quant(fx.grad_host, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, k, k + 1,
-                                   np.zeros(fx.total, np.uint8), np.zeros(nt, np.float32),
-                                   only_tiles=tiles)
-            gc_, gs = to_np(codes), to_np(scales)
-            assert_bits_equal(gs[tiles], es[tiles], f"rank {k} scales")
-            pos = _tile_positions(fx, list(tiles))
-            assert_bits_equal(gc_[pos], ec[pos], f"rank {k} codes")
-            assert np.all(gc_[:lo] == 0xAB) and np.all(gc_[hi:] == 0xAB)
-            yq = torch.full((fx.total,), float("nan"), dtype=torch.float32, device="cuda")
-            R.rs_block_dequant(fx.lay.handle, codes, qf, scales, yq, R.RS_F32, k, k + 1)
-            _sync()
-            eq = O.block_dequant(gc_, gs, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, k, k + 1,
-                                 np.zeros(fx.total, np.float32), "f32", only_tiles=list(tiles))
-            assert_f32_equal_nan_class(to_np(yq)[pos], eq[pos], f"rank {k} dequant")
-            assert np.all(np.isnan(to_np(yq)[:lo])) and np.all(np.isnan(to_np(yq)[hi:]))
-            del codes, scales, yq
+        # quantisation and dequantisation of every tile of the rank: each
+        # of its fragments against the oracle's digests of the grads'
+        # quantisation, the embedding on a tile sample
+        frags = [tuple(f) for f in dig["frags"] if f[1] == k]
+        exp = [e for f, e in zip(dig["frags"], dig["quant_grads"]) if f[1] == k]
+        sample = _embedding_sample(fx, rng, 3000, ranks=[k])
+        codes = torch.full((fx.total,), 0xAB, dtype=torch.uint8, device="cuda")
+        scales = torch.full((nt,), -1.0, dtype=torch.float32, device="cuda")
+        R.rs_block_quant(fx.lay.handle, x, qf, codes, scales, k, k + 1)
+        yq = torch.full((fx.total,), float("nan"), dtype=torch.float32, device="cuda")
+        R.rs_block_dequant(fx.lay.handle, codes, qf, scales, yq, R.RS_F32, k, k + 1)
+        _sync()
+        gc_, gs, gyq = to_np(codes), to_np(scales), to_np(yq)
+
+        def oracle_frag(f):
+            t, kk, flo, fhi, a, b = f
+            ec, es = np.zeros(fx.total, np.uint8), np.zeros(nt, np.float32)
+            O.block_quant(fx.grad_host, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, kk, kk + 1, ec, es,
+                          only_tiles=range(a, b), inplace=True)
+            ey = O.block_dequant(ec, es, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, kk, kk + 1,
+                                 np.zeros(fx.total, np.float32), "f32", only_tiles=range(a, b))
+            return [(gc_[flo:fhi], ec[flo:fhi], "codes"), (gs[a:b], es[a:b], "scales"),
+                    (gyq[flo:fhi], ey[flo:fhi], "dequant")]
+
+        _compare_fragments(fx, frags, lambda f: FC.digest(gc_[f[2]:f[3]], gs[f[4]:f[5]],
+                                                          gyq[f[2]:f[3]]),
+                           exp, oracle_frag, f"rank {k} quant")
+        if sample.size:
+            ec, es = np.zeros(fx.total, np.uint8), np.zeros(nt, np.float32)
+            O.block_quant(fx.grad_host, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, k, k + 1, ec, es,
+                          only_tiles=sample, inplace=True)
+            spos = _tile_positions(fx, list(sample))
+            assert_bits_equal(gs[sample], es[sample], f"rank {k} sampled scales")
+            assert_bits_equal(gc_[spos], ec[spos], f"rank {k} sampled codes")
+            ey = O.block_dequant(gc_, gs, fx.w.tensors, fx.offsets, fx.S, fx.m, fmt, k, k + 1,
+                                 np.zeros(fx.total, np.float32), "f32", only_tiles=sample)
+            assert_f32_equal_nan_class(gyq[spos], ey[spos], f"rank {k} sampled dequant")
+        assert np.all(gc_[:lo] == 0xAB) and np.all(gc_[hi:] == 0xAB)
+        assert np.all(np.isnan(gyq[:lo])) and np.all(np.isnan(gyq[hi:]))
+        del codes, scales, yq, gc_, gyq
         del y, x

@@ -355,3 +355,43 @@ def test_quant_tiles_match_hand_worked_values():
         scale, codes = O.quant_tile(np.array(t["x"], np.float32), t["fmt"])
         assert float(scale) == t["scale"], t["why"]
         assert [int(c) for c in codes.reshape(-1)] == [int(c, 16) for c in t["codes"]], t["why"]
+
+
+def test_fullsize_digests_reproduce_from_the_oracle():
+    """The stored digests of the full-size tile outputs are the oracle's:
+    the fragment holding the whole of the Llama-3-8B layer's Wk (rank 0),
+    quantised from the params and dequantised here by the oracle, matches
+    tests/golden/fullsize_digests.json as written by
+    tests/golden/make_fullsize_digests.py.  Only Wk's params are drawn: each
+    tensor's params come from its own child of the root seed, in tensor
+    order, so the group cut after Wk draws the same values for it."""
+    import json
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import fullsize_cases as FC
+    from oracle import plan as P
+
+    d = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                    "fullsize_digests.json")))["llama3_8b_layer"]
+    w = W.WORKLOADS["llama3_8b_layer"]
+    p = P.plan(P.items_from_specs(w.tensors), w.m, FC.ALIGN)
+    assert (p.S, p.offsets) == (d["S"], d["offsets"])
+    frags = [tuple(f) for f in d["frags"]]
+    assert frags == FC.fragments(w.tensors, p.offsets, p.S)
+    i = 1
+    t, k, lo, hi, a, b = frags[i]
+    assert (t, k, lo, hi) == (1, 0, p.offsets[1], p.offsets[1] + w.tensors[1].numel)
+    cut = W.Workload(w.name, w.tensors[:2], m=w.m, qfmt=w.qfmt, block=w.block)
+    wk = W.make_inputs(cut, grads=False).params[1]
+    total, nt = w.m * p.S, O.num_tiles(w.tensors)
+    # whole-buffer arrays whose untouched pages stay unallocated
+    x = np.zeros(total, np.float32)
+    x[lo:hi] = wk.reshape(-1)
+    codes, scales = np.zeros(total, np.uint8), np.zeros(nt, np.float32)
+    O.block_quant(x, w.tensors, p.offsets, p.S, w.m, w.qfmt, k, k + 1, codes, scales,
+                  only_tiles=range(a, b), inplace=True)
+    y = np.zeros(total, np.float32)
+    O.block_dequant(codes, scales, w.tensors, p.offsets, p.S, w.m, w.qfmt, k, k + 1, y, "f32",
+                    only_tiles=range(a, b), inplace=True)
+    assert FC.digest(codes[lo:hi], scales[a:b], y[lo:hi]) == d["quant_params"][i]
