@@ -16,6 +16,7 @@ import argparse
 import hashlib
 import json
 import os
+import ctypes
 import platform
 import sys
 import time
@@ -104,6 +105,24 @@ def read_counters(workload: str):
     return d.get("traffic_bytes_per_launch")
 
 
+def host_info():
+    """Host CPU model (from /proc/cpuinfo, no subprocess), logical CPUs and
+    the CPUs this process may run on."""
+    model = platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(w, offs, S, inp, k1, align, min_seconds=10.0):
     """The oracle, as it stands, on ranks [0, k1) of the same workload:
     whole passes of all six operations, repeated until min_seconds; and the
@@ -146,9 +165,12 @@ def cpu_baseline(w, offs, S, inp, k1, align, min_seconds=10.0):
     E_in = sum(max(0, min(l + it.numel, k1 * S) - l) for it, l in zip(items, offs))
     eq_in = sum(max(0, min(l + t.numel, k1 * S) - l) for t, l in zip(w.tensors, offs) if t.q_rows)
     b = (4 * E_in + 2 * k1 * S) + 4 * E_in + 12 * E_in + 4 * E_in + 5 * eq_in + 4 * k1 * S
+    hi = host_info()
     return {"value": round(b * passes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"ranks [0,{k1}) of {m} ({k1 * S} buffer positions): {passes} passes of all "
                       f"six operations in {dt:.1f} s, numpy on one host core",
+            "host_cpu": hi["cpu_model"], "host_cpus": hi["cpu_count"],
+            "host_usable_cpus": hi["usable_cpus"],
             "planner_ms": round(plan_s * 1e3, 2)}
 
 
@@ -204,140 +226,168 @@ def padding_study(align: int, out_path: str = "") -> None:
                 f.write(json.dumps(r) + "\n")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama3_8b_layer")
-    ap.add_argument("--align", type=int, default=16)
-    ap.add_argument("--chunk", type=int, default=0)
-    ap.add_argument("--samples", type=int, default=15)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-ranks", type=int, default=0)
-    ap.add_argument("--only", default="", help="comma list of ops to time per op (default all)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run a plain 1 GiB device copy (torch) to scale HBM counters")
-    ap.add_argument("--per-rank", action="store_true", default=True,
-                    help="also time each operation on one rank's shard, cycling over the ranks "
-                         "(default)")
-    ap.add_argument("--no-per-rank", dest="per_rank", action="store_false")
-    ap.add_argument("--no-torch-ref", action="store_true",
-                    help="skip timing torch's own copy/axpy/fill/fused optimizers for context")
-    ap.add_argument("--padding-study", action="store_true",
-                    help="planner-only padding study over granularity and FSDP size (no GPU)")
-    ap.add_argument("--study-out", default="", help="JSON lines of the padding study")
-    args = ap.parse_args()
-    if args.padding_study:
-        padding_study(args.align if "--align" in sys.argv else 1, args.study_out)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the m virtual ranks are slices of one device buffer "
-              "and this library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+# Practical HBM ceilings: plain 128-bit streaming kernels (include/hbm_ceiling.h)
+# for each read:write mix, and the mix each operation moves.
+CEILING_LIB = os.path.join(ROOT, "fsdp_sharded_buffer_amd", "libhbm_ceiling.so")
+CEILING_KINDS = {   # name: (kind, bytes per fp32 (or u8) element)
+    "read": (0, 4), "write": (1, 4), "copy": (2, 8), "axpby_inplace": (3, 12), "axpby": (4, 12),
+    "f32_to_bf16": (5, 6), "f32_to_u8": (6, 5), "u8_to_f32": (7, 5)}
+OP_MIX = {"pack": "f32_to_bf16", "unpack": "copy", "scale_add": "axpby_inplace", "sqnorm": "read",
+          "block_quant": "f32_to_u8", "zero": "write", "block_dequant": "u8_to_f32"}
 
-    import torch
 
-    import fsdp_sharded_buffer_amd as R
-    import workloads as W
-
-    w = W.WORKLOADS[args.workload]
-    log(f"bench: {w.name} m={w.m} elements={w.numel}")
-    offs, pinfo = R.rs_plan(w.tensors, w.m, args.align)
-    S = pinfo["S"]
-    lay = R.Layout(w.tensors, w.m, S, offs, args.chunk)
-    total = w.m * S
-    m = w.m
-    log(f"planned S={S} pad={pinfo['pad_frac']*100:.2f}% in {pinfo['seconds']*1e3:.1f} ms; "
-        f"chunks={lay.info['num_chunks']} tiles={lay.info['num_tiles']}")
-    inp = W.make_inputs(w)
-    log("inputs drawn")
-    dev = torch.device("cuda", 0)
-    params = [torch.from_numpy(a).to(dev) for a in inp.params]
-    pbuf = torch.empty(total, dtype=torch.bfloat16, device=dev)
-    outs = [torch.empty(t.numel, dtype=torch.bfloat16, device=dev) for t in w.tensors]
-    acc = torch.zeros(total, dtype=torch.float32, device=dev)
-    grad = torch.zeros(total, dtype=torch.float32, device=dev)
-    for g, l in zip(inp.grads, offs):
-        grad[l:l + g.size].copy_(torch.from_numpy(g.reshape(-1)))
-        acc[l:l + g.size].copy_(torch.from_numpy(g.reshape(-1)))
-    found = torch.zeros(m, dtype=torch.int32, device=dev)
-    sq = torch.empty(len(w.tensors), dtype=torch.float64, device=dev)
-    codes = torch.empty(total, dtype=torch.uint8, device=dev)
-    scales = torch.empty(lay.info["num_tiles"], dtype=torch.float32, device=dev)
-    ptab, otab = R.ptr_table(params), R.ptr_table(outs)
-    qfmt = R.RS_Q_FP8_E4M3 if w.qfmt == "fp8_e4m3" else R.RS_Q_INT8
-    h = lay.handle
-    stream = torch.cuda.current_stream(dev)
+def measure_ceilings(torch, dev, stream, event_ms, n=1 << 28):
+    """Best GB/s of each streaming kind over 1 GiB of fp32 (vectors per lane
+    1/2/4/8, with and without nontemporal hints), with the variant kept."""
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} is not built; run python -m fsdp_sharded_buffer_amd.build")
+    lib = ctypes.CDLL(CEILING_LIB)
+    lib.hc_stream.restype = ctypes.c_int
+    lib.hc_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                              ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    x = torch.empty(n, dtype=torch.float32, device=dev).normal_()
+    y = torch.empty_like(x).normal_()
+    z = torch.empty_like(x)
     sp = stream.cuda_stream
+    out = {}
+    for name, (kind, per) in CEILING_KINDS.items():
+        best = None
+        forms = (0, 16) if kind >= 5 else (0,)    # conversions: wide and narrow forms
+        for form in forms:
+            for vec in (1, 2, 4, 8):
+                for nt in (0, 1):
+                    def f(k=kind + form, vec=vec, nt=nt):
+                        if lib.hc_stream(k, x.data_ptr(), y.data_ptr(), z.data_ptr(), n, vec, nt, sp):
+                            raise RuntimeError("hc_stream failed")
+                    med, _, _ = event_ms(f, 5)
+                    gbs = per * n / (med * 1e-3) / 1e9
+                    if best is None or gbs > best["GB/s"]:
+                        best = {"GB/s": round(gbs, 1), "vec": vec, "nt": nt,
+                                "form": "narrow" if form else "wide"}
+        out[name] = best
+        log(f"ceiling {name:14s} {best['GB/s']:8.1f} GB/s ({best})")
+    del x, y, z
+    torch.cuda.empty_cache()
+    return out
 
-    # each operation over ranks [a, b)
-    ranged = {
-        "pack": lambda a, b: R.rs_pack(h, ptab, R.RS_F32, pbuf, R.RS_BF16, a, b, sp),
-        "unpack": lambda a, b: R.rs_unpack(h, pbuf, R.RS_BF16, otab, R.RS_BF16, a, b, sp),
-        "scale_add": lambda a, b: R.rs_group_scale_add(h, acc, grad, R.RS_F32, 1.0, 1.0, None,
-                                                       found, a, b, sp),
-        "sqnorm": lambda a, b: R.rs_ragged_sqnorm(h, acc, sq, None, None, lay.ws, a, b, sp),
-        "block_quant": lambda a, b: R.rs_block_quant(h, acc, qfmt, codes, scales, a, b, sp),
-        "zero": lambda a, b: R.rs_group_zero(h, grad, R.RS_F32, None, a, b, sp),
-    }
-    ops = {name: (lambda f=f: f(0, m)) for name, f in ranged.items()}
-    nbytes = op_bytes(w, S, lay.info["num_tiles"])
-    deq = torch.empty(total, dtype=torch.float32, device=dev)
-    mom = torch.zeros(total, dtype=torch.float32, device=dev)
-    codes2 = torch.zeros(total, dtype=torch.uint8, device=dev)
-    scales2 = torch.ones(lay.info["num_tiles"], dtype=torch.float32, device=dev)
-    var = torch.zeros(total, dtype=torch.float32, device=dev)
-    ranged_extra = {
-        "block_dequant": lambda a, b: R.rs_block_dequant(h, codes, qfmt, scales, deq, R.RS_F32, a, b,
-                                                         sp),
-        "adamw_step": lambda a, b: R.rs_adamw_step(h, deq, acc, mom, var, 1e-4, 0.9, 0.95, 1e-8,
-                                                   0.1, 0.5, 0.1, 1.0, None, None, a, b, sp),
-        "sgd_step": lambda a, b: R.rs_sgd_step(h, deq, acc, mom, 1e-4, 0.9, 0.0, False, 1.0, None,
-                                               None, a, b, sp),
-        "adamw8_step": lambda a, b: R.rs_adamw8_step(h, deq, acc, codes, scales, codes2, scales2,
-                                                     qfmt, 1e-4, 0.9, 0.95, 1e-8, 0.1, 0.5, 0.1,
-                                                     1.0, None, a, b, sp),
-    }
-    extra = {name: (lambda f=f: f(0, m)) for name, f in ranged_extra.items()}
-    xbytes = extra_bytes(w, S, lay.info["num_tiles"])
 
-    def step():
-        for f in ops.values():
-            f()
+class Group:
+    """One workload set up on the GPU: plan, layout, inputs and buffers, and
+    every operation as a closure over a rank range [a, b)."""
 
-    # whole-step throughput
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_step = dt / args.steps * 1e3
-    step_bytes = sum(nbytes.values())
-    value = step_bytes * args.steps / dt / 1e9
-    log(f"step: {ms_step:.3f} ms, {value:.1f} GB/s")
+    def __init__(self, name, align, chunk, dev, stream):
+        import torch
 
-    if args.calibrate_copy:
-        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings
-        # turn counter values into bytes
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        import fsdp_sharded_buffer_amd as R
+        import workloads as W
+        self.w = w = W.WORKLOADS[name]
+        log(f"bench: {w.name} m={w.m} elements={w.numel}")
+        self.offs, self.pinfo = R.rs_plan(w.tensors, w.m, align)
+        S = self.S = self.pinfo["S"]
+        self.lay = lay = R.Layout(w.tensors, w.m, S, self.offs, chunk)
+        total, m = w.m * S, w.m
+        log(f"planned S={S} pad={self.pinfo['pad_frac']*100:.2f}% in "
+            f"{self.pinfo['seconds']*1e3:.1f} ms; chunks={lay.info['num_chunks']} "
+            f"tiles={lay.info['num_tiles']}")
+        self.inp = inp = W.make_inputs(w)
+        log("inputs drawn")
+        params = [torch.from_numpy(a).to(dev) for a in inp.params]
+        pbuf = torch.empty(total, dtype=torch.bfloat16, device=dev)
+        outs = [torch.empty(t.numel, dtype=torch.bfloat16, device=dev) for t in w.tensors]
+        acc = torch.zeros(total, dtype=torch.float32, device=dev)
+        grad = torch.zeros(total, dtype=torch.float32, device=dev)
+        for g, l in zip(inp.grads, self.offs):
+            grad[l:l + g.size].copy_(torch.from_numpy(g.reshape(-1)))
+            acc[l:l + g.size].copy_(torch.from_numpy(g.reshape(-1)))
+        found = torch.zeros(m, dtype=torch.int32, device=dev)
+        sq = torch.empty(len(w.tensors), dtype=torch.float64, device=dev)
+        codes = torch.empty(total, dtype=torch.uint8, device=dev)
+        nt = lay.info["num_tiles"]
+        scales = torch.empty(nt, dtype=torch.float32, device=dev)
+        ptab, otab = R.ptr_table(params), R.ptr_table(outs)
+        qfmt = R.RS_Q_FP8_E4M3 if w.qfmt == "fp8_e4m3" else R.RS_Q_INT8
+        h, sp = lay.handle, stream.cuda_stream
+        deq = torch.empty(total, dtype=torch.float32, device=dev)
+        mom = torch.zeros(total, dtype=torch.float32, device=dev)
+        codes2 = torch.zeros(total, dtype=torch.uint8, device=dev)
+        scales2 = torch.ones(nt, dtype=torch.float32, device=dev)
+        var = torch.zeros(total, dtype=torch.float32, device=dev)
+        self.bufs = [params, pbuf, outs, acc, grad, found, sq, codes, scales, ptab, otab, deq, mom,
+                     codes2, scales2, var]
+        # the step's operations, then those measured beside it
+        self.ranged = {
+            "pack": lambda a, b: R.rs_pack(h, ptab, R.RS_F32, pbuf, R.RS_BF16, a, b, sp),
+            "unpack": lambda a, b: R.rs_unpack(h, pbuf, R.RS_BF16, otab, R.RS_BF16, a, b, sp),
+            "scale_add": lambda a, b: R.rs_group_scale_add(h, acc, grad, R.RS_F32, 1.0, 1.0, None,
+                                                           found, a, b, sp),
+            "sqnorm": lambda a, b: R.rs_ragged_sqnorm(h, acc, sq, None, None, lay.ws, a, b, sp),
+            "block_quant": lambda a, b: R.rs_block_quant(h, acc, qfmt, codes, scales, a, b, sp),
+            "zero": lambda a, b: R.rs_group_zero(h, grad, R.RS_F32, None, a, b, sp),
+        }
+        self.ranged_extra = {
+            "block_dequant": lambda a, b: R.rs_block_dequant(h, codes, qfmt, scales, deq, R.RS_F32,
+                                                             a, b, sp),
+            "adamw_step": lambda a, b: R.rs_adamw_step(h, deq, acc, mom, var, 1e-4, 0.9, 0.95, 1e-8,
+                                                       0.1, 0.5, 0.1, 1.0, None, None, a, b, sp),
+            "sgd_step": lambda a, b: R.rs_sgd_step(h, deq, acc, mom, 1e-4, 0.9, 0.0, False, 1.0,
+                                                   None, None, a, b, sp),
+            "adamw8_step": lambda a, b: R.rs_adamw8_step(h, deq, acc, codes, scales, codes2,
+                                                         scales2, qfmt, 1e-4, 0.9, 0.95, 1e-8, 0.1,
+                                                         0.5, 0.1, 1.0, None, a, b, sp),
+        }
+        self.nbytes = op_bytes(w, S, nt)
+        self.xbytes = extra_bytes(w, S, nt)
+        self.rb = rank_bytes(w, self.offs, S)
 
-    # per-operation launch time with HIP events on the launch stream
-    only = [o for o in args.only.split(",") if o] or (list(ops) + list(extra))
-    per_op, per_extra = {}, {}
-    allops = dict(ops, **extra)
-    allbytes = dict(nbytes, **xbytes)
+    @property
+    def m(self):
+        return self.w.m
+
+    def close(self):
+        self.lay.close()
+        self.bufs = self.ranged = self.ranged_extra = None
+
+
+def time_per_rank(g, names, event_ms, stream, samples):
+    """Each operation on one rank's shard: launches over [k, k+1), cycling k
+    so that each launch reads other memory than the last.  The mean comes
+    from whole cycles timed at their ends only; the slowest rank from a pass
+    with an event between launches (which adds the events' own cost)."""
+    import torch
+    m = g.m
+    allr = dict(g.ranged, **g.ranged_extra)
+    res = {}
+    for name in names:
+        f = allr[name]
+        cycle = lambda f=f: [f(k, k + 1) for k in range(m)]
+        med, _, _ = event_ms(cycle, samples)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(m + 1)]
+        times = [[] for _ in range(m)]
+        for _ in range(5):
+            ev[0].record(stream)
+            for k in range(m):
+                f(k, k + 1)
+                ev[k + 1].record(stream)
+            ev[m].synchronize()
+            for k in range(m):
+                times[k].append(ev[k].elapsed_time(ev[k + 1]))
+        each = np.array([np.median(t) for t in times])
+        worst = int(np.argmax(each))
+        byt = sum(g.rb[k][name] for k in range(m))
+        res[name] = {
+            "mean_us": round(med / m * 1e3, 2),
+            "GB/s": round(byt / (med * 1e-3) / 1e9, 1),
+            "slowest_rank": worst, "slowest_us_with_events": round(float(each[worst]) * 1e3, 2),
+            "slowest_GB/s_with_events": round(g.rb[worst][name] / (each[worst] * 1e-3) / 1e9, 1)}
+        log(f"per rank {g.w.name} {name:12s} mean {med / m * 1e3:8.1f} us  "
+            f"{res[name]['GB/s']:8.1f} GB/s; slowest rank {worst}")
+    return res
+
+
+def event_timer(torch, stream):
     def event_ms(f, n_samples):
-        """Median and minimum ms per call, HIP events on the launch stream,
-        each sample at least ~20 ms of back-to-back calls."""
+        """Median ms per call, HIP events on the launch stream, each sample
+        at least ~20 ms of back-to-back calls; also the samples and reps."""
         for _ in range(3):
             f()
         torch.cuda.synchronize()
@@ -357,65 +407,188 @@ def main():
             e1.synchronize()
             samples.append(e0.elapsed_time(e1) / reps)
         return float(np.median(samples)), samples, reps
+    return event_ms
 
-    for name in only:
+
+def time_whole(g, names, event_ms, samples):
+    """Median launch time of each operation over the whole buffer."""
+    allops = dict(g.ranged, **g.ranged_extra)
+    allbytes = dict(g.nbytes, **g.xbytes)
+    out = {}
+    for name in names:
         f = allops[name]
-        med, samples, reps = event_ms(f, args.samples)
-        p90 = float(np.percentile(samples, 90))
+        med, smp, reps = event_ms(lambda f=f: f(0, g.m), samples)
         gbs = allbytes[name] / (med * 1e-3) / 1e9
-        (per_op if name in ops else per_extra)[name] = {
-            "us": round(med * 1e3, 2), "min_us": round(min(samples) * 1e3, 2),
-            "p90_us": round(p90 * 1e3, 2),
-            "bytes": allbytes[name], "GB/s": round(gbs, 1),
-            "frac_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps}
-        log(f"{name:12s} {med*1e3:9.1f} us  {gbs:8.1f} GB/s  {gbs/HBM_PEAK_GBS*100:5.1f}% of peak")
+        out[name] = {"us": round(med * 1e3, 2), "min_us": round(min(smp) * 1e3, 2),
+                     "p90_us": round(float(np.percentile(smp, 90)) * 1e3, 2),
+                     "bytes": allbytes[name], "GB/s": round(gbs, 1),
+                     "frac_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps}
+        log(f"{g.w.name} {name:12s} {med*1e3:9.1f} us  {gbs:8.1f} GB/s  "
+            f"{gbs/HBM_PEAK_GBS*100:5.1f}% of peak")
+    return out
 
-    # one rank's shard: launches over [k, k+1), cycling k so that each
-    # launch reads other memory than the last.  The mean comes from whole
-    # cycles timed at their ends only; the slowest rank from a pass with an
-    # event between launches (which adds the events' own cost to it).
+
+def with_ceiling(res, ceil):
+    """Adds each operation's fraction of its read:write mix's ceiling."""
+    if ceil:
+        for name, r in res.items():
+            mix = OP_MIX.get(name)
+            if mix:
+                r["ceiling_mix"] = mix
+                r["frac_of_ceiling"] = round(r["GB/s"] / ceil[mix]["GB/s"], 4)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_layer")
+    ap.add_argument("--align", type=int, default=16)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--samples", type=int, default=15)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-ranks", type=int, default=0)
+    ap.add_argument("--only", default="", help="comma list of ops to time per op (default all)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (torch) to scale HBM counters")
+    ap.add_argument("--per-rank", action="store_true", default=True,
+                    help="also time each operation on one rank's shard, cycling over the ranks "
+                         "(default)")
+    ap.add_argument("--no-per-rank", dest="per_rank", action="store_false")
+    ap.add_argument("--per-rank-only", action="store_true",
+                    help="only the per-rank cycles (for tracing them): no step, no whole-buffer "
+                         "timings, no extras")
+    ap.add_argument("--no-torch-ref", action="store_true",
+                    help="skip timing torch's own copy/axpy/fill/fused optimizers for context")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the plain streaming kernels that give each mix's HBM ceiling")
+    ap.add_argument("--no-70b", action="store_true",
+                    help="skip the Llama-70B-layer measurements beside the default group")
+    ap.add_argument("--records", default="",
+                    help="write one JSON record per (group, operation, range) to this file")
+    ap.add_argument("--padding-study", action="store_true",
+                    help="planner-only padding study over granularity and FSDP size (no GPU)")
+    ap.add_argument("--study-out", default="", help="JSON lines of the padding study")
+    args = ap.parse_args()
+    if args.padding_study:
+        padding_study(args.align if "--align" in sys.argv else 1, args.study_out)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the m virtual ranks are slices of one device buffer "
+              "and this library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    event_ms = event_timer(torch, stream)
+    records = []
+
+    def record(group, op, rng, r, unit_key="GB/s"):
+        rec = {"group": group, "op": op, "range": rng}
+        rec.update({k: v for k, v in r.items()})
+        records.append(rec)
+
+    g = Group(args.workload, args.align, args.chunk, dev, stream)
+    w, m, S = g.w, g.m, g.S
+    step_names = list(g.ranged)
+    extra_names = list(g.ranged_extra)
+
+    value = ms_step = None
+    step_bytes = sum(g.nbytes.values())
+    per_op, per_extra = {}, {}
+    if not args.per_rank_only:
+        def step():
+            for f in g.ranged.values():
+                f(0, m)
+
+        # whole-step throughput: K steps between two synchronisations
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        ms_step = dt / args.steps * 1e3
+        value = step_bytes * args.steps / dt / 1e9
+        log(f"step: {ms_step:.3f} ms, {value:.1f} GB/s")
+
+        if args.calibrate_copy:
+            # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE
+            # readings turn counter values into bytes
+            a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+            b = torch.empty_like(a)
+            for _ in range(3):
+                b.copy_(a)
+            torch.cuda.synchronize()
+            del a, b
+
+        only = [o for o in args.only.split(",") if o] or (step_names + extra_names)
+        res = time_whole(g, only, event_ms, args.samples)
+        per_op = {k: v for k, v in res.items() if k in g.ranged}
+        per_extra = {k: v for k, v in res.items() if k in g.ranged_extra}
+
     per_rank = None
-    if args.per_rank:
-        rb = rank_bytes(w, offs, S)
-        per_rank = {}
-        for name, f in dict(ranged, **ranged_extra).items():
-            cycle = lambda f=f: [f(k, k + 1) for k in range(m)]
-            med, _, _ = event_ms(cycle, args.samples)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(m + 1)]
-            times = [[] for _ in range(m)]
-            for _ in range(5):
-                ev[0].record(stream)
-                for k in range(m):
-                    f(k, k + 1)
-                    ev[k + 1].record(stream)
-                ev[m].synchronize()
-                for k in range(m):
-                    times[k].append(ev[k].elapsed_time(ev[k + 1]))
-            each = np.array([np.median(t) for t in times])
-            worst = int(np.argmax(each))
-            byt = sum(rb[k][name] for k in range(m))
-            per_rank[name] = {
-                "mean_us": round(med / m * 1e3, 2),
-                "GB/s": round(byt / (med * 1e-3) / 1e9, 1),
-                "slowest_rank": worst, "slowest_us_with_events": round(float(each[worst]) * 1e3, 2)}
-            log(f"per rank {name:12s} mean {med / m * 1e3:8.1f} us  {per_rank[name]['GB/s']:8.1f} GB/s; "
-                f"slowest rank {worst}")
+    if args.per_rank or args.per_rank_only:
+        per_rank = time_per_rank(g, step_names + extra_names, event_ms, stream, args.samples)
 
+    ceil = None
+    if not args.no_ceiling and not args.per_rank_only:
+        ceil = measure_ceilings(torch, dev, stream, event_ms)
+    with_ceiling(per_op, ceil)
+    with_ceiling(per_extra, ceil)
+    for name, r in dict(per_op, **per_extra).items():
+        record(w.name, name, "all ranks", r)
+    for name, r in (per_rank or {}).items():
+        record(w.name, name, "one rank (cycled)", r)
+
+    roof = None
     timed = dict(per_op, **per_extra)
-    dom = "scale_add" if "scale_add" in timed else next(iter(timed))
-    # the dominant kernel as rocprofv3 names it (template argument 0: x in fp32)
-    roof = {"kernel": "scale_add_kernel<0>" if dom == "scale_add" else dom,
-            "bound": "hbm", "achieved": timed[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": timed[dom]["frac_peak"],
-            "traffic": read_counters(w.name) if dom == "scale_add" else None,
-            "bytes_per_launch": allbytes[dom], "avg_launch_us": timed[dom]["us"]}
+    if timed:
+        dom = "scale_add" if "scale_add" in timed else next(iter(timed))
+        allbytes = dict(g.nbytes, **g.xbytes)
+        # the dominant kernel as rocprofv3 names it (template argument 0: x in fp32)
+        roof = {"kernel": "scale_add_kernel<0>" if dom == "scale_add" else dom,
+                "bound": "hbm", "achieved": timed[dom]["GB/s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": timed[dom]["frac_peak"],
+                "traffic": read_counters(w.name) if dom == "scale_add" else None,
+                "bytes_per_launch": allbytes[dom], "avg_launch_us": timed[dom]["us"]}
+        if ceil and dom in OP_MIX:
+            c = ceil[OP_MIX[dom]]
+            roof["ceiling"] = {"kernel": f"hbm_ceiling {OP_MIX[dom]}", "GB/s": c["GB/s"],
+                               "frac": round(timed[dom]["GB/s"] / c["GB/s"], 4)}
+
+    # the Llama-70B layer beside the default group: one rank's share of every
+    # operation (the operating point of one of its 128 ranks) and the
+    # whole-buffer bf16 pack / unpack and FP8 quantisation
+    c70 = None
+    if args.workload == "llama3_8b_layer" and not args.no_70b and not args.per_rank_only:
+        keep_c2 = g
+        g = None
+        g5 = Group("llama70b_layer", args.align, args.chunk, dev, stream)
+        full = with_ceiling(time_whole(g5, ["pack", "unpack", "block_quant"], event_ms,
+                                       min(args.samples, 7)), ceil)
+        pr5 = time_per_rank(g5, step_names + extra_names, event_ms, stream, min(args.samples, 7))
+        for name, r in full.items():
+            record(g5.w.name, name, "all ranks", r)
+        for name, r in pr5.items():
+            record(g5.w.name, name, "one rank (cycled)", r)
+        c70 = {"workload": f"{g5.w.name}: {g5.w.description}", "elements": g5.w.numel,
+               "m": g5.m, "S": g5.S, "whole_buffer": full, "per_rank": pr5}
+        g5.close()
+        del g5
+        torch.cuda.empty_cache()
+        g = keep_c2
 
     # torch's own kernels on one contiguous tensor, same box, same timing:
     # context for the grouped kernels' rates (not a target)
     ref = None
-    if not args.no_torch_ref:
-        del deq, mom, var, codes2, scales2
-        torch.cuda.empty_cache()
+    if not args.no_torch_ref and not args.per_rank_only:
         n = 1 << 28
         a = torch.empty(n, dtype=torch.float32, device=dev).normal_()
         b = torch.empty_like(a).normal_()
@@ -456,33 +629,46 @@ def main():
         log(f"torch reference: {ref}")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.per_rank_only:
         k1 = args.cpu_ranks or m
         log(f"cpu baseline: oracle on ranks [0,{k1})")
-        cpu = cpu_baseline(w, offs, S, inp, k1, args.align)
+        cpu = cpu_baseline(w, g.offs, S, g.inp, k1, args.align)
         log(f"cpu baseline {cpu['value']} GB/s ({cpu['sample']})")
 
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": None if value is None else round(value, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None if ms_step is None else round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "elements": w.numel, "m": m, "S": S,
-                   "align": args.align, "chunk_elems": lay.info["chunk_elems"],
-                   "qfmt": w.qfmt, "step_bytes": step_bytes, "planner_ms": round(pinfo["seconds"] * 1e3, 3),
-                   "pad_frac": round(pinfo["pad_frac"], 5)},
-        "frac_peak": round(value / HBM_PEAK_GBS, 4),
+                   "align": args.align, "chunk_elems": g.lay.info["chunk_elems"],
+                   "qfmt": w.qfmt, "step_bytes": step_bytes,
+                   "planner_ms": round(g.pinfo["seconds"] * 1e3, 3),
+                   "pad_frac": round(g.pinfo["pad_frac"], 5)},
+        "frac_peak": None if value is None else round(value / HBM_PEAK_GBS, 4),
         "ops": per_op,
         "next_ops": per_extra,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "ceilings": ceil,
         "torch_reference": ref,
         "per_rank": per_rank,
+        "configs": {"llama70b_layer": c70} if c70 else None,
         "device": torch.cuda.get_device_name(0),
-        "host": platform.processor() or platform.machine(),
+        "host": host_info(),
     }
+    if args.records:
+        with open(args.records, "w") as f:
+            for r in records:
+                f.write(json.dumps(r) + "\n")
+    # release everything before the line is printed, so nothing of this
+    # process is left running once it has been read
+    g.close()
+    del g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
-    lay.close()
 
 
 if __name__ == "__main__":

@@ -56,6 +56,22 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+CEILING_SRC = os.path.join(CSRC, "hbm_ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "libhbm_ceiling.so")
+
+
+def build_ceiling(verbose: bool = True) -> str:
+    """Measurement-only streaming kernels (include/hbm_ceiling.h) that
+    bench.py times as the practical HBM ceiling of each read:write mix."""
+    tmp = CEILING_LIB + ".tmp"
+    subprocess.run([hipcc(), "-x", "hip"] + DEVICE + [CEILING_SRC, "-shared", "-fPIC", "-o", tmp]
+                   + COMMON, check=True)
+    os.replace(tmp, CEILING_LIB)
+    if verbose:
+        print(f"built {CEILING_LIB}")
+    return CEILING_LIB
+
+
 PROBE_SRC = os.path.join(ROOT, "tests", "native", "hw_probes.hip")
 PROBE_LIB = os.path.join(ROOT, "tests", "native", "libhw_probes.so")
 
@@ -89,6 +105,7 @@ def build_capi_demo(verbose: bool = True) -> str:
 
 if __name__ == "__main__":
     build()
+    build_ceiling()
     build_probe()
     build_capi_demo()
     sys.exit(0)
