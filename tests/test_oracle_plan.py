@@ -300,3 +300,100 @@ def test_s_star_closed_form_of_llama_layers(name, A):
     p = P.plan(items, w.m, A)
     assert p.S == cand
     _independent_check(items, p.offsets, p.S, w.m, A)
+
+
+def test_padding_fraction_hand_values():
+    """padding_fraction = (m*S - E)/E on values worked by hand: the toy unit
+    packs exactly (S = 98,304 = E/4, no padding), and the Llama-3-8B layer
+    at S = 29,360,128 on 8 ranks holds E = 2*4096^2 + 2*1024*4096 +
+    3*14336*4096 + 2*4096 = 218,112,000 elements in 234,881,024 positions,
+    16,769,024 of them padding."""
+    toy = P.items_from_specs(W.toy_unit().tensors)
+    assert P.padding_fraction(toy, 98_304, 4) == 0.0
+    c2 = P.items_from_specs(W.llama8b_layer().tensors)
+    assert sum(it.numel for it in c2) == 218_112_000
+    assert P.padding_fraction(c2, 29_360_128, 8) == 16_769_024 / 218_112_000
+    # one 10-element tensor on 3 ranks of 4: 2 of 12 positions are padding
+    assert P.padding_fraction([P.Item(10, 1)], 4, 3) == 0.2
+
+
+# ------------------------------------------------- S* by a plain scan
+#
+# An independent check of S* for the groups whose S* has no closed form:
+# offsets are found by testing the layout constraints on every aligned
+# candidate offset in turn (no granule or lcm jumps), and every aligned S from
+# ceil(E/m) up to the planner's S* is tried.  Greedy earliest placement is
+# exact for a fixed S (pinned by exhaustive search on tiny groups).
+
+
+def _plain_earliest(lo, E, g, S, m, A):
+    """Smallest aligned l >= lo with l + E <= m*S such that every shard
+    boundary strictly inside (l, l + E) is a whole number of granules after
+    l, found by testing the candidates lo, lo + A, ... in order."""
+    l0 = -(-lo // A) * A
+    end = m * S
+    W = 64
+    while l0 + E <= end:
+        cand = l0 + A * np.arange(W, dtype=np.int64)
+        cand = cand[cand + E <= end]
+        ok = np.ones(cand.size, bool)
+        for k in range(int(cand[0]) // S + 1, min(m - 1, (int(cand[-1]) + E - 1) // S) + 1):
+            b = k * S
+            inside = (cand < b) & (b < cand + E)
+            ok &= ~inside | ((b - cand) % g == 0)
+        hit = np.flatnonzero(ok)
+        if hit.size:
+            return int(cand[hit[0]])
+        l0 = int(cand[-1]) + A
+        W = min(W * 4, 1 << 16)
+    return None
+
+
+def _plain_greedy(items, m, S, A):
+    end, offs = 0, []
+    for it in items:
+        l = _plain_earliest(end, it.numel, it.granule, S, m, A)
+        if l is None:
+            return None
+        offs.append(l)
+        end = l + it.numel
+    return offs
+
+
+def _plain_scan_chunk(args):
+    name, A, lo, hi, step = args
+    items = P.items_from_specs(W.WORKLOADS[name].tensors)
+    m = W.WORKLOADS[name].m
+    return [S for S in range(lo, hi, step) if _plain_greedy(items, m, S, A) is not None]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["ragged_mixed", "moe_experts"])
+def test_s_star_of_mixed_and_expert_groups_by_plain_scan(name):
+    """S* of the ragged mixed group (44,040,192) and of the MoE expert unit
+    (34,734,080) at align 16: no aligned S from ceil(E/m) up to S* admits a
+    layout, and at S* the plain placement gives the planner's offsets.  For
+    the mixed group only multiples of 4096 are tried below S*: its
+    embedding (525,336,576 elements, granule 4096) is longer than 2S for
+    every S there, so it holds two boundaries S apart, each a whole number
+    of granules from its start, which forces S % 4096 == 0."""
+    import multiprocessing as mp
+    A = 16
+    w = W.WORKLOADS[name]
+    items = P.items_from_specs(w.tensors)
+    E = sum(it.numel for it in items)
+    lb = -(-(-(-E // w.m)) // A) * A
+    p = P.plan(items, w.m, A)
+    assert p.S == {"ragged_mixed": 44_040_192, "moe_experts": 34_734_080}[name]
+    assert _plain_greedy(items, w.m, p.S, A) == p.offsets
+    if name == "ragged_mixed":
+        emb = items[0]
+        assert emb.granule == 4096 and emb.numel > 2 * p.S
+        lo, step = -(-lb // 4096) * 4096, 4096
+    else:
+        lo, step = lb, A
+    bounds = list(range(lo, p.S, step * 256)) + [p.S]
+    jobs = [(name, A, a, b, step) for a, b in zip(bounds[:-1], bounds[1:])]
+    with mp.get_context("fork").Pool(min(8, os.cpu_count() or 1)) as pool:
+        feasible = [S for part in pool.map(_plain_scan_chunk, jobs) for S in part]
+    assert feasible == [], feasible[:5]
