@@ -73,8 +73,11 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //   RS_UNROLL        8-element vectors in flight per lane (copies, scale/add)
 //   RS_*_NT          per operation: nontemporal hint on streaming accesses;
 //                    it helps the pure streams (copies, the norm read,
-//                    quantisation input) and hurts read-modify-write
-//                    (scale/add, zero, the fp32 optimizers)
+//                    quantisation input) and the in-place ones (scale/add,
+//                    the fp32 optimizers), whose lanes take one 16-byte
+//                    vector each; it hurts the zero
+//   RS_SCALE_SPLIT   workgroups per chunk of scale/add (1024 elements each
+//                    at the default chunk size)
 //   RS_QUANT_F,      256-lane sub-blocks per quantisation work item of wide
 //   RS_QUANT_F_SMALL tiles, for launches of at least / fewer than
 //                    RS_QUANT_SMALL_ITEMS work items (narrow tiles: one)
@@ -82,6 +85,8 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    fewer coarse chunks than this (too few workgroups)
 //   RS_FILL_BYTES    bytes per workgroup of the unmasked zero: one 16-byte
 //                    store per lane, as many short workgroups write fastest
+//   RS_OPT_NT        nontemporal loads and stores of the streams the AdamW
+//                    / SGD steps read and write in place (p, m, v, momentum)
 //   RS_OPT_G_NT      nontemporal loads of the gradient (read once) in the
 //                    AdamW / SGD steps, beside their read-modify-write streams
 //   RS_ADAMW_SPLIT,  workgroups per chunk of the AdamW / SGD steps
@@ -103,7 +108,10 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #define RS_PACK_NT 1
 #endif
 #ifndef RS_SCALE_NT
-#define RS_SCALE_NT 0
+#define RS_SCALE_NT 1
+#endif
+#ifndef RS_SCALE_SPLIT
+#define RS_SCALE_SPLIT 2
 #endif
 #ifndef RS_SQNORM_NT
 #define RS_SQNORM_NT 1
@@ -132,8 +140,11 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #ifndef RS_OPT_G_NT
 #define RS_OPT_G_NT 1
 #endif
+#ifndef RS_OPT_NT
+#define RS_OPT_NT 1
+#endif
 #ifndef RS_ADAMW_SPLIT
-#define RS_ADAMW_SPLIT 4
+#define RS_ADAMW_SPLIT 8
 #endif
 #ifndef RS_SGD_SPLIT
 #define RS_SGD_SPLIT 4
@@ -338,6 +349,25 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const ChunkDesc* __res
 
 // -------------------------------------------------------------- scale/add
 
+// With SPLIT > 1 workgroup ii takes piece ii % SPLIT of chunk ii / SPLIT:
+// more, shorter workgroups (scale/add, the optimizer kernels).  Pieces
+// are whole multiples of 64 elements, so 16-byte alignment is kept.
+template <int SPLIT>
+__device__ __forceinline__ bool piece_of(const ChunkDesc& c, int q, int64_t& off, int& n) {
+  if (SPLIT == 1) {
+    off = c.buf_off;
+    n = c.len;
+    return true;
+  }
+  const int per = ((c.len + SPLIT - 1) / SPLIT + 63) & ~63;
+  const int lo = q * per;
+  if (lo >= c.len) return false;
+  off = c.buf_off + lo;
+  n = c.len - lo < per ? c.len - lo : per;
+  return true;
+}
+
+
 __device__ __forceinline__ float axpby(float a, float y, float b, float x) {
   // separate roundings: fl(fl(a*y) + fl(b*x)); contraction is off in this file
   const float u = a * y;
@@ -366,33 +396,39 @@ __device__ __forceinline__ void flag_rank(bool bad, uint32_t* found_inf, int ran
   if (found_inf && __any(bad) && (threadIdx.x % kWave) == 0) found_inf[rank] = 1u;
 }
 
-template <int XK>
+// y <- fl(fl(alpha*y) + fl(beta*x)) over n elements: one 16-byte vector of y
+// (and the matching 16 or 8 bytes of x) per lane per step, consecutive lanes
+// on consecutive vectors, so each load and store instruction of a wave covers
+// one contiguous 1 KB span.  x may be y: every element is loaded before it is
+// stored, by the same lane.
+template <int XK, bool NT>
 __device__ __forceinline__ void scale_add_run(float* yp, const char* xp, int n, float alpha,
                                               float beta, bool& bad) {
-  constexpr bool NT = RS_SCALE_NT;
-  const int nv = (aligned16(yp) && aligned16(xp)) ? n / 8 : 0;
-  for (int b = threadIdx.x; b < nv; b += kUnroll * kThreads) {
-    Pack8<0> ry[kUnroll];
-    Pack8<0> rx[kUnroll];
+  const bool vec = aligned16(yp) && (reinterpret_cast<uintptr_t>(xp) & (XK == 0 ? 15u : 7u)) == 0;
+  const int nv = vec ? n / 4 : 0;
+  for (int q0 = threadIdx.x; q0 < nv; q0 += kUnroll * kThreads) {
+    u32x4 Y[kUnroll], X[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = int64_t(b + u * kThreads) * 8;
-      if (b + u * kThreads < nv) {
-        ry[u] = ld8<0, NT>(yp, i);
-        rx[u] = Conv<XK, 0>::run(ld8<XK, NT>(xp, i));
+      const int q = q0 + u * kThreads;
+      if (q < nv) {
+        Y[u] = ld16<NT>(yp + 4 * q);
+        if constexpr (XK == 0) {
+          X[u] = ld16<NT>(xp + 16 * int64_t(q));
+        } else {
+          const u32x2* px = reinterpret_cast<const u32x2*>(xp) + q;
+          const u32x2 w = NT ? __builtin_nontemporal_load(px) : *px;
+          X[u] = u32x4{w.x << 16, w.x & 0xffff0000u, w.y << 16, w.y & 0xffff0000u};
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (b + u * kThreads < nv) {
-        Pack8<0> o;
-        o.a = axpby4(alpha, ry[u].a, beta, rx[u].a, bad);
-        o.b = axpby4(alpha, ry[u].b, beta, rx[u].b, bad);
-        st8<0, NT>(yp, int64_t(b + u * kThreads) * 8, o);
-      }
+      const int q = q0 + u * kThreads;
+      if (q < nv) st16<NT>(yp + 4 * q, axpby4(alpha, Y[u], beta, X[u], bad));
     }
   }
-  for (int i = nv * 8 + threadIdx.x; i < n; i += kThreads) {
+  for (int i = nv * 4 + threadIdx.x; i < n; i += kThreads) {
     float xv;
     if constexpr (XK == 0)
       xv = reinterpret_cast<const float*>(xp)[i];
@@ -408,13 +444,16 @@ template <int XK>
 __global__ __launch_bounds__(kThreads) void scale_add_kernel(
     const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* y, const void* x,
     float alpha, float beta, const uint8_t* __restrict__ mask, uint32_t* __restrict__ found_inf) {
-  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
-    const ChunkDesc c = chunks[c0 + i];
+  for (int64_t ii = blockIdx.x; ii < nc * RS_SCALE_SPLIT; ii += gridDim.x) {
+    const ChunkDesc c = chunks[c0 + ii / RS_SCALE_SPLIT];
     if (c.tensor < 0) continue;
     if (mask && !mask[c.tensor]) continue;
+    int64_t off;
+    int n;
+    if (!piece_of<RS_SCALE_SPLIT>(c, int(ii % RS_SCALE_SPLIT), off, n)) continue;
     bool bad = false;
-    scale_add_run<XK>(y + c.buf_off, static_cast<const char*>(x) + c.buf_off * esize<XK>(), c.len,
-                      alpha, beta, bad);
+    scale_add_run<XK, RS_SCALE_NT>(y + off, static_cast<const char*>(x) + off * esize<XK>(), n,
+                                   alpha, beta, bad);
     flag_rank(bad, found_inf, c.rank);
   }
 }
@@ -494,8 +533,8 @@ __global__ __launch_bounds__(kThreads) void sqnorm_partial_kernel(
     double acc = 0.0;
     bool bad = false;
     const int nv = aligned16(xp) ? n / 4 : 0;
-    int v = threadIdx.x;
     constexpr int U = 2 * kUnroll;
+    int v = threadIdx.x;
     for (; v + (U - 1) * kThreads < nv; v += U * kThreads) {
       u32x4 r[U];
 #pragma unroll
@@ -503,7 +542,17 @@ __global__ __launch_bounds__(kThreads) void sqnorm_partial_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u) sq4(r[u], acc, bad);
     }
-    for (; v < nv; v += kThreads) sq4(ld16<RS_SQNORM_NT>(xp + int64_t(v) * 4), acc, bad);
+    {
+      // the last (at most U - 1) vectors of the lane, loaded together before
+      // any is used: a short chunk's few loads per lane are in flight at once
+      u32x4 r[U - 1];
+#pragma unroll
+      for (int u = 0; u < U - 1; ++u)
+        if (v + u * kThreads < nv) r[u] = ld16<RS_SQNORM_NT>(xp + int64_t(v + u * kThreads) * 4);
+#pragma unroll
+      for (int u = 0; u < U - 1; ++u)
+        if (v + u * kThreads < nv) sq4(r[u], acc, bad);
+    }
     for (int i = nv * 4 + threadIdx.x; i < n; i += kThreads) {
       const uint32_t u = __float_as_uint(xp[i]);
       acc += sq(u);
@@ -551,6 +600,15 @@ __device__ __forceinline__ double frag_lane_sum(const double* __restrict__ part,
   return s;
 }
 
+// A range of one rank holding at most kDirectFrags fragments: the partial
+// index range of each (relative to c0), passed by value so the combine reads
+// no descriptor; fragment i belongs to tensor t_lo + i.
+constexpr int kDirectFrags = 32;
+struct DirectFrags {
+  int32_t nf;  // 0: read the descriptor tables instead
+  int32_t cb[kDirectFrags], ce[kDirectFrags];
+};
+
 // One workgroup per tensor present in the range (tensors [t_lo, t_hi) in
 // buffer order), plus, when some tensor is absent, one last workgroup that
 // writes the zeros of the absent tensors' sq and partial entries.  part[i]
@@ -558,7 +616,8 @@ __device__ __forceinline__ double frag_lane_sum(const double* __restrict__ part,
 __global__ __launch_bounds__(kCombineWaves* kWave) void sqnorm_combine_kernel(
     const TensorDesc* __restrict__ tensors, const FragDesc* __restrict__ frags,
     const double* __restrict__ part, int64_t c0, int32_t n, int32_t k0, int32_t k1, int32_t t_lo,
-    int32_t t_hi, double* __restrict__ sq_out, double* __restrict__ partial, int fine) {
+    int32_t t_hi, double* __restrict__ sq_out, double* __restrict__ partial, int fine,
+    DirectFrags direct) {
   __shared__ double fs[kCombineBatch];
   if (int(blockIdx.x) == t_hi - t_lo) {
     for (int t = threadIdx.x; t < n; t += blockDim.x)
@@ -574,9 +633,31 @@ __global__ __launch_bounds__(kCombineWaves* kWave) void sqnorm_combine_kernel(
     return;
   }
   const int t = t_lo + int(blockIdx.x);
-  const TensorDesc td = tensors[t];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  if (direct.nf > 0) {
+    // one rank, one fragment per tensor, the same fixed order as below
+    const int cb = direct.cb[blockIdx.x], ce = direct.ce[blockIdx.x];
+    double s = 0.0;
+    if (fine) {
+      const double w = frag_lane_sum(part, cb, ce, threadIdx.x, kCombineWaves * kWave);
+      if (lane == 0) fs[wave] = w;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        s = fs[0];
+        for (int i = 1; i < kCombineWaves; ++i) s += fs[i];
+      }
+    } else if (wave == 0) {
+      s = frag_lane_sum(part, cb, ce, lane, kWave);
+    }
+    if (threadIdx.x == 0) {
+      const double total = 0.0 + s;
+      sq_out[t] = total;
+      if (partial) partial[int64_t(k0) * n + t] = s;
+    }
+    return;
+  }
+  const TensorDesc td = tensors[t];
   double total = 0.0;
   if (fine) {
     for (int k = k0; k < k1; ++k) {
@@ -1078,24 +1159,6 @@ __device__ __forceinline__ void adamw1(float& p, float g, float& m, float& v, co
   v = v2;
 }
 
-// With SPLIT > 1 workgroup ii takes piece ii % SPLIT of chunk ii / SPLIT:
-// more, shorter workgroups for the many-stream optimizer kernels.  Pieces
-// are whole multiples of 64 elements, so 16-byte alignment is kept.
-template <int SPLIT>
-__device__ __forceinline__ bool piece_of(const ChunkDesc& c, int q, int64_t& off, int& n) {
-  if (SPLIT == 1) {
-    off = c.buf_off;
-    n = c.len;
-    return true;
-  }
-  const int per = ((c.len + SPLIT - 1) / SPLIT + 63) & ~63;
-  const int lo = q * per;
-  if (lo >= c.len) return false;
-  off = c.buf_off + lo;
-  n = c.len - lo < per ? c.len - lo : per;
-  return true;
-}
-
 template <int SPLIT>
 __global__ __launch_bounds__(kThreads) void adamw_kernel(
     const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* __restrict__ p,
@@ -1120,10 +1183,10 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(
       for (int u = 0; u < kUnroll; ++u) {
         const int q = q0 + u * kThreads;
         if (q < nv) {
-          P[u] = ld16<false>(pp + 4 * q);
+          P[u] = ld16<RS_OPT_NT>(pp + 4 * q);
           G[u] = ld16<RS_OPT_G_NT>(gp + 4 * q);
-          M[u] = ld16<false>(mp + 4 * q);
-          V[u] = ld16<false>(vp + 4 * q);
+          M[u] = ld16<RS_OPT_NT>(mp + 4 * q);
+          V[u] = ld16<RS_OPT_NT>(vp + 4 * q);
         }
       }
 #pragma unroll
@@ -1136,9 +1199,9 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(
           const float e[4] = {f32(G[u].x), f32(G[u].y), f32(G[u].z), f32(G[u].w)};
 #pragma unroll
           for (int j = 0; j < 4; ++j) adamw1(a[j], e[j], b[j], d[j], k);
-          st16<false>(pp + 4 * q, u32x4{u32(a[0]), u32(a[1]), u32(a[2]), u32(a[3])});
-          st16<false>(mp + 4 * q, u32x4{u32(b[0]), u32(b[1]), u32(b[2]), u32(b[3])});
-          st16<false>(vp + 4 * q, u32x4{u32(d[0]), u32(d[1]), u32(d[2]), u32(d[3])});
+          st16<RS_OPT_NT>(pp + 4 * q, u32x4{u32(a[0]), u32(a[1]), u32(a[2]), u32(a[3])});
+          st16<RS_OPT_NT>(mp + 4 * q, u32x4{u32(b[0]), u32(b[1]), u32(b[2]), u32(b[3])});
+          st16<RS_OPT_NT>(vp + 4 * q, u32x4{u32(d[0]), u32(d[1]), u32(d[2]), u32(d[3])});
         }
       }
     }
@@ -1188,9 +1251,9 @@ __global__ __launch_bounds__(kThreads) void sgd_kernel(
       for (int u = 0; u < kUnroll; ++u) {
         const int q = q0 + u * kThreads;
         if (q < nv) {
-          P[u] = ld16<false>(pp + 4 * q);
+          P[u] = ld16<RS_OPT_NT>(pp + 4 * q);
           G[u] = ld16<RS_OPT_G_NT>(gp + 4 * q);
-          B[u] = ld16<false>(bp + 4 * q);
+          B[u] = ld16<RS_OPT_NT>(bp + 4 * q);
         }
       }
 #pragma unroll
@@ -1202,8 +1265,8 @@ __global__ __launch_bounds__(kThreads) void sgd_kernel(
           const float e[4] = {f32(G[u].x), f32(G[u].y), f32(G[u].z), f32(G[u].w)};
 #pragma unroll
           for (int j = 0; j < 4; ++j) sgd1(a[j], e[j], b[j], k);
-          st16<false>(pp + 4 * q, u32x4{u32(a[0]), u32(a[1]), u32(a[2]), u32(a[3])});
-          st16<false>(bp + 4 * q, u32x4{u32(b[0]), u32(b[1]), u32(b[2]), u32(b[3])});
+          st16<RS_OPT_NT>(pp + 4 * q, u32x4{u32(a[0]), u32(a[1]), u32(a[2]), u32(a[3])});
+          st16<RS_OPT_NT>(bp + 4 * q, u32x4{u32(b[0]), u32(b[1]), u32(b[2]), u32(b[3])});
         }
       }
     }
@@ -1610,7 +1673,7 @@ extern "C" rs_status rs_group_scale_add(const rs_layout* L, float* y, const void
   if (nc == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
-  const dim3 g = chunk_grid(nc), b(kThreads);
+  const dim3 g = chunk_grid(nc * RS_SCALE_SPLIT), b(kThreads);
   if (x_dt == RS_F32)
     launch((scale_add_kernel<0>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
                        found_inf);
@@ -1690,9 +1753,18 @@ rs_status sqnorm_launch(const rs_layout* L, const float* x, double* sq_out, doub
   const int32_t t_lo = f1 > f0 ? L->frags[f0].tensor : 0;
   const int32_t t_hi = f1 > f0 ? L->frags[f1 - 1].tensor + 1 : 0;
   const unsigned groups = unsigned(t_hi - t_lo) + (t_hi - t_lo < L->n ? 1u : 0u);
+  DirectFrags direct{};
+  if (k1 - k0 == 1 && f1 - f0 <= kDirectFrags) {
+    direct.nf = int32_t(f1 - f0);
+    for (int64_t f = f0; f < f1; ++f) {
+      const FragDesc& fd = L->frags[f];
+      direct.cb[f - f0] = int32_t((fine ? fd.chunk_begin : fd.cchunk_begin) - c0);
+      direct.ce[f - f0] = int32_t((fine ? fd.chunk_end : fd.cchunk_end) - c0);
+    }
+  }
   launch(sqnorm_combine_kernel, dim3(groups), dim3(kCombineWaves * kWave), 0, s,
          table<TensorDesc>(L, L->off_tensors), table<FragDesc>(L, L->off_frags), part, c0, L->n,
-         k0, k1, t_lo, t_hi, sq_out, partial, fine);
+         k0, k1, t_lo, t_hi, sq_out, partial, fine, direct);
   return after_launch(fn);
 }
 

@@ -296,6 +296,36 @@ def test_sqnorm(name, src):
         assert np.array_equal(to_np(sq2).view(np.uint64), to_np(sq).view(np.uint64)), what + " rerun"
 
 
+@pytest.mark.parametrize("name", ["ragged_a1_c64", "mixed_div", "moe_div8", "llama70b_div32",
+                                  "pad_ranks", "tiny"])
+def test_sqnorm_one_rank_equals_wider_ranges(name):
+    """A one-rank call (its fragments' chunk ranges passed to the combine by
+    value) gives the same per-rank partials, bit for bit, as a call over all
+    ranks that reads the same (fine) chunk table, and its per-tensor sums
+    equal its partial row; padding-only ranks give zeros."""
+    import torch
+    c = case(name)
+    R = c.R
+    n = len(c.w.tensors)
+    if c.lay.info["num_coarse_chunks"] >= 256:
+        pytest.skip("the whole range would read coarse chunks")
+    x = from_np(c.flat(c.inputs().grads, fill=np.float32(1e30)))
+    pall = torch.full((c.m * n,), -1.0, dtype=torch.float64, device="cuda")
+    sq = torch.empty(n, dtype=torch.float64, device="cuda")
+    R.rs_ragged_sqnorm(c.lay.handle, x, sq, pall, None, c.lay.ws, 0, c.m)
+    _sync()
+    want = to_np(pall).reshape(c.m, n)
+    for k in range(c.m):
+        log(f"sqnorm one rank {name} [{k},{k + 1})")
+        p1 = torch.full((c.m * n,), -1.0, dtype=torch.float64, device="cuda")
+        sq1 = torch.full((n,), -1.0, dtype=torch.float64, device="cuda")
+        R.rs_ragged_sqnorm(c.lay.handle, x, sq1, p1, None, c.lay.ws, k, k + 1)
+        _sync()
+        row = to_np(p1).reshape(c.m, n)[k]
+        assert row.tobytes() == want[k].tobytes(), f"{name} rank {k} partial"
+        assert to_np(sq1).tobytes() == row.tobytes(), f"{name} rank {k} sq"
+
+
 def test_sqnorm_closed_forms():
     import torch
     c = case("ragged_a1_c64")
