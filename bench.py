@@ -236,36 +236,46 @@ OP_MIX = {"pack": "f32_to_bf16", "unpack": "copy", "scale_add": "axpby_inplace",
           "block_quant": "f32_to_u8", "zero": "write", "block_dequant": "u8_to_f32"}
 
 
-def measure_ceilings(torch, dev, stream, event_ms, n=1 << 28):
-    """Best GB/s of each streaming kind over 1 GiB of fp32 (vectors per lane
-    1/2/4/8, with and without nontemporal hints), with the variant kept."""
+def measure_ceilings(torch, dev, stream, event_ms, n=1 << 28, slices=1, vecs=(1, 2, 4, 8),
+                     kinds=None):
+    """Best GB/s of each streaming kind over n fp32 elements (vectors per
+    lane, nontemporal hints and, for conversions, wide and narrow forms
+    swept), with the variant kept.  With slices > 1, each timed call is one
+    launch per slice of n elements, in turn over `slices` consecutive slices:
+    one rank's share, cycled over the ranks as the per-rank launches are."""
     if not os.path.exists(CEILING_LIB):
         raise RuntimeError(f"{CEILING_LIB} is not built; run python -m fsdp_sharded_buffer_amd.build")
     lib = ctypes.CDLL(CEILING_LIB)
     lib.hc_stream.restype = ctypes.c_int
     lib.hc_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                               ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    x = torch.empty(n, dtype=torch.float32, device=dev).normal_()
+    n -= n % (4096 * max(vecs))
+    x = torch.empty(n * slices, dtype=torch.float32, device=dev).normal_()
     y = torch.empty_like(x).normal_()
     z = torch.empty_like(x)
     sp = stream.cuda_stream
     out = {}
     for name, (kind, per) in CEILING_KINDS.items():
+        if kinds and name not in kinds:
+            continue
         best = None
         forms = (0, 16) if kind >= 5 else (0,)    # conversions: wide and narrow forms
         for form in forms:
-            for vec in (1, 2, 4, 8):
+            for vec in vecs:
                 for nt in (0, 1):
                     def f(k=kind + form, vec=vec, nt=nt):
-                        if lib.hc_stream(k, x.data_ptr(), y.data_ptr(), z.data_ptr(), n, vec, nt, sp):
-                            raise RuntimeError("hc_stream failed")
+                        for j in range(slices):
+                            o = 4 * n * j
+                            if lib.hc_stream(k, x.data_ptr() + o, y.data_ptr() + o, z.data_ptr() + o,
+                                             n, vec, nt, sp):
+                                raise RuntimeError("hc_stream failed")
                     med, _, _ = event_ms(f, 5)
-                    gbs = per * n / (med * 1e-3) / 1e9
+                    gbs = per * n * slices / (med * 1e-3) / 1e9
                     if best is None or gbs > best["GB/s"]:
                         best = {"GB/s": round(gbs, 1), "vec": vec, "nt": nt,
                                 "form": "narrow" if form else "wide"}
         out[name] = best
-        log(f"ceiling {name:14s} {best['GB/s']:8.1f} GB/s ({best})")
+        log(f"ceiling {name:14s} {best['GB/s']:8.1f} GB/s ({best}, {slices} x {n} elements)")
     del x, y, z
     torch.cuda.empty_cache()
     return out
@@ -433,10 +443,18 @@ def with_ceiling(res, ceil):
     if ceil:
         for name, r in res.items():
             mix = OP_MIX.get(name)
-            if mix:
+            if mix and mix in ceil:
                 r["ceiling_mix"] = mix
                 r["frac_of_ceiling"] = round(r["GB/s"] / ceil[mix]["GB/s"], 4)
     return res
+
+
+def rank_ceilings(torch, dev, stream, event_ms, g):
+    """The streaming kinds the operations map to, timed on one rank's share
+    (S elements) cycled over the m rank slices: the practical ceiling at the
+    per-rank launch size, fixed launch costs included."""
+    return measure_ceilings(torch, dev, stream, event_ms, n=g.S, slices=g.m, vecs=(1, 2),
+                            kinds=set(OP_MIX.values()))
 
 
 def main():
@@ -536,6 +554,10 @@ def main():
     per_rank = None
     if args.per_rank or args.per_rank_only:
         per_rank = time_per_rank(g, step_names + extra_names, event_ms, stream, args.samples)
+        if not args.no_ceiling and not args.per_rank_only:
+            per_rank["ceilings_at_rank_size"] = rank_ceilings(torch, dev, stream, event_ms, g)
+            with_ceiling({k: v for k, v in per_rank.items() if k in OP_MIX},
+                         per_rank["ceilings_at_rank_size"])
 
     ceil = None
     if not args.no_ceiling and not args.per_rank_only:
@@ -545,7 +567,8 @@ def main():
     for name, r in dict(per_op, **per_extra).items():
         record(w.name, name, "all ranks", r)
     for name, r in (per_rank or {}).items():
-        record(w.name, name, "one rank (cycled)", r)
+        if name in OP_MIX or name in g.ranged_extra:
+            record(w.name, name, "one rank (cycled)", r)
 
     roof = None
     timed = dict(per_op, **per_extra)
@@ -574,10 +597,14 @@ def main():
         full = with_ceiling(time_whole(g5, ["pack", "unpack", "block_quant"], event_ms,
                                        min(args.samples, 7)), ceil)
         pr5 = time_per_rank(g5, step_names + extra_names, event_ms, stream, min(args.samples, 7))
+        if not args.no_ceiling:
+            pr5["ceilings_at_rank_size"] = rank_ceilings(torch, dev, stream, event_ms, g5)
+            with_ceiling({k: v for k, v in pr5.items() if k in OP_MIX}, pr5["ceilings_at_rank_size"])
         for name, r in full.items():
             record(g5.w.name, name, "all ranks", r)
         for name, r in pr5.items():
-            record(g5.w.name, name, "one rank (cycled)", r)
+            if name != "ceilings_at_rank_size":
+                record(g5.w.name, name, "one rank (cycled)", r)
         c70 = {"workload": f"{g5.w.name}: {g5.w.description}", "elements": g5.w.numel,
                "m": g5.m, "S": g5.S, "whole_buffer": full, "per_rank": pr5}
         g5.close()
