@@ -453,8 +453,12 @@ def rank_ceilings(torch, dev, stream, event_ms, g):
     """The streaming kinds the operations map to, timed on one rank's share
     (S elements) cycled over the m rank slices: the practical ceiling at the
     per-rank launch size, fixed launch costs included."""
-    return measure_ceilings(torch, dev, stream, event_ms, n=g.S, slices=g.m, vecs=(1, 2),
-                            kinds=set(OP_MIX.values()))
+    out = measure_ceilings(torch, dev, stream, event_ms, n=g.S, slices=g.m, vecs=(1, 2),
+                           kinds=set(OP_MIX.values()) - {"copy"})
+    # unpack moves bf16: a copy of S/2 fp32 elements moves the same bytes
+    out.update(measure_ceilings(torch, dev, stream, event_ms, n=g.S // 2, slices=g.m, vecs=(1, 2),
+                                kinds={"copy"}))
+    return out
 
 
 def main():

@@ -89,13 +89,16 @@ def _convert(seg: np.ndarray, to: str) -> np.ndarray:
 
 def unpack(buf: np.ndarray, shapes: Sequence[Tuple[int, int]], offsets: Sequence[int],
            S: int, m: int, dsts: Sequence[np.ndarray], dst_dtype: str,
-           k0: int, k1: int) -> List[np.ndarray]:
+           k0: int, k1: int, inplace: bool = False) -> List[np.ndarray]:
     """dst_t.flat[i] = cast(buf[l_t + i]) for positions in ranks [k0, k1);
-    other destination elements are kept."""
+    other destination elements are kept.  With inplace the destinations
+    (contiguous arrays) are written and returned as views."""
     out = []
     for (r, c), l, d in zip(shapes, offsets, dsts):
         n = r * c
-        dd = np.asarray(d).reshape(-1).copy()
+        dd = np.asarray(d).reshape(-1)
+        if not inplace:
+            dd = dd.copy()
         i0, i1 = _range_of(l, n, S, k0, k1)
         if i1 > i0:
             dd[i0:i1] = _convert(buf[l + i0:l + i1], dst_dtype)
@@ -133,10 +136,12 @@ def scale_add(y: np.ndarray, x: np.ndarray, alpha: float, beta: float,
 
 
 def zero(y: np.ndarray, items: Sequence[Item], offsets: Sequence[int], S: int, m: int,
-         k0: int, k1: int, mask: Optional[Sequence[int]] = None) -> np.ndarray:
+         k0: int, k1: int, mask: Optional[Sequence[int]] = None, inplace: bool = False
+         ) -> np.ndarray:
     """y <- +0 on the tensor elements of ranks [k0, k1) whose mask is set;
-    with no mask, on every position of those ranks including padding."""
-    out = y.copy()
+    with no mask, on every position of those ranks including padding.
+    Returns a new array (y itself when inplace)."""
+    out = y if inplace else y.copy()
     if mask is None:
         out[k0 * S:k1 * S] = 0
         return out

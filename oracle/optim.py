@@ -84,10 +84,11 @@ def adamw_step(p, g, m, v, items: Sequence[Item], offsets, S, m_ranks, k0, k1, h
 
 
 def sgd_step(p, g, b, items: Sequence[Item], offsets, S, m_ranks, k0, k1, lr, momentum, wd,
-             nesterov, grad_scale, mask=None, found_inf=None):
+             nesterov, grad_scale, mask=None, found_inf=None, inplace: bool = False):
     """SGD with momentum over the buffer's tensor elements in ranks [k0, k1).
-    Returns new (p, b)."""
-    p, b = p.copy(), b.copy()
+    Returns new (p, b) (the inputs themselves when inplace)."""
+    if not inplace:
+        p, b = p.copy(), b.copy()
     if _skip(found_inf):
         return p, b
     lr, mu, wd = F32(lr), F32(momentum), F32(wd)
