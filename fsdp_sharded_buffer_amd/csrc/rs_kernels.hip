@@ -21,6 +21,7 @@
 #include <utility>
 
 #include "rs_internal.h"
+#include "rs_divc.h"
 
 #pragma clang fp contract(off)
 
@@ -96,6 +97,8 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //   RS_DEQ_LDS       stage a tile's codes in LDS before decoding
 //   RS_ADAM8_F       256-lane sub-blocks per 8-bit Adam work item of wide tiles
 //   RS_ADAM8_BATCH   8-bit Adam slots loaded ahead of their arithmetic
+//   RS_ADAM8_DIVC    8-bit Adam divides by sqrt(bc2) with div_by_const when
+//                    the constant allows it
 //   RS_NT_STORE_BELOW  launches of quantisation, dequantisation and the
 //                    unmasked zero that write fewer bytes than this (one
 //                    rank's share, say) use nontemporal stores: a short
@@ -130,6 +133,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_QUANT_SMALL_ITEMS
 #define RS_QUANT_SMALL_ITEMS 1024
+#endif
+#ifndef RS_ADAM8_DIVC
+#define RS_ADAM8_DIVC 1
 #endif
 #ifndef RS_SQNORM_FINE_BELOW
 #define RS_SQNORM_FINE_BELOW 256
@@ -1137,6 +1143,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const QuantWork* __re
 
 struct AdamConst {
   float beta1, beta2, omb1, omb2, eps, decay, step, bc2s, inv;
+  float rbc2s;  // RN(1/bc2s), for div_by_const
 };
 
 // True (uniformly) when any of the m found-inf flags is set: the step is
@@ -1358,12 +1365,17 @@ struct TileScale {
   }
 };
 
+// The AdamW parameter update from m' and v'.  DIVC: sqrt(v') / bc2s through
+// div_by_const (the host checked bc2s), the same correctly rounded quotient
+// in three operations instead of the IEEE division sequence.
+template <bool DIVC>
 __device__ __forceinline__ float adam_p(float p, float m2, float v2, const AdamConst& k) {
-  const float den = sqrtf(v2) / k.bc2s + k.eps;
+  const float sq = sqrtf(v2);
+  const float den = (DIVC ? div_by_const(sq, k.bc2s, k.rbc2s) : sq / k.bc2s) + k.eps;
   return p * k.decay - k.step * (m2 / den);
 }
 
-template <int FMT, int F, int NS>
+template <int FMT, int F, int NS, bool DIVC>
 __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
     const QuantWork* __restrict__ work, int64_t w0, float* __restrict__ p, const float* __restrict__ g, uint8_t* __restrict__ mc,
     float* __restrict__ ms, uint8_t* __restrict__ vc, float* __restrict__ vs, AdamConst k,
@@ -1402,6 +1414,8 @@ __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         o[u] = sw.off;
+        G[u] = P[u] = u32x4{0u, 0u, 0u, 0u};
+        CM[u] = CV[u] = 0u;
         if (lane + (s0 + b + u) * team < nf) {
           const int64_t q = o0 + o[u];
           G[u] = ld16<RS_ADAM8_NT>(g + q);
@@ -1411,20 +1425,23 @@ __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
         }
         sw.next();
       }
+      // The arithmetic runs on every slot (zeros past the tile) and only the
+      // absmax and the store are predicated: M and V are then never merged
+      // across branches, which would copy the whole arrays once per slot.
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const int i = b + u;
-        if (lane + (s0 + i) * team < nf) {
-          moments4<FMT>(G[u], CM[u], CV[u], sm_old, sv_old, k, M[i], V[i]);
-          am = absmax4(M[i], am);
-          av = absmax4(V[i], av);
-          u32x4 out;
-          out.x = u32(adam_p(f32(P[u].x), M[i][0], V[i][0], k));
-          out.y = u32(adam_p(f32(P[u].y), M[i][1], V[i][1], k));
-          out.z = u32(adam_p(f32(P[u].z), M[i][2], V[i][2], k));
-          out.w = u32(adam_p(f32(P[u].w), M[i][3], V[i][3], k));
-          st16<RS_ADAM8_NT>(p + o0 + o[u], out);
-        }
+        const bool in = lane + (s0 + i) * team < nf;
+        moments4<FMT>(G[u], CM[u], CV[u], sm_old, sv_old, k, M[i], V[i]);
+        const uint32_t am2 = absmax4(M[i], am), av2 = absmax4(V[i], av);
+        am = in ? am2 : am;
+        av = in ? av2 : av;
+        u32x4 out;
+        out.x = u32(adam_p<DIVC>(f32(P[u].x), M[i][0], V[i][0], k));
+        out.y = u32(adam_p<DIVC>(f32(P[u].y), M[i][1], V[i][1], k));
+        out.z = u32(adam_p<DIVC>(f32(P[u].z), M[i][2], V[i][2], k));
+        out.w = u32(adam_p<DIVC>(f32(P[u].w), M[i][3], V[i][3], k));
+        if (in) st16<RS_ADAM8_NT>(p + o0 + o[u], out);
       }
     }
   } else {
@@ -1435,7 +1452,7 @@ __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
       moments4<FMT>(u32x4{u32(g[o]), 0u, 0u, 0u}, mc[o], vc[o], sm_old, sv_old, k, m1, v1);
       am = max(am, u32(m1[0]) & 0x7fffffffu);
       av = max(av, u32(v1[0]) & 0x7fffffffu);
-      p[o] = adam_p(p[o], m1[0], v1[0], k);
+      p[o] = adam_p<DIVC>(p[o], m1[0], v1[0], k);
     }
   }
   const int red = team < kWave ? team : kWave;
@@ -2004,6 +2021,8 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
   k.step = hp->lr / hp->bias_correction1;
   k.bc2s = std::sqrt(hp->bias_correction2);
   k.inv = 1.0f / hp->grad_scale;
+  k.rbc2s = 1.0f / k.bc2s;
+  const bool divc = RS_ADAM8_DIVC && div_by_const_ok(k.bc2s);
   const int vec_ok = (reinterpret_cast<uintptr_t>(p) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(g) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(m_codes) % 4 == 0 &&
@@ -2020,20 +2039,23 @@ extern "C" rs_status rs_adamw8_step(const rs_layout* L, float* p, const float* g
     const int64_t per = max_groups(kThreads * F);
     for (int64_t w1 = w0; w1 < w0 + nw; w1 += per) {  // one work item per workgroup
       const dim3 gr(static_cast<unsigned>(std::min(per, w0 + nw - w1)));
-#define RS_ADAM8_LAUNCH(FM)                                                                     \
+#define RS_ADAM8_LAUNCH(FM, DC)                                                                 \
   do {                                                                                          \
     if (c == 0)                                                                                 \
-      launch((adamw8_kernel<FM, 1, kNarrowSlots>), gr, b, 0, s, wk, w1, p, g,       \
-                         m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);     \
+      launch((adamw8_kernel<FM, 1, kNarrowSlots, DC>), gr, b, 0, s, wk, w1, p, g,               \
+             m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);                 \
     else                                                                                        \
-      launch((adamw8_kernel<FM, RS_ADAM8_F, kWideSlots / RS_ADAM8_F>), gr, b, 0, s, \
-                         wk, w1, p, g, m_codes, m_scales, v_codes, v_scales, k, found_inf,      \
-                         L->m, vec_ok);                                                         \
+      launch((adamw8_kernel<FM, RS_ADAM8_F, kWideSlots / RS_ADAM8_F, DC>), gr, b, 0, s, wk, w1, \
+             p, g, m_codes, m_scales, v_codes, v_scales, k, found_inf, L->m, vec_ok);           \
   } while (0)
-      if (fmt == RS_Q_FP8_E4M3)
-        RS_ADAM8_LAUNCH(RS_Q_FP8_E4M3);
+      if (fmt == RS_Q_FP8_E4M3 && divc)
+        RS_ADAM8_LAUNCH(RS_Q_FP8_E4M3, true);
+      else if (fmt == RS_Q_FP8_E4M3)
+        RS_ADAM8_LAUNCH(RS_Q_FP8_E4M3, false);
+      else if (divc)
+        RS_ADAM8_LAUNCH(RS_Q_INT8, true);
       else
-        RS_ADAM8_LAUNCH(RS_Q_INT8);
+        RS_ADAM8_LAUNCH(RS_Q_INT8, false);
 #undef RS_ADAM8_LAUNCH
       RS_TRY(after_launch(fn));
     }

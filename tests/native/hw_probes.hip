@@ -6,10 +6,14 @@
 //    of the fast path's domain with the CPU oracle;
 //  * fp32 division and square root as the kernels compile them (the exact
 //    quantisation path and the AdamW steps rely on both being correctly
-//    rounded).
+//    rounded);
+//  * the division by a per-call constant of the 8-bit AdamW step
+//    (rs_divc.h), on every input it can receive, against the IEEE quotient.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+
+#include "rs_divc.h"
 
 namespace {
 
@@ -34,7 +38,38 @@ __global__ void divsqrt_kernel(const float* x, const float* y, int64_t n, float*
   r[i] = sqrtf(x[i]);
 }
 
+// For every fp32 y with bits first + i, i < n: rs::div_by_const(sqrtf(y),
+// c, r) against the IEEE quotient sqrtf(y) / c.  Results whose bits differ
+// (NaN results compare by class) are counted in *bad and the smallest such
+// y pattern is kept in *first_bad.
+__global__ void divc_kernel(uint32_t first, int64_t n, float c, float r, unsigned long long* bad,
+                            uint32_t* first_bad) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint32_t bits = first + uint32_t(i);
+    const float x = sqrtf(__uint_as_float(bits));
+    const float a = rs::div_by_const(x, c, r);
+    const float q = x / c;
+    const bool same = (a != a && q != q) || __float_as_uint(a) == __float_as_uint(q);
+    if (!same) {
+      atomicAdd(bad, 1ull);
+      atomicMin(first_bad, bits);
+    }
+  }
+}
+
 }  // namespace
+
+// Counts, over the fp32 patterns [first, first + n) (n <= 2^32), the y
+// where the constant-divisor quotient of sqrtf(y) by c differs from IEEE's;
+// bad and first_bad are device words the caller set to 0 and 0xffffffff.
+extern "C" int probe_divc(uint32_t first, int64_t n, float c, float r, unsigned long long* bad,
+                          uint32_t* first_bad, void* stream) {
+  if (n <= 0 || n > (int64_t(1) << 32) || !bad || !first_bad) return -1;
+  hipLaunchKernelGGL(divc_kernel, dim3(8192), dim3(256), 0, static_cast<hipStream_t>(stream), first,
+                     n, c, r, bad, first_bad);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
 
 // q[i] = x[i] / y[i] and r[i] = sqrtf(x[i]) for i < n (device arrays).
 extern "C" int probe_div_sqrt(const float* x, const float* y, int64_t n, float* q, float* r,

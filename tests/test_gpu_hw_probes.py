@@ -103,3 +103,47 @@ def test_division_and_sqrt_are_correctly_rounded():
             assert np.array_equal(gn, en), what + ": NaN positions differ"
             bad = (got.view(np.uint32) != exp.view(np.uint32)) & ~gn
             assert not bad.any(), f"{what}: {int(bad.sum())} results differ, e.g. x={x[bad][0]!r}"
+
+
+def _divc_constants():
+    """sqrt(1 - beta2^t) in fp32, as a caller's bias correction gives it, for
+    common beta2 and steps; the ends of the accepted range; and seeded random
+    normals inside it."""
+    cs = []
+    for beta2 in (0.95, 0.98, 0.99, 0.995, 0.999, 0.9999):
+        for t in (1, 2, 3, 10, 100, 1000, 10 ** 4, 10 ** 5, 10 ** 6):
+            bc2 = np.float32(1) - np.float32(beta2) ** np.float32(t)
+            cs.append(np.sqrt(np.float32(bc2)).astype(np.float32))
+    cs += [np.float32(2.0 ** -16), np.float32(2.0 ** 16), np.float32(1.0)]
+    rng = np.random.default_rng(5)
+    cs += list((2.0 ** rng.uniform(-16, 16, 12)).astype(np.float32))
+    return sorted(set(float(c) for c in cs if np.float32(c) > 0))
+
+
+@pytest.mark.timeout(900)
+def test_division_by_a_constant_is_correctly_rounded():
+    """The 8-bit AdamW step divides sqrt(v') by the per-call constant
+    sqrt(bc2) with rs_divc.h's three-operation form.  For every fp32 v' (all
+    2^32 bit patterns: zeros, subnormals, normals, infinities and NaNs of
+    both signs) and each constant above, its quotient has the bits of the
+    IEEE quotient (NaN by class)."""
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib = ctypes.CDLL(LIB)
+    lib.probe_divc.restype = ctypes.c_int
+    lib.probe_divc.argtypes = [ctypes.c_uint32, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    for c in _divc_constants():
+        cf = np.float32(c)
+        r = np.float32(1) / cf                  # IEEE fp32 reciprocal, as the host computes it
+        bad = torch.zeros(1, dtype=torch.int64, device="cuda")
+        first = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        log(f"constant division: c = {float(cf)!r}")
+        assert lib.probe_divc(0, 1 << 32, float(cf), float(r), bad.data_ptr(), first.data_ptr(),
+                              stream) == 0
+        torch.cuda.synchronize()
+        nbad = int(bad.item())
+        assert nbad == 0, (f"c = {float(cf)!r}: {nbad} quotients differ, first at input "
+                           f"{int(first.item()) & 0xffffffff:#010x}")
