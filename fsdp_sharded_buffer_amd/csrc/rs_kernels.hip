@@ -21,7 +21,7 @@
 #include <utility>
 
 #include "rs_internal.h"
-#include "rs_divc.h"
+#include "rs_exact.h"
 
 #pragma clang fp contract(off)
 
@@ -99,6 +99,7 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //   RS_ADAM8_BATCH   8-bit Adam slots loaded ahead of their arithmetic
 //   RS_ADAM8_DIVC    8-bit Adam divides by sqrt(bc2) with div_by_const when
 //                    the constant allows it
+//   RS_ADAM8_SQRT    8-bit Adam takes sqrt(v') with sqrt_rn
 //   RS_NT_STORE_BELOW  launches of quantisation, dequantisation and the
 //                    unmasked zero that write fewer bytes than this (one
 //                    rank's share, say) use nontemporal stores: a short
@@ -136,6 +137,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_ADAM8_DIVC
 #define RS_ADAM8_DIVC 1
+#endif
+#ifndef RS_ADAM8_SQRT
+#define RS_ADAM8_SQRT 1
 #endif
 #ifndef RS_SQNORM_FINE_BELOW
 #define RS_SQNORM_FINE_BELOW 256
@@ -1367,10 +1371,11 @@ struct TileScale {
 
 // The AdamW parameter update from m' and v'.  DIVC: sqrt(v') / bc2s through
 // div_by_const (the host checked bc2s), the same correctly rounded quotient
-// in three operations instead of the IEEE division sequence.
+// in three operations instead of the IEEE division sequence; the square
+// root through sqrt_rn.
 template <bool DIVC>
 __device__ __forceinline__ float adam_p(float p, float m2, float v2, const AdamConst& k) {
-  const float sq = sqrtf(v2);
+  const float sq = RS_ADAM8_SQRT ? sqrt_rn(v2) : sqrtf(v2);
   const float den = (DIVC ? div_by_const(sq, k.bc2s, k.rbc2s) : sq / k.bc2s) + k.eps;
   return p * k.decay - k.step * (m2 / den);
 }

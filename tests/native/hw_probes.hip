@@ -7,13 +7,13 @@
 //  * fp32 division and square root as the kernels compile them (the exact
 //    quantisation path and the AdamW steps rely on both being correctly
 //    rounded);
-//  * the division by a per-call constant of the 8-bit AdamW step
-//    (rs_divc.h), on every input it can receive, against the IEEE quotient.
+//  * the division by a per-call constant and the square root of the 8-bit
+//    AdamW step (rs_exact.h), on every fp32 input, against the IEEE results.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
-#include "rs_divc.h"
+#include "rs_exact.h"
 
 namespace {
 
@@ -58,7 +58,34 @@ __global__ void divc_kernel(uint32_t first, int64_t n, float c, float r, unsigne
   }
 }
 
+// For every fp32 v with bits first + i, i < n: rs::sqrt_rn(v) against the
+// IEEE sqrtf(v), counted and located as above.
+__global__ void sqrt_kernel(uint32_t first, int64_t n, unsigned long long* bad,
+                            uint32_t* first_bad) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint32_t bits = first + uint32_t(i);
+    const float v = __uint_as_float(bits);
+    const float a = rs::sqrt_rn(v);
+    const float q = sqrtf(v);
+    const bool same = (a != a && q != q) || __float_as_uint(a) == __float_as_uint(q);
+    if (!same) {
+      atomicAdd(bad, 1ull);
+      atomicMin(first_bad, bits);
+    }
+  }
+}
+
 }  // namespace
+
+// The same count for rs::sqrt_rn against sqrtf over [first, first + n).
+extern "C" int probe_sqrt(uint32_t first, int64_t n, unsigned long long* bad, uint32_t* first_bad,
+                          void* stream) {
+  if (n <= 0 || n > (int64_t(1) << 32) || !bad || !first_bad) return -1;
+  hipLaunchKernelGGL(sqrt_kernel, dim3(8192), dim3(256), 0, static_cast<hipStream_t>(stream), first,
+                     n, bad, first_bad);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
 
 // Counts, over the fp32 patterns [first, first + n) (n <= 2^32), the y
 // where the constant-divisor quotient of sqrtf(y) by c differs from IEEE's;

@@ -123,7 +123,7 @@ def _divc_constants():
 @pytest.mark.timeout(900)
 def test_division_by_a_constant_is_correctly_rounded():
     """The 8-bit AdamW step divides sqrt(v') by the per-call constant
-    sqrt(bc2) with rs_divc.h's three-operation form.  For every fp32 v' (all
+    sqrt(bc2) with rs_exact.h's three-operation form.  For every fp32 v' (all
     2^32 bit patterns: zeros, subnormals, normals, infinities and NaNs of
     both signs) and each constant above, its quotient has the bits of the
     IEEE quotient (NaN by class)."""
@@ -147,3 +147,25 @@ def test_division_by_a_constant_is_correctly_rounded():
         nbad = int(bad.item())
         assert nbad == 0, (f"c = {float(cf)!r}: {nbad} quotients differ, first at input "
                            f"{int(first.item()) & 0xffffffff:#010x}")
+
+
+@pytest.mark.timeout(900)
+def test_square_root_is_correctly_rounded():
+    """The 8-bit AdamW step takes sqrt(v') with rs_exact.h's sqrt_rn (the
+    hardware root, then the neighbour chosen by exact residuals).  On all 2^32
+    fp32 patterns it has the bits of the IEEE square root (NaN by class)."""
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib = ctypes.CDLL(LIB)
+    lib.probe_sqrt.restype = ctypes.c_int
+    lib.probe_sqrt.argtypes = [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    bad = torch.zeros(1, dtype=torch.int64, device="cuda")
+    first = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    log("square root: all 2^32 inputs")
+    assert lib.probe_sqrt(0, 1 << 32, bad.data_ptr(), first.data_ptr(), stream) == 0
+    torch.cuda.synchronize()
+    nbad = int(bad.item())
+    assert nbad == 0, f"{nbad} roots differ, first at input {int(first.item()) & 0xffffffff:#010x}"
