@@ -1143,7 +1143,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const QuantWork* __re
 //
 // Fused optimizer steps over the fragments of a rank range, one launch for
 // the whole group, fp32 with every operation rounded once (contraction is
-// off in this file; sqrt and division are IEEE).
+// off in this file; sqrt and division are IEEE, or in 8-bit AdamW the
+// shorter forms of rs_exact.h, which give the same bits).
 
 struct AdamConst {
   float beta1, beta2, omb1, omb2, eps, decay, step, bc2s, inv;
