@@ -365,7 +365,8 @@ typedef struct {
  * when NULL) change.  found_inf: device uint32 [m] or NULL; when any entry
  * is non-zero nothing is written (the step is skipped).
  *   p, g, m, v   device fp32, m*S elements each (buffer layout)
- *   hp           host */
+ *   hp           host; RS_ERR_INVALID_ARG unless both bias corrections are
+ *                > 0 and grad_scale is non-zero */
 rs_status rs_adamw_step(const rs_layout* layout, float* p, const float* g, float* m, float* v,
                         const rs_adamw_params* hp, const uint8_t* tensor_mask,
                         const uint32_t* found_inf, int32_t k0, int32_t k1, void* stream);
@@ -383,7 +384,8 @@ rs_status rs_adamw_step(const rs_layout* layout, float* p, const float* g, float
  *   m_codes, v_codes   device uint8, m*S bytes, in place
  *   m_scales, v_scales device fp32 [info.num_tiles], in place (may be NULL
  *                      when num_tiles is 0)
- *   fmt                RS_Q_INT8 or RS_Q_FP8_E4M3 */
+ *   fmt                RS_Q_INT8 or RS_Q_FP8_E4M3
+ *   hp                 host, checked as in rs_adamw_step */
 rs_status rs_adamw8_step(const rs_layout* layout, float* p, const float* g, uint8_t* m_codes,
                          float* m_scales, uint8_t* v_codes, float* v_scales, rs_qfmt fmt,
                          const rs_adamw_params* hp, const uint32_t* found_inf, int32_t k0,
@@ -401,7 +403,8 @@ typedef struct {
  *   p = p - lr*d
  * (fp32, each operation rounded once; no dampening - a zeroed b makes the
  * first step b = g).  Masks, rank range and found_inf as in rs_adamw_step.
- *   p, g, buf    device fp32, m*S elements each */
+ *   p, g, buf    device fp32, m*S elements each
+ *   hp           host; RS_ERR_INVALID_ARG when grad_scale is 0 */
 rs_status rs_sgd_step(const rs_layout* layout, float* p, const float* g, float* buf,
                       const rs_sgd_params* hp, const uint8_t* tensor_mask,
                       const uint32_t* found_inf, int32_t k0, int32_t k1, void* stream);
