@@ -79,6 +79,8 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    vector each; it hurts the zero
 //   RS_SCALE_SPLIT   workgroups per chunk of scale/add (1024 elements each
 //                    at the default chunk size)
+//   RS_XCD_REMAP_MIN scale/add ranges of at least this many elements give
+//                    each XCD one contiguous run of chunks (0: never)
 //   RS_QUANT_F,      256-lane sub-blocks per quantisation work item of wide
 //   RS_QUANT_F_SMALL tiles, for launches of at least / fewer than
 //                    RS_QUANT_SMALL_ITEMS work items (narrow tiles: one)
@@ -134,6 +136,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_QUANT_SMALL_ITEMS
 #define RS_QUANT_SMALL_ITEMS 1024
+#endif
+#ifndef RS_XCD_REMAP_MIN
+#define RS_XCD_REMAP_MIN (int64_t(1) << 26)
 #endif
 #ifndef RS_ADAM8_DIVC
 #define RS_ADAM8_DIVC 1
@@ -326,6 +331,17 @@ __device__ __forceinline__ void zero_run(void* dst, int64_t n) {
 // longer-lived workgroups or consecutive chunk runs per workgroup were
 // slower), striding by the grid if the grid is ever smaller than nc.
 
+// The first item of workgroup b of G.  With remap the items are grouped by
+// XCD: the hardware hands workgroup b to XCD b % 8, and each XCD's
+// workgroups then take one contiguous run of items (a bijection on [0, G);
+// the identity when G < 8).  Long scale/add launches run faster that way;
+// short ones, the copies and the optimizer steps do not.
+__device__ __forceinline__ int64_t first_item(int64_t b, int64_t G, int remap) {
+  if (!remap) return b;
+  const int64_t q = G / 8, r = G % 8, x = b % 8, k = b / 8;
+  return x * q + (x < r ? x : r) + k;
+}
+
 template <int SK, int DK>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const ChunkDesc* __restrict__ chunks,
                                                         int64_t c0, int64_t nc,
@@ -453,8 +469,10 @@ __device__ __forceinline__ void scale_add_run(float* yp, const char* xp, int n, 
 template <int XK>
 __global__ __launch_bounds__(kThreads) void scale_add_kernel(
     const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* y, const void* x,
-    float alpha, float beta, const uint8_t* __restrict__ mask, uint32_t* __restrict__ found_inf) {
-  for (int64_t ii = blockIdx.x; ii < nc * RS_SCALE_SPLIT; ii += gridDim.x) {
+    float alpha, float beta, const uint8_t* __restrict__ mask, uint32_t* __restrict__ found_inf,
+    int remap) {
+  for (int64_t ii = first_item(blockIdx.x, gridDim.x, remap); ii < nc * RS_SCALE_SPLIT;
+       ii += gridDim.x) {
     const ChunkDesc c = chunks[c0 + ii / RS_SCALE_SPLIT];
     if (c.tensor < 0) continue;
     if (mask && !mask[c.tensor]) continue;
@@ -1602,6 +1620,18 @@ int64_t max_groups(int threads) {
   return env_cap > 0 ? std::min(env_cap, hw) : hw;
 }
 
+// Whether scale/add groups its items by XCD: for ranges of at least
+// RS_XCD_REMAP_MIN elements (0: never).  The environment variable of the
+// same name, read once per process, overrides it (tests force the remap on
+// small groups with it).
+int xcd_remap(const rs_layout* L, int32_t k0, int32_t k1) {
+  static const int64_t min_elems = [] {
+    const char* e = std::getenv("RS_XCD_REMAP_MIN");
+    return e ? std::max<int64_t>(0, std::atoll(e)) : int64_t(RS_XCD_REMAP_MIN);
+  }();
+  return min_elems > 0 && int64_t(k1 - k0) * L->S >= min_elems ? 1 : 0;
+}
+
 // Workgroups for n chunk-kernel items: one per item, up to the launch cap;
 // the chunk kernels stride by the grid beyond it.
 dim3 chunk_grid(int64_t n) {
@@ -1697,12 +1727,13 @@ extern "C" rs_status rs_group_scale_add(const rs_layout* L, float* y, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
   const dim3 g = chunk_grid(nc * RS_SCALE_SPLIT), b(kThreads);
+  const int remap = xcd_remap(L, k0, k1);
   if (x_dt == RS_F32)
     launch((scale_add_kernel<0>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
-                       found_inf);
+           found_inf, remap);
   else
     launch((scale_add_kernel<1>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
-                       found_inf);
+           found_inf, remap);
   return after_launch(fn);
 } catch (...) {
   return rs::on_exception("rs_group_scale_add");
