@@ -79,8 +79,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    vector each; it hurts the zero
 //   RS_SCALE_SPLIT   workgroups per chunk of scale/add (1024 elements each
 //                    at the default chunk size)
-//   RS_XCD_REMAP_MIN scale/add ranges of at least this many elements give
-//                    each XCD one contiguous run of chunks (0: never)
+//   RS_XCD_REMAP_MIN scale/add, unpack and unmasked-zero ranges of at least
+//                    this many elements give each XCD one contiguous run of
+//                    chunks (0: never)
 //   RS_QUANT_F,      256-lane sub-blocks per quantisation work item of wide
 //   RS_QUANT_F_SMALL tiles, for launches of at least / fewer than
 //                    RS_QUANT_SMALL_ITEMS work items (narrow tiles: one)
@@ -334,8 +335,9 @@ __device__ __forceinline__ void zero_run(void* dst, int64_t n) {
 // The first item of workgroup b of G.  With remap the items are grouped by
 // XCD: the hardware hands workgroup b to XCD b % 8, and each XCD's
 // workgroups then take one contiguous run of items (a bijection on [0, G);
-// the identity when G < 8).  Long scale/add launches run faster that way;
-// short ones, the copies and the optimizer steps do not.
+// the identity when G < 8).  Long scale/add, unpack and unmasked zero
+// launches run faster that way; short ones, pack, the norms, the tile
+// kernels and the optimizer steps do not.
 __device__ __forceinline__ int64_t first_item(int64_t b, int64_t G, int remap) {
   if (!remap) return b;
   const int64_t q = G / 8, r = G % 8, x = b % 8, k = b / 8;
@@ -363,8 +365,9 @@ template <int SK, int DK>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const ChunkDesc* __restrict__ chunks,
                                                           int64_t c0, int64_t nc,
                                                           const void* __restrict__ buf,
-                                                          void* const* __restrict__ dst) {
-  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
+                                                          void* const* __restrict__ dst,
+                                                          int remap) {
+  for (int64_t i = first_item(blockIdx.x, gridDim.x, remap); i < nc; i += gridDim.x) {
     const ChunkDesc c = chunks[c0 + i];
     if (c.tensor < 0) continue;
     const char* s = static_cast<const char*>(buf) + c.buf_off * esize<SK>();
@@ -505,8 +508,8 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(const ChunkDesc* __restr
 // per workgroup.
 template <bool NT>
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(char* __restrict__ base,
-                                                             int64_t nbytes) {
-  const int64_t lo = int64_t(blockIdx.x) * RS_FILL_BYTES;
+                                                             int64_t nbytes, int remap) {
+  const int64_t lo = first_item(blockIdx.x, gridDim.x, remap) * RS_FILL_BYTES;
   const int64_t n16 = (nbytes - lo < RS_FILL_BYTES ? nbytes - lo : RS_FILL_BYTES) / 16;
   const u32x4 z = {0u, 0u, 0u, 0u};
   char* d = base + lo;
@@ -1620,10 +1623,10 @@ int64_t max_groups(int threads) {
   return env_cap > 0 ? std::min(env_cap, hw) : hw;
 }
 
-// Whether scale/add groups its items by XCD: for ranges of at least
-// RS_XCD_REMAP_MIN elements (0: never).  The environment variable of the
-// same name, read once per process, overrides it (tests force the remap on
-// small groups with it).
+// Whether scale/add, unpack and the unmasked zero group their items by XCD:
+// for ranges of at least RS_XCD_REMAP_MIN elements (0: never).  The
+// environment variable of the same name, read once per process, overrides
+// it (tests force the remap on small groups with it).
 int xcd_remap(const rs_layout* L, int32_t k0, int32_t k1) {
   static const int64_t min_elems = [] {
     const char* e = std::getenv("RS_XCD_REMAP_MIN");
@@ -1699,14 +1702,15 @@ extern "C" rs_status rs_unpack(const rs_layout* L, const void* buf, rs_dtype buf
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
   const dim3 g = chunk_grid(nc), b(kThreads);
+  const int remap = xcd_remap(L, k0, k1);
   if (buf_dt == RS_BF16 && dst_dt == RS_BF16)
-    launch((unpack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, buf, dst);
+    launch((unpack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, buf, dst, remap);
   else if (buf_dt == RS_BF16 && dst_dt == RS_F32)
-    launch((unpack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, buf, dst);
+    launch((unpack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, buf, dst, remap);
   else if (buf_dt == RS_F32 && dst_dt == RS_F32)
-    launch((unpack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, buf, dst);
+    launch((unpack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, buf, dst, remap);
   else
-    launch((unpack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, buf, dst);
+    launch((unpack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, buf, dst, remap);
   return after_launch(fn);
 } catch (...) {
   return rs::on_exception("rs_unpack");
@@ -1754,15 +1758,16 @@ extern "C" rs_status rs_group_zero(const rs_layout* L, void* y, rs_dtype dt,
     // the whole rank range, padding included: one contiguous fill, in
     // launches of at most the grid cap
     const int64_t per = max_groups(kThreads) * RS_FILL_BYTES;
+    const int remap = xcd_remap(L, k0, k1);
     for (int64_t o = 0; o < nbytes; o += per) {
       const int64_t nb = std::min(per, nbytes - o);
       const int64_t g = (nb + RS_FILL_BYTES - 1) / RS_FILL_BYTES;
       if (nbytes < RS_NT_STORE_BELOW)
         launch(fill_zero_kernel<true>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
-                           s, lo + o, nb);
+                           s, lo + o, nb, remap);
       else
         launch(fill_zero_kernel<false>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
-                           s, lo + o, nb);
+                           s, lo + o, nb, remap);
       RS_TRY(after_launch(fn));
     }
     return RS_OK;

@@ -8,9 +8,10 @@ library's environment variables (read once per process) in a child pytest.
   only past about 34 GB of fp32; RS_MAX_GRID=3 makes every call take the
   split paths, and the small-group parity and optimizer tests of five groups
   run again against the same oracle bar.
-* scale/add with its chunks grouped by XCD, which it does only on ranges of
-  at least RS_XCD_REMAP_MIN elements (2^26 by default); RS_XCD_REMAP_MIN=1
-  turns it on for every scale/add parity case.
+* scale/add, unpack and the unmasked zero with their chunks grouped by XCD,
+  which they do only on ranges of at least RS_XCD_REMAP_MIN elements (2^26
+  by default); RS_XCD_REMAP_MIN=1 turns it on for every parity case of
+  those operations.
 """
 import os
 import subprocess
@@ -43,11 +44,12 @@ def test_parity_with_three_workgroup_grid_cap():
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("grid_cap", [None, "5"])
-def test_scale_add_grouped_by_xcd(grid_cap):
-    """scale/add gives each XCD a contiguous run of chunks on long ranges
-    (at least RS_XCD_REMAP_MIN elements).  The small groups never reach the
-    threshold, so a child process sets RS_XCD_REMAP_MIN=1 and re-runs every
-    scale/add parity case with the remap on: once with the normal grid and
+def test_chunks_grouped_by_xcd(grid_cap):
+    """scale/add, unpack and the unmasked zero give each XCD a contiguous
+    run of chunks on long ranges (at least RS_XCD_REMAP_MIN elements).  The
+    small groups never reach the threshold, so a child process sets
+    RS_XCD_REMAP_MIN=1 and re-runs those operations' parity cases (and the
+    two-stream test) with the remap on: once with the normal grid and
     once with the grid capped at 5 workgroups (the remapped first item plus
     the strided loop, and a grid below 8 where the remap is the identity)."""
     if os.environ.get("RS_XCD_REMAP_MIN") or os.environ.get("RS_MAX_GRID"):
@@ -59,8 +61,8 @@ def test_scale_add_grouped_by_xcd(grid_cap):
     if grid_cap:
         env["RS_MAX_GRID"] = grid_cap
     cmd = [sys.executable, "-u", "-m", "pytest", "tests/test_gpu_parity.py", "tests/test_gpu_streams.py",
-           "-x", "-q", "-m", "gpu", "-k", "scale_add or disjoint", "-p", "no:cacheprovider",
-           "--timeout", "300", "--timeout-method", "thread"]
+           "-x", "-q", "-m", "gpu", "-k", "scale_add or unpack or zero or disjoint or roundtrip",
+           "-p", "no:cacheprovider", "--timeout", "300", "--timeout-method", "thread"]
     print("child:", " ".join(cmd), "with RS_XCD_REMAP_MIN=1",
           f"and RS_MAX_GRID={grid_cap}" if grid_cap else "", flush=True)
     r = subprocess.run(cmd, cwd=ROOT, env=env, timeout=840)
