@@ -79,9 +79,11 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    vector each; it hurts the zero
 //   RS_SCALE_SPLIT   workgroups per chunk of scale/add (1024 elements each
 //                    at the default chunk size)
-//   RS_XCD_REMAP_MIN scale/add, unpack and unmasked-zero ranges of at least
-//                    this many elements give each XCD one contiguous run of
-//                    chunks (0: never)
+//   RS_XCD_REMAP_MIN pack, unpack, scale/add and unmasked-zero ranges of at
+//                    least this many elements group their chunks by XCD (0:
+//                    never)
+//   RS_XCD_RUN       chunks per XCD run for pack, unpack and scale/add, a
+//                    power of two (the unmasked zero takes one run per XCD)
 //   RS_QUANT_F,      256-lane sub-blocks per quantisation work item of wide
 //   RS_QUANT_F_SMALL tiles, for launches of at least / fewer than
 //                    RS_QUANT_SMALL_ITEMS work items (narrow tiles: one)
@@ -140,6 +142,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_XCD_REMAP_MIN
 #define RS_XCD_REMAP_MIN (int64_t(1) << 26)
+#endif
+#ifndef RS_XCD_RUN
+#define RS_XCD_RUN 128
 #endif
 #ifndef RS_ADAM8_DIVC
 #define RS_ADAM8_DIVC 1
@@ -332,24 +337,38 @@ __device__ __forceinline__ void zero_run(void* dst, int64_t n) {
 // longer-lived workgroups or consecutive chunk runs per workgroup were
 // slower), striding by the grid if the grid is ever smaller than nc.
 
-// The first item of workgroup b of G.  With remap the items are grouped by
-// XCD: the hardware hands workgroup b to XCD b % 8, and each XCD's
-// workgroups then take one contiguous run of items (a bijection on [0, G);
-// the identity when G < 8).  Long scale/add, unpack and unmasked zero
-// launches run faster that way; short ones, pack, the norms, the tile
-// kernels and the optimizer steps do not.
-__device__ __forceinline__ int64_t first_item(int64_t b, int64_t G, int remap) {
-  if (!remap) return b;
-  const int64_t q = G / 8, r = G % 8, x = b % 8, k = b / 8;
-  return x * q + (x < r ? x : r) + k;
+// How a launch's workgroups map onto its items.  The hardware hands
+// workgroup b to XCD b % 8.  kXcdRuns: in rounds of 8 runs of 2^shift
+// consecutive items, XCD x takes run x of each round (a last partial round
+// keeps the hardware order); kXcdOneRun: each XCD takes one contiguous run of
+// about G/8 items; kXcdNone: the hardware order.  Shifts and masks only: the
+// mapping runs once at the start of every (short-lived) workgroup.
+enum { kXcdNone = 0, kXcdRuns = 1, kXcdOneRun = 2 };
+struct XcdOrder {
+  int32_t mode, shift;
+};
+
+// The first item of workgroup b of G under order o: a bijection on [0, G)
+// in every mode (the identity when G < 8).
+__device__ __forceinline__ int64_t first_item(int64_t b, int64_t G, XcdOrder o) {
+  if (o.mode == kXcdNone) return b;
+  if (o.mode == kXcdOneRun) {
+    const int64_t q = G >> 3, r = G & 7, x = b & 7, k = b >> 3;
+    return x * q + (x < r ? x : r) + k;
+  }
+  const int sr = o.shift + 3;  // items per round: 8 << shift
+  const int64_t round = b >> sr;
+  if ((round + 1) << sr > G) return b;
+  const int64_t within = b & ((int64_t(1) << sr) - 1);
+  return (round << sr) + ((within & 7) << o.shift) + (within >> 3);
 }
 
 template <int SK, int DK>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const ChunkDesc* __restrict__ chunks,
                                                         int64_t c0, int64_t nc,
                                                         const void* const* __restrict__ src,
-                                                        void* __restrict__ buf) {
-  for (int64_t i = blockIdx.x; i < nc; i += gridDim.x) {
+                                                        void* __restrict__ buf, XcdOrder run) {
+  for (int64_t i = first_item(blockIdx.x, gridDim.x, run); i < nc; i += gridDim.x) {
     const ChunkDesc c = chunks[c0 + i];
     char* d = static_cast<char*>(buf) + c.buf_off * esize<DK>();
     if (c.tensor < 0) {
@@ -366,8 +385,8 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const ChunkDesc* __res
                                                           int64_t c0, int64_t nc,
                                                           const void* __restrict__ buf,
                                                           void* const* __restrict__ dst,
-                                                          int remap) {
-  for (int64_t i = first_item(blockIdx.x, gridDim.x, remap); i < nc; i += gridDim.x) {
+                                                          XcdOrder run) {
+  for (int64_t i = first_item(blockIdx.x, gridDim.x, run); i < nc; i += gridDim.x) {
     const ChunkDesc c = chunks[c0 + i];
     if (c.tensor < 0) continue;
     const char* s = static_cast<const char*>(buf) + c.buf_off * esize<SK>();
@@ -473,8 +492,8 @@ template <int XK>
 __global__ __launch_bounds__(kThreads) void scale_add_kernel(
     const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* y, const void* x,
     float alpha, float beta, const uint8_t* __restrict__ mask, uint32_t* __restrict__ found_inf,
-    int remap) {
-  for (int64_t ii = first_item(blockIdx.x, gridDim.x, remap); ii < nc * RS_SCALE_SPLIT;
+    XcdOrder run) {
+  for (int64_t ii = first_item(blockIdx.x, gridDim.x, run); ii < nc * RS_SCALE_SPLIT;
        ii += gridDim.x) {
     const ChunkDesc c = chunks[c0 + ii / RS_SCALE_SPLIT];
     if (c.tensor < 0) continue;
@@ -508,8 +527,8 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(const ChunkDesc* __restr
 // per workgroup.
 template <bool NT>
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(char* __restrict__ base,
-                                                             int64_t nbytes, int remap) {
-  const int64_t lo = first_item(blockIdx.x, gridDim.x, remap) * RS_FILL_BYTES;
+                                                             int64_t nbytes, XcdOrder run) {
+  const int64_t lo = first_item(blockIdx.x, gridDim.x, run) * RS_FILL_BYTES;
   const int64_t n16 = (nbytes - lo < RS_FILL_BYTES ? nbytes - lo : RS_FILL_BYTES) / 16;
   const u32x4 z = {0u, 0u, 0u, 0u};
   char* d = base + lo;
@@ -1623,16 +1642,25 @@ int64_t max_groups(int threads) {
   return env_cap > 0 ? std::min(env_cap, hw) : hw;
 }
 
-// Whether scale/add, unpack and the unmasked zero group their items by XCD:
-// for ranges of at least RS_XCD_REMAP_MIN elements (0: never).  The
-// environment variable of the same name, read once per process, overrides
-// it (tests force the remap on small groups with it).
-int xcd_remap(const rs_layout* L, int32_t k0, int32_t k1) {
-  static const int64_t min_elems = [] {
-    const char* e = std::getenv("RS_XCD_REMAP_MIN");
-    return e ? std::max<int64_t>(0, std::atoll(e)) : int64_t(RS_XCD_REMAP_MIN);
+// The workgroup order of pack, unpack and scale/add (runs of RS_XCD_RUN
+// chunks per XCD, a power of two) and of the unmasked zero (one run per
+// XCD) over ranges of at least RS_XCD_REMAP_MIN elements (0: never); the
+// hardware order below that.  Environment variables of the same names, read
+// once per process, override both (tests force short runs on small groups).
+int64_t env_or(const char* name, int64_t dflt) {
+  const char* e = std::getenv(name);
+  return e ? std::atoll(e) : dflt;
+}
+XcdOrder xcd_run(const rs_layout* L, int32_t k0, int32_t k1, bool one_run) {
+  static const int64_t min_elems = std::max<int64_t>(0, env_or("RS_XCD_REMAP_MIN", RS_XCD_REMAP_MIN));
+  static const int shift = [] {  // log2 of the run, rounded down, in [0, 20]
+    const int64_t run = std::max<int64_t>(1, std::min<int64_t>(env_or("RS_XCD_RUN", RS_XCD_RUN), 1 << 20));
+    int sh = 0;
+    while ((int64_t(2) << sh) <= run) ++sh;
+    return sh;
   }();
-  return min_elems > 0 && int64_t(k1 - k0) * L->S >= min_elems ? 1 : 0;
+  if (min_elems == 0 || int64_t(k1 - k0) * L->S < min_elems) return XcdOrder{kXcdNone, 0};
+  return one_run ? XcdOrder{kXcdOneRun, 0} : XcdOrder{kXcdRuns, shift};
 }
 
 // Workgroups for n chunk-kernel items: one per item, up to the launch cap;
@@ -1675,14 +1703,15 @@ extern "C" rs_status rs_pack(const rs_layout* L, const void* const* src, rs_dtyp
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
   const dim3 g = chunk_grid(nc), b(kThreads);
+  const XcdOrder run = xcd_run(L, k0, k1, false);
   if (src_dt == RS_F32 && buf_dt == RS_BF16)
-    launch((pack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, src, buf);
+    launch((pack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, src, buf, run);
   else if (src_dt == RS_F32 && buf_dt == RS_F32)
-    launch((pack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, src, buf);
+    launch((pack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, src, buf, run);
   else if (src_dt == RS_BF16 && buf_dt == RS_BF16)
-    launch((pack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, src, buf);
+    launch((pack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, src, buf, run);
   else
-    launch((pack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, src, buf);
+    launch((pack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, src, buf, run);
   return after_launch(fn);
 } catch (...) {
   return rs::on_exception("rs_pack");
@@ -1702,15 +1731,15 @@ extern "C" rs_status rs_unpack(const rs_layout* L, const void* buf, rs_dtype buf
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
   const dim3 g = chunk_grid(nc), b(kThreads);
-  const int remap = xcd_remap(L, k0, k1);
+  const XcdOrder run = xcd_run(L, k0, k1, false);
   if (buf_dt == RS_BF16 && dst_dt == RS_BF16)
-    launch((unpack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, buf, dst, remap);
+    launch((unpack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, buf, dst, run);
   else if (buf_dt == RS_BF16 && dst_dt == RS_F32)
-    launch((unpack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, buf, dst, remap);
+    launch((unpack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, buf, dst, run);
   else if (buf_dt == RS_F32 && dst_dt == RS_F32)
-    launch((unpack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, buf, dst, remap);
+    launch((unpack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, buf, dst, run);
   else
-    launch((unpack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, buf, dst, remap);
+    launch((unpack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, buf, dst, run);
   return after_launch(fn);
 } catch (...) {
   return rs::on_exception("rs_unpack");
@@ -1731,13 +1760,13 @@ extern "C" rs_status rs_group_scale_add(const rs_layout* L, float* y, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
   const dim3 g = chunk_grid(nc * RS_SCALE_SPLIT), b(kThreads);
-  const int remap = xcd_remap(L, k0, k1);
+  const XcdOrder run = xcd_run(L, k0, k1, false);
   if (x_dt == RS_F32)
     launch((scale_add_kernel<0>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
-           found_inf, remap);
+           found_inf, run);
   else
     launch((scale_add_kernel<1>), g, b, 0, s, ch, c0, nc, y, x, alpha, beta, tensor_mask,
-           found_inf, remap);
+           found_inf, run);
   return after_launch(fn);
 } catch (...) {
   return rs::on_exception("rs_group_scale_add");
@@ -1758,16 +1787,16 @@ extern "C" rs_status rs_group_zero(const rs_layout* L, void* y, rs_dtype dt,
     // the whole rank range, padding included: one contiguous fill, in
     // launches of at most the grid cap
     const int64_t per = max_groups(kThreads) * RS_FILL_BYTES;
-    const int remap = xcd_remap(L, k0, k1);
+    const XcdOrder run = xcd_run(L, k0, k1, true);
     for (int64_t o = 0; o < nbytes; o += per) {
       const int64_t nb = std::min(per, nbytes - o);
       const int64_t g = (nb + RS_FILL_BYTES - 1) / RS_FILL_BYTES;
       if (nbytes < RS_NT_STORE_BELOW)
         launch(fill_zero_kernel<true>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
-                           s, lo + o, nb, remap);
+                           s, lo + o, nb, run);
       else
         launch(fill_zero_kernel<false>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
-                           s, lo + o, nb, remap);
+                           s, lo + o, nb, run);
       RS_TRY(after_launch(fn));
     }
     return RS_OK;

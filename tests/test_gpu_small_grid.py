@@ -8,9 +8,10 @@ library's environment variables (read once per process) in a child pytest.
   only past about 34 GB of fp32; RS_MAX_GRID=3 makes every call take the
   split paths, and the small-group parity and optimizer tests of five groups
   run again against the same oracle bar.
-* scale/add, unpack and the unmasked zero with their chunks grouped by XCD,
-  which they do only on ranges of at least RS_XCD_REMAP_MIN elements (2^26
-  by default); RS_XCD_REMAP_MIN=1 turns it on for every parity case of
+* pack, unpack, scale/add and the unmasked zero with their chunks grouped
+  by XCD, which they do only on ranges of at least RS_XCD_REMAP_MIN
+  elements (2^26 by default), in runs of RS_XCD_RUN chunks (128);
+  RS_XCD_REMAP_MIN=1 with short runs turns it on for every parity case of
   those operations.
 """
 import os
@@ -43,27 +44,29 @@ def test_parity_with_three_workgroup_grid_cap():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("grid_cap", [None, "5"])
-def test_chunks_grouped_by_xcd(grid_cap):
-    """scale/add, unpack and the unmasked zero give each XCD a contiguous
-    run of chunks on long ranges (at least RS_XCD_REMAP_MIN elements).  The
-    small groups never reach the threshold, so a child process sets
-    RS_XCD_REMAP_MIN=1 and re-runs those operations' parity cases (and the
-    two-stream test) with the remap on: once with the normal grid and
-    once with the grid capped at 5 workgroups (the remapped first item plus
-    the strided loop, and a grid below 8 where the remap is the identity)."""
-    if os.environ.get("RS_XCD_REMAP_MIN") or os.environ.get("RS_MAX_GRID"):
-        pytest.skip("already running under a remap or grid override")
+@pytest.mark.parametrize("run,grid_cap", [("2", None), ("8", None), ("2", "5")])
+def test_chunks_grouped_by_xcd(run, grid_cap):
+    """Pack, unpack, scale/add and the unmasked zero group their chunks by
+    XCD on long ranges (at least RS_XCD_REMAP_MIN elements): runs of
+    RS_XCD_RUN consecutive chunks per XCD (one run per XCD for the zero).
+    The small groups reach neither the threshold nor a full round of the
+    default 128-chunk runs, so a child process sets RS_XCD_REMAP_MIN=1 and
+    short runs (2 or 8 chunks: rounds of 16 or 64, then a partial round),
+    and re-runs those operations' parity cases and the two-stream test; once
+    more with the grid capped at 5 workgroups (the first item plus the
+    strided loop, with a grid below one round)."""
+    if any(os.environ.get(v) for v in ("RS_XCD_REMAP_MIN", "RS_XCD_RUN", "RS_MAX_GRID")):
+        pytest.skip("already running under a launch-shape override")
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    env = dict(os.environ, RS_XCD_REMAP_MIN="1")
+    env = dict(os.environ, RS_XCD_REMAP_MIN="1", RS_XCD_RUN=run)
     if grid_cap:
         env["RS_MAX_GRID"] = grid_cap
     cmd = [sys.executable, "-u", "-m", "pytest", "tests/test_gpu_parity.py", "tests/test_gpu_streams.py",
-           "-x", "-q", "-m", "gpu", "-k", "scale_add or unpack or zero or disjoint or roundtrip",
+           "-x", "-q", "-m", "gpu", "-k", "pack or scale_add or zero or disjoint",
            "-p", "no:cacheprovider", "--timeout", "300", "--timeout-method", "thread"]
-    print("child:", " ".join(cmd), "with RS_XCD_REMAP_MIN=1",
-          f"and RS_MAX_GRID={grid_cap}" if grid_cap else "", flush=True)
+    print("child:", " ".join(cmd), f"with RS_XCD_REMAP_MIN=1 RS_XCD_RUN={run}",
+          f"RS_MAX_GRID={grid_cap}" if grid_cap else "", flush=True)
     r = subprocess.run(cmd, cwd=ROOT, env=env, timeout=840)
-    assert r.returncode == 0, f"child pytest with the remap forced exited with {r.returncode}"
+    assert r.returncode == 0, f"child pytest with XCD runs forced exited with {r.returncode}"
