@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import ctypes
@@ -246,8 +247,8 @@ OP_MIX = {"pack": "f32_to_bf16", "unpack": "copy", "scale_add": "axpby_inplace",
 def measure_ceilings(torch, dev, stream, event_ms, n=1 << 28, slices=1, vecs=(1, 2, 4, 8),
                      kinds=None):
     """Best GB/s of each streaming kind over n fp32 elements (vectors per
-    lane, nontemporal hints and, for conversions, wide and narrow forms
-    swept), with the variant kept.  With slices > 1, each timed call is one
+    lane, nontemporal hints, workgroup order by XCD and, for conversions,
+    wide and narrow forms swept), with the variant kept.  With slices > 1, each timed call is one
     launch per slice of n elements, in turn over `slices` consecutive slices:
     one rank's share, cycled over the ranks as the per-rank launches are."""
     if not os.path.exists(CEILING_LIB):
@@ -267,20 +268,19 @@ def measure_ceilings(torch, dev, stream, event_ms, n=1 << 28, slices=1, vecs=(1,
             continue
         best = None
         forms = (0, 16) if kind >= 5 else (0,)    # conversions: wide and narrow forms
-        for form in forms:
-            for vec in vecs:
-                for nt in (0, 1):
-                    def f(k=kind + form, vec=vec, nt=nt):
-                        for j in range(slices):
-                            o = 4 * n * j
-                            if lib.hc_stream(k, x.data_ptr() + o, y.data_ptr() + o, z.data_ptr() + o,
-                                             n, vec, nt, sp):
-                                raise RuntimeError("hc_stream failed")
-                    med, _, _ = event_ms(f, 5)
-                    gbs = per * n * slices / (med * 1e-3) / 1e9
-                    if best is None or gbs > best["GB/s"]:
-                        best = {"GB/s": round(gbs, 1), "vec": vec, "nt": nt,
-                                "form": "narrow" if form else "wide"}
+        for form, order, vec, nt in itertools.product(forms, (0, 32, 64), vecs, (0, 1)):
+            def f(k=kind + form + order, vec=vec, nt=nt):
+                for j in range(slices):
+                    o = 4 * n * j
+                    if lib.hc_stream(k, x.data_ptr() + o, y.data_ptr() + o, z.data_ptr() + o,
+                                     n, vec, nt, sp):
+                        raise RuntimeError("hc_stream failed")
+            med, _, _ = event_ms(f, 5)
+            gbs = per * n * slices / (med * 1e-3) / 1e9
+            if best is None or gbs > best["GB/s"]:
+                best = {"GB/s": round(gbs, 1), "vec": vec, "nt": nt,
+                        "form": "narrow" if form else "wide",
+                        "order": {0: "hardware", 32: "xcd runs", 64: "xcd one run"}[order]}
         out[name] = best
         log(f"ceiling {name:14s} {best['GB/s']:8.1f} GB/s ({best}, {slices} x {n} elements)")
     del x, y, z

@@ -41,14 +41,35 @@ __device__ __forceinline__ u32x4 axpby4(u32x4 y, u32x4 x) {
   return u32x4{axpby(y.x, x.x), axpby(y.y, x.y), axpby(y.z, x.z), axpby(y.w, x.w)};
 }
 
-// Workgroup b covers units [b*256*VEC, (b+1)*256*VEC); lane i takes units
-// i, i+256, ...  A unit is one 16-byte vector of the widest stream.  All
-// loads of a lane are issued before its stores.
+// The block of units workgroup b covers.  The hardware hands workgroup b to
+// XCD b % 8; order 1 gives XCD x block x of every round of 8 runs of 128
+// blocks (a last partial round keeps the hardware order), order 2 one
+// contiguous run of about G/8 blocks per XCD, order 0 the hardware order.
+__device__ __forceinline__ int64_t block_of(int order) {
+  const int64_t b = blockIdx.x, G = gridDim.x;
+  if (order == 2) {
+    const int64_t q = G >> 3, r = G & 7, x = b & 7, k = b >> 3;
+    return x * q + (x < r ? x : r) + k;
+  }
+  if (order == 1) {
+    const int64_t round = b >> 10;
+    if ((round + 1) << 10 <= G) {
+      const int64_t within = b & 1023;
+      return (round << 10) + ((within & 7) << 7) + (within >> 3);
+    }
+  }
+  return b;
+}
+
+// Workgroup b covers the units of block block_of(order): [B*256*VEC,
+// (B+1)*256*VEC); lane i takes units i, i+256, ...  A unit is one 16-byte
+// vector of the widest stream.  All loads of a lane are issued before its
+// stores.
 template <int KIND, int VEC, bool NT>
 __global__ __launch_bounds__(kThreads) void stream_kernel(const u32x4* __restrict__ x,
                                                           u32x4* __restrict__ y,
-                                                          u32x4* __restrict__ z) {
-  const int64_t u0 = int64_t(blockIdx.x) * kThreads * VEC + threadIdx.x;
+                                                          u32x4* __restrict__ z, int order) {
+  const int64_t u0 = block_of(order) * kThreads * VEC + threadIdx.x;
   if constexpr (KIND == HC_READ) {
     u32x4 r[VEC];
 #pragma unroll
@@ -164,25 +185,26 @@ constexpr int elems_per_unit(int kind) {
 }
 
 template <int KIND, int VEC>
-hipError_t run(const void* x, void* y, void* z, int64_t n, int nt, hipStream_t s) {
+hipError_t run(const void* x, void* y, void* z, int64_t n, int nt, int order, hipStream_t s) {
   const int64_t units = n / elems_per_unit(KIND);
   const dim3 grid(static_cast<unsigned>(units / (int64_t(kThreads) * VEC)));
   const u32x4* xx = static_cast<const u32x4*>(x);
   u32x4* yy = static_cast<u32x4*>(y);
   u32x4* zz = static_cast<u32x4*>(z);
-  void* args[] = {&xx, &yy, &zz};
+  void* args[] = {&xx, &yy, &zz, &order};
   const void* k = nt ? reinterpret_cast<const void*>(&stream_kernel<KIND, VEC, true>)
                      : reinterpret_cast<const void*>(&stream_kernel<KIND, VEC, false>);
   return hipLaunchKernel(k, grid, dim3(kThreads), args, 0, s);  // this launch's own status
 }
 
 template <int KIND>
-hipError_t run_vec(const void* x, void* y, void* z, int64_t n, int vec, int nt, hipStream_t s) {
+hipError_t run_vec(const void* x, void* y, void* z, int64_t n, int vec, int nt, int order,
+                   hipStream_t s) {
   switch (vec) {
-    case 1: return run<KIND, 1>(x, y, z, n, nt, s);
-    case 2: return run<KIND, 2>(x, y, z, n, nt, s);
-    case 4: return run<KIND, 4>(x, y, z, n, nt, s);
-    default: return run<KIND, 8>(x, y, z, n, nt, s);
+    case 1: return run<KIND, 1>(x, y, z, n, nt, order, s);
+    case 2: return run<KIND, 2>(x, y, z, n, nt, order, s);
+    case 4: return run<KIND, 4>(x, y, z, n, nt, order, s);
+    default: return run<KIND, 8>(x, y, z, n, nt, order, s);
   }
 }
 
@@ -192,6 +214,9 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 extern "C" int hc_stream(int kind, const void* x, void* y, void* z, int64_t n, int vec, int nt,
                          void* stream) {
+  const int order = (kind & HC_XCD_ONE) ? 2 : (kind & HC_XCD_RUNS) ? 1 : 0;
+  if ((kind & HC_XCD_ONE) && (kind & HC_XCD_RUNS)) return -1;
+  kind &= ~(HC_XCD_RUNS | HC_XCD_ONE);
   const bool narrow = kind >= HC_NARROW;
   if (narrow) kind -= HC_NARROW;
   if (kind < HC_READ || kind > HC_U8_TO_F32 || n <= 0 || (vec != 1 && vec != 2 && vec != 4 && vec != 8) ||
@@ -203,22 +228,22 @@ extern "C" int hc_stream(int kind, const void* x, void* y, void* z, int64_t n, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (kind) {
-    case HC_READ: e = run_vec<HC_READ>(x, y, z, n, vec, nt, s); break;
-    case HC_WRITE: e = run_vec<HC_WRITE>(x, y, z, n, vec, nt, s); break;
-    case HC_COPY: e = run_vec<HC_COPY>(x, y, z, n, vec, nt, s); break;
-    case HC_AXPBY_INPLACE: e = run_vec<HC_AXPBY_INPLACE>(x, y, z, n, vec, nt, s); break;
-    case HC_AXPBY: e = run_vec<HC_AXPBY>(x, y, z, n, vec, nt, s); break;
+    case HC_READ: e = run_vec<HC_READ>(x, y, z, n, vec, nt, order, s); break;
+    case HC_WRITE: e = run_vec<HC_WRITE>(x, y, z, n, vec, nt, order, s); break;
+    case HC_COPY: e = run_vec<HC_COPY>(x, y, z, n, vec, nt, order, s); break;
+    case HC_AXPBY_INPLACE: e = run_vec<HC_AXPBY_INPLACE>(x, y, z, n, vec, nt, order, s); break;
+    case HC_AXPBY: e = run_vec<HC_AXPBY>(x, y, z, n, vec, nt, order, s); break;
     case HC_F32_TO_BF16:
-      e = narrow ? run_vec<HC_F32_TO_BF16 + 16>(x, y, z, n, vec, nt, s)
-                 : run_vec<HC_F32_TO_BF16>(x, y, z, n, vec, nt, s);
+      e = narrow ? run_vec<HC_F32_TO_BF16 + 16>(x, y, z, n, vec, nt, order, s)
+                 : run_vec<HC_F32_TO_BF16>(x, y, z, n, vec, nt, order, s);
       break;
     case HC_F32_TO_U8:
-      e = narrow ? run_vec<HC_F32_TO_U8 + 16>(x, y, z, n, vec, nt, s)
-                 : run_vec<HC_F32_TO_U8>(x, y, z, n, vec, nt, s);
+      e = narrow ? run_vec<HC_F32_TO_U8 + 16>(x, y, z, n, vec, nt, order, s)
+                 : run_vec<HC_F32_TO_U8>(x, y, z, n, vec, nt, order, s);
       break;
     default:
-      e = narrow ? run_vec<HC_U8_TO_F32 + 16>(x, y, z, n, vec, nt, s)
-                 : run_vec<HC_U8_TO_F32>(x, y, z, n, vec, nt, s);
+      e = narrow ? run_vec<HC_U8_TO_F32 + 16>(x, y, z, n, vec, nt, order, s)
+                 : run_vec<HC_U8_TO_F32>(x, y, z, n, vec, nt, order, s);
       break;
   }
   return e == hipSuccess ? 0 : -6;

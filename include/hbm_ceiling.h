@@ -27,8 +27,9 @@
  *   stream    hipStream_t as void*
  * Returns 0, or -1 for a bad argument (nothing launched), or -6 when the
  * launch fails.  Each workgroup of 256 lanes covers 256*vec contiguous
- * 16-byte vectors of the widest stream, lane-strided, as the grouped
- * kernels do.
+ * 16-byte vectors of the widest stream (one block), lane-strided, as the
+ * grouped kernels do; the blocks go to workgroups in the hardware order or
+ * grouped by XCD (HC_XCD_RUNS, HC_XCD_ONE), as the grouped kernels may.
  */
 #ifndef HBM_CEILING_H
 #define HBM_CEILING_H
@@ -52,7 +53,13 @@ enum {
    * one 16-byte vector of the wider side and the narrower side is written or
    * read as consecutive 8- or 4-byte words, so every instruction of a wave
    * touches one contiguous span on both sides */
-  HC_NARROW = 16
+  HC_NARROW = 16,
+  /* added to any kind: the workgroup order.  The hardware hands workgroup b
+   * to XCD b % 8.  HC_XCD_RUNS: XCD x takes block x of every round of 8 runs
+   * of 128 consecutive blocks; HC_XCD_ONE: each XCD takes one contiguous run
+   * of about 1/8 of the blocks (not both) */
+  HC_XCD_RUNS = 32,
+  HC_XCD_ONE = 64
 };
 
 int hc_stream(int kind, const void* x, void* y, void* z, int64_t n, int vec, int nt, void* stream);
