@@ -79,12 +79,11 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    vector each; it hurts the zero
 //   RS_SCALE_SPLIT   workgroups per chunk of scale/add (1024 elements each
 //                    at the default chunk size)
-//   RS_XCD_REMAP_MIN pack, unpack, scale/add, unmasked-zero and SGD ranges of
-//                    at least this many elements group their chunks by XCD
-//                    (0: never)
+//   RS_XCD_REMAP_MIN pack, unpack, scale/add and unmasked-zero ranges of at
+//                    least this many elements group their chunks by XCD (0:
+//                    never)
 //   RS_XCD_RUN       chunks per XCD run for pack, unpack and scale/add, a
-//                    power of two (the unmasked zero and SGD take one run
-//                    per XCD)
+//                    power of two (the unmasked zero takes one run per XCD)
 //   RS_QUANT_F,      256-lane sub-blocks per quantisation work item of wide
 //   RS_QUANT_F_SMALL tiles, for launches of at least / fewer than
 //                    RS_QUANT_SMALL_ITEMS work items (narrow tiles: one)
@@ -1285,10 +1284,9 @@ template <int SPLIT>
 __global__ __launch_bounds__(kThreads) void sgd_kernel(
     const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, float* __restrict__ p,
     const float* __restrict__ g, float* __restrict__ buf, SgdConst k,
-    const uint8_t* __restrict__ mask, const uint32_t* __restrict__ found_inf, int m_ranks,
-    XcdOrder run) {
+    const uint8_t* __restrict__ mask, const uint32_t* __restrict__ found_inf, int m_ranks) {
   if (skip_step(found_inf, m_ranks)) return;
-  for (int64_t ii = first_item(blockIdx.x, gridDim.x, run); ii < nc * SPLIT; ii += gridDim.x) {
+  for (int64_t ii = blockIdx.x; ii < nc * SPLIT; ii += gridDim.x) {
     const ChunkDesc c = chunks[c0 + ii / SPLIT];
     if (c.tensor < 0 || (mask && !mask[c.tensor])) continue;
     int64_t off;
@@ -1645,9 +1643,9 @@ int64_t max_groups(int threads) {
 }
 
 // The workgroup order of pack, unpack and scale/add (runs of RS_XCD_RUN
-// chunks per XCD, a power of two) and of the unmasked zero and SGD (one run
-// per XCD) over ranges of at least RS_XCD_REMAP_MIN elements (0: never);
-// the hardware order below that.  Environment variables of the same names, read
+// chunks per XCD, a power of two) and of the unmasked zero (one run per
+// XCD) over ranges of at least RS_XCD_REMAP_MIN elements (0: never); the
+// hardware order below that.  Environment variables of the same names, read
 // once per process, override both (tests force short runs on small groups).
 int64_t env_or(const char* name, int64_t dflt) {
   const char* e = std::getenv(name);
@@ -2056,7 +2054,7 @@ extern "C" rs_status rs_sgd_step(const rs_layout* L, float* p, const float* g, f
   if (nc == 0) return RS_OK;
   launch(sgd_kernel<RS_SGD_SPLIT>, chunk_grid(nc * RS_SGD_SPLIT), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), table<ChunkDesc>(L, L->off_chunks), c0, nc,
-                     p, g, buf, k, tensor_mask, found_inf, L->m, xcd_run(L, k0, k1, true));
+                     p, g, buf, k, tensor_mask, found_inf, L->m);
   return after_launch(fn);
 } catch (...) {
   return rs::on_exception("rs_sgd_step");

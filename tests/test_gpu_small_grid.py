@@ -8,8 +8,8 @@ library's environment variables (read once per process) in a child pytest.
   only past about 34 GB of fp32; RS_MAX_GRID=3 makes every call take the
   split paths, and the small-group parity and optimizer tests of five groups
   run again against the same oracle bar.
-* pack, unpack, scale/add, the unmasked zero and SGD with their chunks
-  grouped by XCD, which they do only on ranges of at least RS_XCD_REMAP_MIN
+* pack, unpack, scale/add and the unmasked zero with their chunks grouped
+  by XCD, which they do only on ranges of at least RS_XCD_REMAP_MIN
   elements (2^26 by default), in runs of RS_XCD_RUN chunks (128);
   RS_XCD_REMAP_MIN=1 with short runs turns it on for every parity case of
   those operations.
@@ -46,10 +46,9 @@ def test_parity_with_three_workgroup_grid_cap():
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("run,grid_cap", [("2", None), ("8", None), ("2", "5")])
 def test_chunks_grouped_by_xcd(run, grid_cap):
-    """Pack, unpack, scale/add, the unmasked zero and SGD group their chunks
-    by XCD on long ranges (at least RS_XCD_REMAP_MIN elements): runs of
-    RS_XCD_RUN consecutive chunks per XCD (one run per XCD for the zero and
-    SGD).
+    """Pack, unpack, scale/add and the unmasked zero group their chunks by
+    XCD on long ranges (at least RS_XCD_REMAP_MIN elements): runs of
+    RS_XCD_RUN consecutive chunks per XCD (one run per XCD for the zero).
     The small groups reach neither the threshold nor a full round of the
     default 128-chunk runs, so a child process sets RS_XCD_REMAP_MIN=1 and
     short runs (2 or 8 chunks: rounds of 16 or 64, then a partial round),
@@ -65,8 +64,7 @@ def test_chunks_grouped_by_xcd(run, grid_cap):
     if grid_cap:
         env["RS_MAX_GRID"] = grid_cap
     cmd = [sys.executable, "-u", "-m", "pytest", "tests/test_gpu_parity.py", "tests/test_gpu_streams.py",
-           "tests/test_gpu_optim.py", "-x", "-q", "-m", "gpu", "-k",
-           "pack or scale_add or zero or disjoint or sgd",
+           "-x", "-q", "-m", "gpu", "-k", "pack or scale_add or zero or disjoint",
            "-p", "no:cacheprovider", "--timeout", "300", "--timeout-method", "thread"]
     print("child:", " ".join(cmd), f"with RS_XCD_REMAP_MIN=1 RS_XCD_RUN={run}",
           f"RS_MAX_GRID={grid_cap}" if grid_cap else "", flush=True)
