@@ -188,6 +188,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #ifndef RS_NT_STORE_BELOW
 #define RS_NT_STORE_BELOW (192ll << 20)
 #endif
+#ifndef RS_QUANT_NT_STORE_BELOW
+#define RS_QUANT_NT_STORE_BELOW RS_NT_STORE_BELOW
+#endif
 
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -760,52 +763,39 @@ __global__ __launch_bounds__(kCombineWaves* kWave) void sqnorm_combine_kernel(
 // division is a ~10-instruction sequence), so each element first takes
 // q' = fl(x * fl(1/scale)), which is within 3 ulp of fl(x / scale) when the
 // scale is a normal number.  The code can only differ when a rounding
-// midpoint of the code grid lies within that distance; exactly those
-// elements (window of 8 ulp), and every element of a tile whose scale is
-// zero, subnormal, infinite or NaN, are encoded from the true quotient.
+// midpoint of the code grid lies within that distance; the elements near
+// a midpoint (a window of at least 3.5 ulp), and every element of a tile
+// whose scale is zero, subnormal, infinite or NaN, are encoded from the
+// true quotient.
 
-// FP8 E4M3: q' is safe when 2^-6 (plus margin) <= |q'| < 464 - below, the
-// E4M3 subnormal grid applies; 464 is the first midpoint past 448 - and its
-// 20 dropped mantissa bits are more than 8 ulp from the half-way pattern
-// 0x80000.
-__device__ __forceinline__ bool e4m3_safe(uint32_t u) {
-  const uint32_t a = u & 0x7fffffffu;
-  return a - 0x3c800010u < 0x43e80000u - 0x3c800010u && ((a & 0xfffffu) - 0x7fff8u) > 16u;
-}
-
-// Four safe values -> four E4M3 codes, little-endian in one word, with
-// gfx950's conversion instruction (OCP E4M3, round to nearest even).  For
-// finite inputs with 2^-6 <= |q| < 464 it equals the saturating encoder
-// above; a test checks that on every such fp32 input.
-__device__ __forceinline__ uint32_t e4m3_pack4_normal(float q0, float q1, float q2, float q3) {
+// Four values -> four E4M3 codes, little-endian in one word, with gfx950's
+// conversion instruction (OCP E4M3, round to nearest even).  For finite
+// inputs with |q| < 464 (464 is the first midpoint past 448) it equals the
+// saturating encoder above, subnormal codes included; a test checks that
+// on every such fp32 input.
+__device__ __forceinline__ uint32_t e4m3_pack4(float q0, float q1, float q2, float q3) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
   return uint32_t(w);
 }
 
-// Four fast-path E4M3 codes.  Values in the instruction's checked domain
-// take its code; values below it lie on the uniform 2^-9 grid of codes 0-16
-// (subnormals and the first binade alike), so their code is rint(|q'|*512)
-// with the sign bit - safe under the INT8 midpoint rule on |q'|*512 (x512
-// is exact).  safe turns false when some value needs the exact quotient.
-__device__ __forceinline__ bool int8_safe(float q, float r);
-
+// Four fast-path E4M3 codes.  The encoder is monotone in |q| and keeps the
+// sign, so when q'(1 - 2^-21) and q'(1 + 2^-21) have the same code, so has
+// every value between them, and that interval holds the true quotient: it
+// is within 2 ulp of q' (one rounding of x * rcp, one of x / scale, and the
+// reciprocal's half ulp), while 2^-21 of a normal |q'| is at least 4 ulp,
+// at least 3.5 after the product's own rounding.  A subnormal q' makes the
+// interval a point, but then q' and the quotient both lie far below 2^-10,
+// the half-way point to the smallest code, and both encode to a signed
+// zero.  With a normal, finite scale, |q'| stays below 449, inside the
+// instruction's checked domain.  safe turns false when the two codes
+// differ: that value needs the exact quotient.
 __device__ __forceinline__ uint32_t e4m3_fast4(const float* q, bool& safe) {
-  uint32_t w = e4m3_pack4_normal(q[0], q[1], q[2], q[3]);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t u = __float_as_uint(q[j]), a = u & 0x7fffffffu;
-    if (a < 0x3c800010u) {
-      const float p = __uint_as_float(a) * 512.0f;
-      const float r = __builtin_rintf(p);
-      safe = safe && int8_safe(p, r);
-      const uint32_t code = uint32_t(r) | ((u >> 24) & 0x80u);
-      w = (w & ~(0xffu << (8 * j))) | (code << (8 * j));
-    } else {
-      safe = safe && e4m3_safe(u);
-    }
-  }
-  return w;
+  constexpr float lo = 1.0f - 0x1p-21f, hi = 1.0f + 0x1p-21f;
+  const uint32_t a = e4m3_pack4(q[0] * lo, q[1] * lo, q[2] * lo, q[3] * lo);
+  const uint32_t b = e4m3_pack4(q[0] * hi, q[1] * hi, q[2] * hi, q[3] * hi);
+  safe = safe && a == b;
+  return a;
 }
 
 // INT8: q' is safe when its distance to the nearest integer is below
@@ -979,26 +969,19 @@ __global__ __launch_bounds__(kThreads* F) void quant_kernel(const QuantWork* __r
     return;
   }
   uint32_t slow = 0;  // bit i: slot s0 + i needs the exact path
-  {
-    SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
+  SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
+  if (fast) {
+    // every in-range slot stores its fast code; a slot that needs the exact
+    // quotient is stored again below by the same lane, which wins
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (lane + (s0 + i) * team < nf) {
         float q[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) q[j] = v[4 * i + j] * rcp;
-        bool safe = fast;
+        bool safe = true;
         uint32_t word;
-        if (!fast) {  // tile-uniform: codes that need no division, else exact
-          safe = zero_tile || nan_tile || inf_scale;
-          if (zero_tile)
-            word = 0u;
-          else if (nan_tile)
-            word = FMT == RS_Q_FP8_E4M3 ? 0x7f7f7f7fu : 0u;
-          else
-            word = encode<FMT>(q[0]) | (encode<FMT>(q[1]) << 8) | (encode<FMT>(q[2]) << 16) |
-                   (encode<FMT>(q[3]) << 24);
-        } else if constexpr (FMT == RS_Q_FP8_E4M3) {
+        if constexpr (FMT == RS_Q_FP8_E4M3) {
           word = e4m3_fast4(q, safe);
         } else {
           float r[4];
@@ -1010,11 +993,36 @@ __global__ __launch_bounds__(kThreads* F) void quant_kernel(const QuantWork* __r
           word = int8_from_rint(r[0]) | (int8_from_rint(r[1]) << 8) | (int8_from_rint(r[2]) << 16) |
                  (int8_from_rint(r[3]) << 24);
         }
-        if (safe) {
-          if constexpr (NTS)
-            __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(cbase + sw.off));
-          else
-            *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
+        if constexpr (NTS)
+          __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(cbase + sw.off));
+        else
+          *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
+        slow |= safe ? 0u : 1u << i;
+      }
+      sw.next();
+    }
+  } else {
+    // tile-uniform: a zero or NaN scale gives constant codes, an Inf scale
+    // the encoder applied to x * 0 (exactly x / Inf); a subnormal scale
+    // takes the exact path for every slot
+    const bool direct = zero_tile || nan_tile || inf_scale;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (lane + (s0 + i) * team < nf) {
+        if (direct) {
+          uint32_t word;
+          if (zero_tile) {
+            word = 0u;
+          } else if (nan_tile) {
+            word = FMT == RS_Q_FP8_E4M3 ? 0x7f7f7f7fu : 0u;
+          } else {
+            float q[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) q[j] = v[4 * i + j] * rcp;
+            word = encode<FMT>(q[0]) | (encode<FMT>(q[1]) << 8) | (encode<FMT>(q[2]) << 16) |
+                   (encode<FMT>(q[3]) << 24);
+          }
+          *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
         } else {
           slow |= 1u << i;
         }
@@ -1022,16 +1030,15 @@ __global__ __launch_bounds__(kThreads* F) void quant_kernel(const QuantWork* __r
       sw.next();
     }
   }
-  if (slow) {  // rare: re-read the slot (cache resident) and divide
+  if (slow) {  // rare: divide the slot's values, still in registers
     SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
-#pragma unroll 1
+#pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (slow & (1u << i)) {
-        const u32x4 q = ld16<false>(base + sw.off);
-        const uint32_t word = encode_exact<FMT>(f32(q.x), scale, zero_tile, nan_tile) |
-                              (encode_exact<FMT>(f32(q.y), scale, zero_tile, nan_tile) << 8) |
-                              (encode_exact<FMT>(f32(q.z), scale, zero_tile, nan_tile) << 16) |
-                              (encode_exact<FMT>(f32(q.w), scale, zero_tile, nan_tile) << 24);
+        const uint32_t word = encode_exact<FMT>(v[4 * i + 0], scale, zero_tile, nan_tile) |
+                              (encode_exact<FMT>(v[4 * i + 1], scale, zero_tile, nan_tile) << 8) |
+                              (encode_exact<FMT>(v[4 * i + 2], scale, zero_tile, nan_tile) << 16) |
+                              (encode_exact<FMT>(v[4 * i + 3], scale, zero_tile, nan_tile) << 24);
         *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
       }
       sw.next();
@@ -1559,15 +1566,14 @@ __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
     for (int i = 0; i < NS; ++i) {
       if (lane + (s0 + i) * team < nf) {
         const int64_t q = o0 + sw.off;
+        // the fast codes are stored whatever the test says; a slot that
+        // needs the exact quotient is stored again below by the same lane
         bool safe = tm.fast && tv.fast;
         const uint32_t wm = fast_encode4<FMT>(M[i], tm.rcp, safe);
         const uint32_t wv = fast_encode4<FMT>(V[i], tv.rcp, safe);
-        if (safe) {
-          *reinterpret_cast<uint32_t*>(mc + q) = wm;
-          *reinterpret_cast<uint32_t*>(vc + q) = wv;
-        } else {
-          slow |= 1u << i;
-        }
+        *reinterpret_cast<uint32_t*>(mc + q) = wm;
+        *reinterpret_cast<uint32_t*>(vc + q) = wv;
+        slow |= safe ? 0u : 1u << i;
       }
       sw.next();
     }
@@ -1895,7 +1901,7 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
   // sub-block, 4 slots per lane.  Wide tiles: 256-lane tiles spread over F
   // sub-blocks, more of them in launches with few work items.
   // nontemporal code stores for launches that write little (see RS_NT_STORE_BELOW)
-  const bool nts = int64_t(k1 - k0) * L->S < RS_NT_STORE_BELOW;
+  const bool nts = int64_t(k1 - k0) * L->S < RS_QUANT_NT_STORE_BELOW;
   for (int c = 0; c < 2; ++c) {
     const int64_t w0 = L->rank_work[c][k0], nw = L->rank_work[c][k1] - w0;
     if (nw == 0) continue;

@@ -1,8 +1,10 @@
 """The block quantisation fast path encodes with gfx950's fp32 -> OCP E4M3
 conversion instruction.  It only ever receives finite values with
-2^-6 (plus 16 ulp) <= |q| < 464; on every fp32 value of that domain, both
-signs, the instruction must give the oracle's saturating round-to-nearest-
-even code."""
+|q| < 464 (the first midpoint past 448); on every fp32 value of that
+domain, zeros and subnormals included, both signs, the instruction must
+give the oracle's saturating round-to-nearest-even code.  The fast path
+also relies on that code being monotone in |q|, which the oracle's rounding
+to a grid is."""
 import ctypes
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -17,7 +19,7 @@ from harness import log
 pytestmark = pytest.mark.gpu
 
 LIB = os.path.join(os.path.dirname(__file__), "native", "libhw_probes.so")
-LO, HI = 0x3C800010, 0x43E80000     # the fast path's |q| bit-pattern domain
+LO, HI = 0x00000000, 0x43E80000     # the fast path's |q| bit-pattern domain
 CHUNK = 1 << 24
 
 
