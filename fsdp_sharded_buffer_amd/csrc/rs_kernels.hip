@@ -188,9 +188,6 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #ifndef RS_NT_STORE_BELOW
 #define RS_NT_STORE_BELOW (192ll << 20)
 #endif
-#ifndef RS_QUANT_NT_STORE_BELOW
-#define RS_QUANT_NT_STORE_BELOW RS_NT_STORE_BELOW
-#endif
 
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -969,19 +966,26 @@ __global__ __launch_bounds__(kThreads* F) void quant_kernel(const QuantWork* __r
     return;
   }
   uint32_t slow = 0;  // bit i: slot s0 + i needs the exact path
-  SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
-  if (fast) {
-    // every in-range slot stores its fast code; a slot that needs the exact
-    // quotient is stored again below by the same lane, which wins
+  {
+    SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (lane + (s0 + i) * team < nf) {
         float q[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) q[j] = v[4 * i + j] * rcp;
-        bool safe = true;
+        bool safe = fast;
         uint32_t word;
-        if constexpr (FMT == RS_Q_FP8_E4M3) {
+        if (!fast) {  // tile-uniform: codes that need no division, else exact
+          safe = zero_tile || nan_tile || inf_scale;
+          if (zero_tile)
+            word = 0u;
+          else if (nan_tile)
+            word = FMT == RS_Q_FP8_E4M3 ? 0x7f7f7f7fu : 0u;
+          else
+            word = encode<FMT>(q[0]) | (encode<FMT>(q[1]) << 8) | (encode<FMT>(q[2]) << 16) |
+                   (encode<FMT>(q[3]) << 24);
+        } else if constexpr (FMT == RS_Q_FP8_E4M3) {
           word = e4m3_fast4(q, safe);
         } else {
           float r[4];
@@ -993,36 +997,11 @@ __global__ __launch_bounds__(kThreads* F) void quant_kernel(const QuantWork* __r
           word = int8_from_rint(r[0]) | (int8_from_rint(r[1]) << 8) | (int8_from_rint(r[2]) << 16) |
                  (int8_from_rint(r[3]) << 24);
         }
-        if constexpr (NTS)
-          __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(cbase + sw.off));
-        else
-          *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
-        slow |= safe ? 0u : 1u << i;
-      }
-      sw.next();
-    }
-  } else {
-    // tile-uniform: a zero or NaN scale gives constant codes, an Inf scale
-    // the encoder applied to x * 0 (exactly x / Inf); a subnormal scale
-    // takes the exact path for every slot
-    const bool direct = zero_tile || nan_tile || inf_scale;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (lane + (s0 + i) * team < nf) {
-        if (direct) {
-          uint32_t word;
-          if (zero_tile) {
-            word = 0u;
-          } else if (nan_tile) {
-            word = FMT == RS_Q_FP8_E4M3 ? 0x7f7f7f7fu : 0u;
-          } else {
-            float q[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) q[j] = v[4 * i + j] * rcp;
-            word = encode<FMT>(q[0]) | (encode<FMT>(q[1]) << 8) | (encode<FMT>(q[2]) << 16) |
-                   (encode<FMT>(q[3]) << 24);
-          }
-          *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
+        if (safe) {
+          if constexpr (NTS)
+            __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(cbase + sw.off));
+          else
+            *reinterpret_cast<uint32_t*>(cbase + sw.off) = word;
         } else {
           slow |= 1u << i;
         }
@@ -1566,14 +1545,15 @@ __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
     for (int i = 0; i < NS; ++i) {
       if (lane + (s0 + i) * team < nf) {
         const int64_t q = o0 + sw.off;
-        // the fast codes are stored whatever the test says; a slot that
-        // needs the exact quotient is stored again below by the same lane
         bool safe = tm.fast && tv.fast;
         const uint32_t wm = fast_encode4<FMT>(M[i], tm.rcp, safe);
         const uint32_t wv = fast_encode4<FMT>(V[i], tv.rcp, safe);
-        *reinterpret_cast<uint32_t*>(mc + q) = wm;
-        *reinterpret_cast<uint32_t*>(vc + q) = wv;
-        slow |= safe ? 0u : 1u << i;
+        if (safe) {
+          *reinterpret_cast<uint32_t*>(mc + q) = wm;
+          *reinterpret_cast<uint32_t*>(vc + q) = wv;
+        } else {
+          slow |= 1u << i;
+        }
       }
       sw.next();
     }
@@ -1901,7 +1881,7 @@ extern "C" rs_status rs_block_quant(const rs_layout* L, const float* x, rs_qfmt 
   // sub-block, 4 slots per lane.  Wide tiles: 256-lane tiles spread over F
   // sub-blocks, more of them in launches with few work items.
   // nontemporal code stores for launches that write little (see RS_NT_STORE_BELOW)
-  const bool nts = int64_t(k1 - k0) * L->S < RS_QUANT_NT_STORE_BELOW;
+  const bool nts = int64_t(k1 - k0) * L->S < RS_NT_STORE_BELOW;
   for (int c = 0; c < 2; ++c) {
     const int64_t w0 = L->rank_work[c][k0], nw = L->rank_work[c][k1] - w0;
     if (nw == 0) continue;
