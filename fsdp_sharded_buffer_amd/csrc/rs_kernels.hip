@@ -631,19 +631,38 @@ constexpr int kCombineWaves = 16;
 constexpr int kCombineBatch = 2048;
 
 // One wave's fixed-order share of a fragment's chunk partials: lane `first`
-// of the lanes that stride by `stride` over [cb, ce), four accumulators, then
-// the sum over the wave (every lane of the wave gets it).
+// of the lanes that stride by `stride` over [cb, ce) takes its n partials
+// j = 0, 1, ... in order; partial j goes to accumulator j % 4 while j is
+// below 4 floor(n / 4), the rest to accumulator 0; then (a0 + a1) + (a2 +
+// a3) and the sum over the wave (every lane of the wave gets it).  The
+// partials are loaded kFragBatch at a time, all loads of a batch issued
+// before the first addition, so a lane's few partials cost one round trip
+// to memory instead of one each.  Every partial goes to its accumulator and
+// +0.0 to the others; partials are sums of squares, never -0.0, so adding
+// +0.0 changes no bits.
+constexpr int kFragBatch = 8;
 __device__ __forceinline__ double frag_lane_sum(const double* __restrict__ part, int cb, int ce,
                                                 int first, int stride) {
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-  int i = cb + first;
-  for (; i + 3 * stride < ce; i += 4 * stride) {
-    a0 += part[i];
-    a1 += part[i + stride];
-    a2 += part[i + 2 * stride];
-    a3 += part[i + 3 * stride];
+  const int i0 = cb + first;
+  const int n = i0 < ce ? (ce - i0 + stride - 1) / stride : 0;
+  const int n4 = n & ~3;
+  for (int j0 = 0; j0 < n; j0 += kFragBatch) {
+    double v[kFragBatch];
+#pragma unroll
+    for (int b = 0; b < kFragBatch; ++b)
+      v[b] = j0 + b < n ? part[i0 + (j0 + b) * stride] : 0.0;
+#pragma unroll
+    for (int b = 0; b < kFragBatch; ++b) {
+      const bool grouped = j0 + b < n4;  // else the tail, all into a0
+      switch (b % 4) {
+        case 0: a0 += v[b]; break;
+        case 1: a1 += grouped ? v[b] : 0.0; a0 += grouped ? 0.0 : v[b]; break;
+        case 2: a2 += grouped ? v[b] : 0.0; a0 += grouped ? 0.0 : v[b]; break;
+        default: a3 += grouped ? v[b] : 0.0; a0 += grouped ? 0.0 : v[b]; break;
+      }
+    }
   }
-  for (; i < ce; i += stride) a0 += part[i];
   double s = (a0 + a1) + (a2 + a3);
 #pragma unroll
   for (int o = kWave / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);

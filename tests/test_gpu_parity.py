@@ -590,13 +590,19 @@ def test_pack_bf16_cast_every_fp32_pattern():
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("fmt,amax_value", [("fp8_e4m3", 1344.0), ("int8", 1344.0),
+                                            ("fp8_e4m3", 1791.9998779296875),
                                             ("fp8_e4m3", 448.0), ("int8", 127.0)])
 def test_quant_every_fp32_up_to_amax(fmt, amax_value):
     """Quantisation of every fp32 value x with |x| <= amax, both signs, in
     1 x 16384 tiles whose first element is amax.  With amax = 1344 the scale
     is fl(1344/Q) (3 for E4M3), an inexact reciprocal, so the codes come
     through the reciprocal fast path, its safety windows and the exact
-    fallback over the whole code range.  With amax = Q the scale is 1 and
+    fallback over the whole code range.  amax = 1791.9998779296875 (the fp32
+    below 1792) gives the scale just below 4 whose rounded reciprocal is off
+    by almost half an ulp, the most rounding allows and the largest relative
+    error for amax in [1024, 2048): there x times
+    the reciprocal misses the rounded quotient for about 43% of x, so the
+    window test decides many codes.  With amax = Q the scale is 1 and
     every code is the encoder applied to x itself: every fp32 input of the
     code range, each rounding midpoint included.  Against the oracle's cast
     of the fp32 quotient, with the oracle on host threads."""
