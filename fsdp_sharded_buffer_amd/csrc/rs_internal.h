@@ -125,6 +125,9 @@ struct rs_layout {
   // rank_work[c][m] ends the list.
   std::vector<int64_t> rank_work[2];
   std::vector<int32_t> rank_min_tile_rows[2];  // per class and rank; INT32_MAX without tiles
+  // per class: the median, over the class's tiles, of the width (columns)
+  // of the tensor a tile belongs to; 0 without tiles
+  int64_t median_tile_tensor_cols[2] = {0, 0};
 
   // byte offsets of each table inside the device blob
   size_t off_tensors = 0, off_frags = 0, off_chunks = 0, off_cchunks = 0,

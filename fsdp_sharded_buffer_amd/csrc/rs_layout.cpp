@@ -139,6 +139,7 @@ rs_status build(rs_layout* L) {
   int cur_cls = 0;
   QuantWork cur{};
   std::vector<QuantWork> lists[2];
+  std::vector<std::pair<int64_t, int64_t>> widths[2];  // (tensor cols, tiles) per class
   for (int32_t t = 0; t < n; ++t) {
     const rs_tensor_spec& s = L->specs[t];
     if (s.q_rows <= 0) continue;
@@ -162,6 +163,9 @@ rs_status build(rs_layout* L) {
           return fail(RS_ERR_INVALID_ARG, "rs_layout_create: more than 2^31 quantisation tiles");
         L->rank_min_tile_rows[cls][rank] =
             std::min(L->rank_min_tile_rows[cls][rank], int32_t(rows));
+        if (widths[cls].empty() || widths[cls].back().first != s.cols)
+          widths[cls].push_back({s.cols, 0});
+        ++widths[cls].back().second;
         if (open && cur_cls == cls && cur.rank == rank && cur.team == team && cur.vec == vec &&
             cur.count < 256 / team && cur.base == l && int64_t(cur.t0) + cur.count == idx) {
           ++cur.count;
@@ -189,6 +193,19 @@ rs_status build(rs_layout* L) {
   }
   if (open) lists[cur_cls].push_back(cur);
   L->num_tiles = scale_idx;
+  for (int c = 0; c < 2; ++c) {  // tile-weighted median tensor width of the class
+    std::sort(widths[c].begin(), widths[c].end());
+    int64_t total = 0, seen = 0;
+    for (const auto& w : widths[c]) total += w.second;
+    L->median_tile_tensor_cols[c] = 0;
+    for (const auto& w : widths[c]) {
+      seen += w.second;
+      if (2 * seen >= total) {
+        L->median_tile_tensor_cols[c] = w.first;
+        break;
+      }
+    }
+  }
   // the narrow list, then the wide list; each rank's first item of each
   for (int c = 0; c < 2; ++c) {
     const int64_t base = int64_t(L->work.size());
