@@ -113,6 +113,85 @@ def read_counters(workload: str):
     return d.get("traffic_bytes_per_launch")
 
 
+def live_counters(workload: str, align: int, chunk: int, timeout_s: float = 240.0):
+    """HBM traffic of one whole-buffer scale-add launch, measured in this run:
+    two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE) over a child
+    run of this script in --counter-pass mode, each counter scaled by what it
+    reads for a plain 1 GiB device copy in the same child.  None when
+    rocprofv3 is missing or a pass gives no complete counter file."""
+    import csv
+    import shutil
+    import signal
+    import subprocess
+    import tempfile
+
+    exe = shutil.which("rocprofv3")
+    if not exe:
+        return None
+    per = {}
+    with tempfile.TemporaryDirectory(prefix="rs_pmc_") as tmp:
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            out = os.path.join(tmp, ctr.lower())
+            cmd = [exe, "--pmc", ctr, "-f", "csv", "-d", out, "-o", "c", "--", sys.executable,
+                   os.path.abspath(__file__), "--counter-pass", "--workload", workload,
+                   "--align", str(align), "--chunk", str(chunk)]
+            log(f"live counters: {ctr}")
+            p = subprocess.Popen(cmd, cwd=ROOT, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL,
+                                 env=dict(os.environ, TMPDIR="/tmp"), start_new_session=True)
+            try:
+                p.wait(timeout=timeout_s)
+            except subprocess.TimeoutExpired:
+                os.killpg(p.pid, signal.SIGKILL)
+                p.wait()
+                log(f"live counters: {ctr} pass timed out")
+                return None
+            # the profiler may exit non-zero after the program finished and
+            # its files are whole: the file decides
+            files = [os.path.join(dp, f) for dp, _, fs in os.walk(out) for f in fs
+                     if f.endswith("counter_collection.csv")]
+            if not files:
+                log(f"live counters: no {ctr} file (rocprofv3 exit {p.returncode})")
+                return None
+            copy, kern = [], {}
+            with open(files[0]) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") != ctr:
+                        continue
+                    name, v = r["Kernel_Name"], float(r["Counter_Value"])
+                    if name.startswith("__amd_rocclr_copyBuffer"):
+                        copy.append(v)
+                    elif "scale_add_kernel<0>" in name:
+                        kern.setdefault(int(r["Grid_Size"]), []).append(v)
+            if not copy or not kern:
+                log(f"live counters: {ctr} file lacks the copy or the scale-add dispatches")
+                return None
+            big = kern[max(kern)]
+            per[ctr] = (sum(big) / len(big), max(copy))
+    gib_kib = float(1 << 20)  # 1 GiB copied = 1 GiB read + 1 GiB written, in KiB
+    fetch, fcal = per["FETCH_SIZE"]
+    write, wcal = per["WRITE_SIZE"]
+    return {"traffic_bytes": int(round(fetch * 1024 * gib_kib / fcal + write * 1024 * gib_kib / wcal)),
+            "fetch_kib": round(fetch, 1), "write_kib": round(write, 1),
+            "copy_fetch_kib": round(fcal, 1), "copy_write_kib": round(wcal, 1)}
+
+
+def counter_pass(args):
+    """The child of live_counters: two whole-buffer scale-add launches and a
+    plain 1 GiB device copy (torch), nothing else."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    g = Group(args.workload, args.align, args.chunk, dev, stream)
+    for _ in range(2):
+        g.ranged["scale_add"](0, g.m)
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    g.close()
+
+
 def host_info():
     """Host CPU model (from /proc/cpuinfo, no subprocess), logical CPUs and
     the CPUs this process may run on."""
@@ -480,6 +559,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-ranks", type=int, default=0)
     ap.add_argument("--only", default="", help="comma list of ops to time per op (default all)")
+    ap.add_argument("--no-live-counters", action="store_true",
+                    help="skip measuring the scale-add kernel's HBM traffic with two short "
+                         "rocprofv3 counter passes (the committed profile is read instead)")
+    ap.add_argument("--counter-pass", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) to scale HBM counters")
     ap.add_argument("--per-rank", action="store_true", default=True,
@@ -503,6 +586,9 @@ def main():
     args = ap.parse_args()
     if args.padding_study:
         padding_study(args.align if "--align" in sys.argv else 1, args.study_out)
+        return
+    if args.counter_pass:
+        counter_pass(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the m virtual ranks are slices of one device buffer "
@@ -587,10 +673,19 @@ def main():
         dom = "scale_add" if "scale_add" in timed else next(iter(timed))
         allbytes = dict(g.nbytes, **g.xbytes)
         # the dominant kernel as rocprofv3 names it (template argument 0: x in fp32)
+        traffic, source = None, None
+        if dom == "scale_add":
+            live = None if args.no_live_counters else live_counters(w.name, args.align, args.chunk)
+            if live:
+                traffic, source = live["traffic_bytes"], dict(live, kind="rocprofv3 in this run")
+            else:
+                traffic = read_counters(w.name)
+                if traffic is not None:
+                    source = {"kind": f"profiles/counters_scale_add_{w.name}.json, same kernel source"}
         roof = {"kernel": "scale_add_kernel<0>" if dom == "scale_add" else dom,
                 "bound": "hbm", "achieved": timed[dom]["GB/s"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": timed[dom]["frac_peak"],
-                "traffic": read_counters(w.name) if dom == "scale_add" else None,
+                "unit": "GB/s", "frac": timed[dom]["frac_peak"], "traffic": traffic,
+                "traffic_source": source,
                 "bytes_per_launch": allbytes[dom], "avg_launch_us": timed[dom]["us"]}
         if ceil and dom in OP_MIX:
             c = ceil[OP_MIX[dom]]
