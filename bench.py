@@ -113,7 +113,7 @@ def read_counters(workload: str):
     return d.get("traffic_bytes_per_launch")
 
 
-def live_counters(workload: str, align: int, chunk: int, timeout_s: float = 240.0):
+def live_counters(workload: str, align: int, chunk: int, timeout_s: float = 150.0):
     """HBM traffic of one whole-buffer scale-add launch, measured in this run:
     two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE) over a child
     run of this script in --counter-pass mode, each counter scaled by what it
