@@ -105,7 +105,6 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    to tensors of at least RS_DEQ_XCD_MIN_COLS columns
 //                    (a 70B-layer group: 12% faster; narrower groups lose)
 //   RS_ADAM8_F       256-lane sub-blocks per 8-bit Adam work item of wide tiles
-//   RS_ADAM8_BATCH   8-bit Adam slots loaded ahead of their arithmetic
 //   RS_ADAM8_DIVC    8-bit Adam divides by sqrt(bc2) with div_by_const when
 //                    the constant allows it
 //   RS_ADAM8_SQRT    8-bit Adam takes sqrt(v') with sqrt_rn
@@ -186,9 +185,6 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_ADAM8_F
 #define RS_ADAM8_F 2
-#endif
-#ifndef RS_ADAM8_BATCH
-#define RS_ADAM8_BATCH 1
 #endif
 #ifndef RS_ADAM8_NT
 #define RS_ADAM8_NT 1
@@ -1474,44 +1470,52 @@ __global__ __launch_bounds__(kThreads* F) void adamw8_kernel(
   if (vec) {
     // p' needs m' and v' only, not the new scales: it is written here, so
     // the encode pass after the absmax reduction touches no input
-    constexpr int NB = RS_ADAM8_BATCH < NS ? RS_ADAM8_BATCH : NS;
+    // One slot ahead: slot i + 1's loads are issued before slot i's
+    // arithmetic, so their latency hides behind it.  The arithmetic runs on
+    // every slot (zeros past the tile) and only the absmax and the store
+    // are predicated: M and V are then never merged across branches, which
+    // would copy the whole arrays once per slot.
     SlotWalk sw(lane + s0 * team, team, c4, int(td.ld));
-#pragma unroll
-    for (int b = 0; b < NS; b += NB) {
-      u32x4 P[NB], G[NB];
-      uint32_t CM[NB], CV[NB];
-      int o[NB];
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        o[u] = sw.off;
-        G[u] = P[u] = u32x4{0u, 0u, 0u, 0u};
-        CM[u] = CV[u] = 0u;
-        if (lane + (s0 + b + u) * team < nf) {
-          const int64_t q = o0 + o[u];
-          G[u] = ld16<RS_ADAM8_NT>(g + q);
-          P[u] = ld16<RS_ADAM8_NT>(p + q);
-          CM[u] = *reinterpret_cast<const uint32_t*>(mc + q);
-          CV[u] = *reinterpret_cast<const uint32_t*>(vc + q);
-        }
-        sw.next();
+    u32x4 Pc, Gc;
+    uint32_t CMc, CVc;
+    int oc;
+    auto load_slot = [&](int i, u32x4& P_, u32x4& G_, uint32_t& CM_, uint32_t& CV_, int& o_) {
+      o_ = sw.off;
+      G_ = P_ = u32x4{0u, 0u, 0u, 0u};
+      CM_ = CV_ = 0u;
+      if (lane + (s0 + i) * team < nf) {
+        const int64_t q = o0 + o_;
+        G_ = ld16<RS_ADAM8_NT>(g + q);
+        P_ = ld16<RS_ADAM8_NT>(p + q);
+        CM_ = *reinterpret_cast<const uint32_t*>(mc + q);
+        CV_ = *reinterpret_cast<const uint32_t*>(vc + q);
       }
-      // The arithmetic runs on every slot (zeros past the tile) and only the
-      // absmax and the store are predicated: M and V are then never merged
-      // across branches, which would copy the whole arrays once per slot.
+      sw.next();
+    };
+    load_slot(0, Pc, Gc, CMc, CVc, oc);
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int i = b + u;
-        const bool in = lane + (s0 + i) * team < nf;
-        moments4<FMT>(G[u], CM[u], CV[u], sm_old, sv_old, k, M[i], V[i]);
-        const uint32_t am2 = absmax4(M[i], am), av2 = absmax4(V[i], av);
-        am = in ? am2 : am;
-        av = in ? av2 : av;
-        u32x4 out;
-        out.x = u32(adam_p<DIVC>(f32(P[u].x), M[i][0], V[i][0], k));
-        out.y = u32(adam_p<DIVC>(f32(P[u].y), M[i][1], V[i][1], k));
-        out.z = u32(adam_p<DIVC>(f32(P[u].z), M[i][2], V[i][2], k));
-        out.w = u32(adam_p<DIVC>(f32(P[u].w), M[i][3], V[i][3], k));
-        if (in) st16<RS_ADAM8_NT>(p + o0 + o[u], out);
+    for (int i = 0; i < NS; ++i) {
+      u32x4 Pn, Gn;
+      uint32_t CMn = 0u, CVn = 0u;
+      int on = 0;
+      if (i + 1 < NS) load_slot(i + 1, Pn, Gn, CMn, CVn, on);
+      const bool in = lane + (s0 + i) * team < nf;
+      moments4<FMT>(Gc, CMc, CVc, sm_old, sv_old, k, M[i], V[i]);
+      const uint32_t am2 = absmax4(M[i], am), av2 = absmax4(V[i], av);
+      am = in ? am2 : am;
+      av = in ? av2 : av;
+      u32x4 out;
+      out.x = u32(adam_p<DIVC>(f32(Pc.x), M[i][0], V[i][0], k));
+      out.y = u32(adam_p<DIVC>(f32(Pc.y), M[i][1], V[i][1], k));
+      out.z = u32(adam_p<DIVC>(f32(Pc.z), M[i][2], V[i][2], k));
+      out.w = u32(adam_p<DIVC>(f32(Pc.w), M[i][3], V[i][3], k));
+      if (in) st16<RS_ADAM8_NT>(p + o0 + oc, out);
+      if (i + 1 < NS) {
+        Pc = Pn;
+        Gc = Gn;
+        CMc = CMn;
+        CVc = CVn;
+        oc = on;
       }
     }
   } else {
