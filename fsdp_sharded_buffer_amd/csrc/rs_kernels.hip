@@ -89,6 +89,8 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    RS_QUANT_SMALL_ITEMS work items (narrow tiles: one)
 //   RS_SQNORM_FINE_BELOW  the norm reads fine chunks when the range has
 //                    fewer coarse chunks than this (too few workgroups)
+//   RS_SQNORM_FINE_LANES  lanes per norm workgroup over fine chunks (128:
+//                    all of a 70B-layer rank's 3584 chunks resident at once)
 //   RS_FILL_BYTES    bytes per workgroup of the unmasked zero: one 16-byte
 //                    store per lane, as many short workgroups write fastest
 //   RS_OPT_NT        nontemporal loads and stores of the streams the AdamW
@@ -191,6 +193,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_NT_STORE_BELOW
 #define RS_NT_STORE_BELOW (192ll << 20)
+#endif
+#ifndef RS_SQNORM_FINE_LANES
+#define RS_SQNORM_FINE_LANES 128
 #endif
 #ifndef RS_DEQ_XCD_RUN
 #define RS_DEQ_XCD_RUN 16
@@ -550,8 +555,9 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(char* __restrict__ 
 
 // ----------------------------------------------------------------- sqnorm
 
-// Fixed-order sum over the workgroup: butterfly inside each wave, then the
-// four wave sums in wave order.  Result valid in thread 0.
+// Fixed-order sum over a workgroup of NT lanes: butterfly inside each wave,
+// then the wave sums in wave order.  Result valid in thread 0.
+template <int NT = kThreads>
 __device__ __forceinline__ double block_sum(double v, double* lds) {
 #pragma unroll
   for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -561,7 +567,7 @@ __device__ __forceinline__ double block_sum(double v, double* lds) {
   double s = 0.0;
   if (threadIdx.x == 0) {
     s = lds[0];
-    for (int i = 1; i < kThreads / kWave; ++i) s += lds[i];
+    for (int i = 1; i < NT / kWave; ++i) s += lds[i];
   }
   __syncthreads();
   return s;
@@ -582,11 +588,14 @@ __device__ __forceinline__ void sq4(u32x4 r, double& acc, bool& bad) {
 
 // Per (fine or coarse) chunk ci of the range [c0, c0 + nc): fp64 sum of
 // squares into part[ci - c0], so the scratch holds one partial per chunk of
-// the range.
-__global__ __launch_bounds__(kThreads) void sqnorm_partial_kernel(
+// the range.  NT lanes per workgroup: fine chunks (few-rank ranges) take
+// RS_SQNORM_FINE_LANES, so that more of their short workgroups are resident
+// at once; each lane still adds its vectors in increasing order.
+template <int NT>
+__global__ __launch_bounds__(NT) void sqnorm_partial_kernel(
     const ChunkDesc* __restrict__ chunks, int64_t c0, int64_t nc, const float* __restrict__ x,
     double* __restrict__ part, uint32_t* __restrict__ found_inf) {
-  __shared__ double lds[kThreads / kWave];
+  __shared__ double lds[NT / kWave];
   for (int64_t ii = blockIdx.x; ii < nc; ii += gridDim.x) {
     const int64_t ci = c0 + ii;
     const ChunkDesc c = chunks[ci];
@@ -598,10 +607,10 @@ __global__ __launch_bounds__(kThreads) void sqnorm_partial_kernel(
     const int nv = aligned16(xp) ? n / 4 : 0;
     constexpr int U = 2 * kUnroll;
     int v = threadIdx.x;
-    for (; v + (U - 1) * kThreads < nv; v += U * kThreads) {
+    for (; v + (U - 1) * NT < nv; v += U * NT) {
       u32x4 r[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) r[u] = ld16<RS_SQNORM_NT>(xp + int64_t(v + u * kThreads) * 4);
+      for (int u = 0; u < U; ++u) r[u] = ld16<RS_SQNORM_NT>(xp + int64_t(v + u * NT) * 4);
 #pragma unroll
       for (int u = 0; u < U; ++u) sq4(r[u], acc, bad);
     }
@@ -611,18 +620,18 @@ __global__ __launch_bounds__(kThreads) void sqnorm_partial_kernel(
       u32x4 r[U - 1];
 #pragma unroll
       for (int u = 0; u < U - 1; ++u)
-        if (v + u * kThreads < nv) r[u] = ld16<RS_SQNORM_NT>(xp + int64_t(v + u * kThreads) * 4);
+        if (v + u * NT < nv) r[u] = ld16<RS_SQNORM_NT>(xp + int64_t(v + u * NT) * 4);
 #pragma unroll
       for (int u = 0; u < U - 1; ++u)
-        if (v + u * kThreads < nv) sq4(r[u], acc, bad);
+        if (v + u * NT < nv) sq4(r[u], acc, bad);
     }
-    for (int i = nv * 4 + threadIdx.x; i < n; i += kThreads) {
+    for (int i = nv * 4 + threadIdx.x; i < n; i += NT) {
       const uint32_t u = __float_as_uint(xp[i]);
       acc += sq(u);
       bad |= !finite_bits(u);
     }
     flag_rank(bad, found_inf, c.rank);
-    const double s = block_sum(acc, lds);
+    const double s = block_sum<NT>(acc, lds);
     if (threadIdx.x == 0) part[ii] = s;
   }
 }
@@ -1882,9 +1891,15 @@ rs_status sqnorm_launch(const rs_layout* L, const float* x, double* sq_out, doub
   int fine = 0;
   const int64_t nc = sqnorm_partials(L, k0, k1, &fine);
   const int64_t c0 = (fine ? L->rank_chunk : L->rank_cchunk)[k0];
-  if (nc > 0)
-    launch(sqnorm_partial_kernel, chunk_grid(nc), dim3(kThreads), 0, s,
-           table<ChunkDesc>(L, fine ? L->off_chunks : L->off_cchunks), c0, nc, x, part, found_inf);
+  if (nc > 0) {
+    const ChunkDesc* ct = table<ChunkDesc>(L, fine ? L->off_chunks : L->off_cchunks);
+    if (fine && RS_SQNORM_FINE_LANES == 128)
+      launch(sqnorm_partial_kernel<128>, dim3(unsigned(std::min(nc, max_groups(128)))), dim3(128), 0,
+             s, ct, c0, nc, x, part, found_inf);
+    else
+      launch(sqnorm_partial_kernel<kThreads>, chunk_grid(nc), dim3(kThreads), 0, s, ct, c0, nc, x,
+             part, found_inf);
+  }
   // tensors with a fragment in the range: a contiguous run in buffer order
   const int64_t f0 = L->rank_frag[k0], f1 = L->rank_frag[k1];
   const int32_t t_lo = f1 > f0 ? L->frags[f0].tensor : 0;
