@@ -89,6 +89,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 //                    RS_QUANT_SMALL_ITEMS work items (narrow tiles: one)
 //   RS_SQNORM_FINE_BELOW  the norm reads fine chunks when the range has
 //                    fewer coarse chunks than this (too few workgroups)
+//   RS_UNPACK_SHORT_LANES  lanes per unpack workgroup on launches shorter
+//                    than RS_XCD_REMAP_MIN elements (one rank's share):
+//                    128 is 2-4% faster there; pack keeps 256 (128: 3% slower)
 //   RS_SQNORM_FINE_LANES  lanes per norm workgroup over fine chunks (128:
 //                    all of a 70B-layer rank's 3584 chunks resident at once)
 //   RS_FILL_BYTES    bytes per workgroup of the unmasked zero: one 16-byte
@@ -196,6 +199,9 @@ __device__ __forceinline__ uint32_t int8_encode(float q) {
 #endif
 #ifndef RS_SQNORM_FINE_LANES
 #define RS_SQNORM_FINE_LANES 128
+#endif
+#ifndef RS_UNPACK_SHORT_LANES
+#define RS_UNPACK_SHORT_LANES 128
 #endif
 #ifndef RS_DEQ_XCD_RUN
 #define RS_DEQ_XCD_RUN 16
@@ -317,30 +323,30 @@ constexpr int kUnroll = RS_UNROLL;
 // Convert-copy n elements; the workgroup's lanes stride over 8-element
 // vectors.  Each pass issues the loads of kUnroll vectors per lane (the
 // last pass predicated) before any of their stores.
-template <int SK, int DK, bool NT>
+template <int SK, int DK, bool NT, int LANES = kThreads>
 __device__ __forceinline__ void copy_run(const void* src, void* dst, int n) {
   const int nv = (aligned16(src) && aligned16(dst)) ? n / 8 : 0;
-  for (int b = threadIdx.x; b < nv; b += kUnroll * kThreads) {
+  for (int b = threadIdx.x; b < nv; b += kUnroll * LANES) {
     Pack8<SK> r[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (b + u * kThreads < nv) r[u] = ld8<SK, NT>(src, int64_t(b + u * kThreads) * 8);
+      if (b + u * LANES < nv) r[u] = ld8<SK, NT>(src, int64_t(b + u * LANES) * 8);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (b + u * kThreads < nv)
-        st8<DK, NT>(dst, int64_t(b + u * kThreads) * 8, Conv<SK, DK>::run(r[u]));
+      if (b + u * LANES < nv)
+        st8<DK, NT>(dst, int64_t(b + u * LANES) * 8, Conv<SK, DK>::run(r[u]));
   }
-  for (int i = nv * 8 + threadIdx.x; i < n; i += kThreads) copy1<SK, DK>(src, dst, i);
+  for (int i = nv * 8 + threadIdx.x; i < n; i += LANES) copy1<SK, DK>(src, dst, i);
 }
 
-template <int K, bool NT>
+template <int K, bool NT, int LANES = kThreads>
 __device__ __forceinline__ void zero_run(void* dst, int64_t n) {
   const int64_t nv = aligned16(dst) ? n * esize<K>() / 16 : 0;
   char* d = static_cast<char*>(dst);
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int64_t v = threadIdx.x; v < nv; v += kThreads) st16<NT>(d + v * 16, z);
+  for (int64_t v = threadIdx.x; v < nv; v += LANES) st16<NT>(d + v * 16, z);
   const int64_t done = nv * 16 / esize<K>();
-  for (int64_t i = done + threadIdx.x; i < n; i += kThreads) {
+  for (int64_t i = done + threadIdx.x; i < n; i += LANES) {
     if constexpr (K == 0)
       static_cast<float*>(dst)[i] = 0.0f;
     else
@@ -381,8 +387,8 @@ __device__ __forceinline__ int64_t first_item(int64_t b, int64_t G, XcdOrder o) 
   return (round << sr) + ((within & 7) << o.shift) + (within >> 3);
 }
 
-template <int SK, int DK>
-__global__ __launch_bounds__(kThreads) void pack_kernel(const ChunkDesc* __restrict__ chunks,
+template <int SK, int DK, int LANES = kThreads>
+__global__ __launch_bounds__(LANES) void pack_kernel(const ChunkDesc* __restrict__ chunks,
                                                         int64_t c0, int64_t nc,
                                                         const void* const* __restrict__ src,
                                                         void* __restrict__ buf, XcdOrder run) {
@@ -390,16 +396,16 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const ChunkDesc* __restr
     const ChunkDesc c = chunks[c0 + i];
     char* d = static_cast<char*>(buf) + c.buf_off * esize<DK>();
     if (c.tensor < 0) {
-      zero_run<DK, RS_PACK_NT>(d, c.len);
+      zero_run<DK, RS_PACK_NT, LANES>(d, c.len);
     } else {
       const char* s = static_cast<const char*>(src[c.tensor]) + c.ten_off * esize<SK>();
-      copy_run<SK, DK, RS_PACK_NT>(s, d, c.len);
+      copy_run<SK, DK, RS_PACK_NT, LANES>(s, d, c.len);
     }
   }
 }
 
-template <int SK, int DK>
-__global__ __launch_bounds__(kThreads) void unpack_kernel(const ChunkDesc* __restrict__ chunks,
+template <int SK, int DK, int LANES = kThreads>
+__global__ __launch_bounds__(LANES) void unpack_kernel(const ChunkDesc* __restrict__ chunks,
                                                           int64_t c0, int64_t nc,
                                                           const void* __restrict__ buf,
                                                           void* const* __restrict__ dst,
@@ -409,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const ChunkDesc* __res
     if (c.tensor < 0) continue;
     const char* s = static_cast<const char*>(buf) + c.buf_off * esize<SK>();
     char* d = static_cast<char*>(dst[c.tensor]) + c.ten_off * esize<DK>();
-    copy_run<SK, DK, RS_PACK_NT>(s, d, c.len);
+    copy_run<SK, DK, RS_PACK_NT, LANES>(s, d, c.len);
   }
 }
 
@@ -1788,16 +1794,25 @@ extern "C" rs_status rs_unpack(const rs_layout* L, const void* buf, rs_dtype buf
   if (nc == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ChunkDesc* ch = table<ChunkDesc>(L, L->off_chunks);
-  const dim3 g = chunk_grid(nc), b(kThreads);
+  // short launches (those xcd_run leaves in the hardware order, one rank's
+  // share say) take RS_UNPACK_SHORT_LANES lanes per workgroup
   const XcdOrder run = xcd_run(L, k0, k1, false);
+  constexpr int kShort = RS_UNPACK_SHORT_LANES;
+  const bool narrow = run.mode == kXcdNone;
+  const dim3 g(unsigned(std::min(nc, max_groups(narrow ? kShort : kThreads)))),
+      b(narrow ? kShort : kThreads);
+#define RS_UNPACK_LAUNCH(SK, DK)                                                        \
+  (narrow ? launch((unpack_kernel<SK, DK, kShort>), g, b, 0, s, ch, c0, nc, buf, dst, run) \
+          : launch((unpack_kernel<SK, DK>), g, b, 0, s, ch, c0, nc, buf, dst, run))
   if (buf_dt == RS_BF16 && dst_dt == RS_BF16)
-    launch((unpack_kernel<1, 1>), g, b, 0, s, ch, c0, nc, buf, dst, run);
+    RS_UNPACK_LAUNCH(1, 1);
   else if (buf_dt == RS_BF16 && dst_dt == RS_F32)
-    launch((unpack_kernel<1, 0>), g, b, 0, s, ch, c0, nc, buf, dst, run);
+    RS_UNPACK_LAUNCH(1, 0);
   else if (buf_dt == RS_F32 && dst_dt == RS_F32)
-    launch((unpack_kernel<0, 0>), g, b, 0, s, ch, c0, nc, buf, dst, run);
+    RS_UNPACK_LAUNCH(0, 0);
   else
-    launch((unpack_kernel<0, 1>), g, b, 0, s, ch, c0, nc, buf, dst, run);
+    RS_UNPACK_LAUNCH(0, 1);
+#undef RS_UNPACK_LAUNCH
   return after_launch(fn);
 } catch (...) {
   return rs::on_exception("rs_unpack");
