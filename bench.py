@@ -595,6 +595,19 @@ def main():
               "and this library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    # The counter passes run before this process touches the GPU, so the
+    # profiler they start (which replaces itself with the program it
+    # profiles) descends from a process without GPU state.  None run under
+    # a profiler, which does not nest: rocprofv3 sets ROCPROF_OUTPUT_PATH
+    # for the program it runs.
+    only = [o for o in args.only.split(",") if o]
+    live = None
+    if not args.per_rank_only and not args.no_live_counters and (not only or "scale_add" in only):
+        if "ROCPROF_OUTPUT_PATH" in os.environ:
+            log("live counters: skipped under rocprofv3")
+        else:
+            live = live_counters(args.workload, args.align, args.chunk)
+
     import torch
 
     dev = torch.device("cuda", 0)
@@ -643,8 +656,7 @@ def main():
             torch.cuda.synchronize()
             del a, b
 
-        only = [o for o in args.only.split(",") if o] or (step_names + extra_names)
-        res = time_whole(g, only, event_ms, args.samples)
+        res = time_whole(g, only or (step_names + extra_names), event_ms, args.samples)
         per_op = {k: v for k, v in res.items() if k in g.ranged}
         per_extra = {k: v for k, v in res.items() if k in g.ranged_extra}
 
@@ -675,7 +687,6 @@ def main():
         # the dominant kernel as rocprofv3 names it (template argument 0: x in fp32)
         traffic, source = None, None
         if dom == "scale_add":
-            live = None if args.no_live_counters else live_counters(w.name, args.align, args.chunk)
             if live:
                 traffic, source = live["traffic_bytes"], dict(live, kind="rocprofv3 in this run")
             else:
