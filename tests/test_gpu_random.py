@@ -5,7 +5,11 @@ up to 64 ranks, 1 x k tiles up to 1 x 16384, tall k x 1 tiles up to
 16384 rows, square blocks of 8-128 with partial edges, alignment up to 64
 and chunks up to 4096.  Every operation runs on the whole rank range and on
 a random sub-range and is compared with the oracle (bit-exact; norms within
-1e-5 relative of fp64), with canary guard bands around every output."""
+1e-5 relative of fp64), with canary guard bands around every output.
+RS_RANDOM_SEED0 (default 0) shifts every seed, for a sweep over other
+groups than the ones this file runs by default."""
+import os
+
 import numpy as np
 import pytest
 
@@ -23,6 +27,7 @@ BF16_CANARY = 0x7FA5
 U8_CANARY = 0xAB
 N_GROUPS = 120
 N_WIDE = 40
+SEED0 = int(os.environ.get("RS_RANDOM_SEED0", "0"))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -105,8 +110,8 @@ def _sync():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("gen,seed", [("basic", s) for s in range(N_GROUPS)] +
-                         [("wide", s) for s in range(N_WIDE)])
+@pytest.mark.parametrize("gen,seed", [("basic", SEED0 + s) for s in range(N_GROUPS)] +
+                         [("wide", SEED0 + s) for s in range(N_WIDE)])
 def test_random_group(gen, seed):
     import torch
     w, A, chunk, rng = (_random_workload if gen == "basic" else _wide_workload)(seed)
