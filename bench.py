@@ -175,6 +175,19 @@ def live_counters(workload: str, align: int, chunk: int, timeout_s: float = 150.
             "copy_fetch_kib": round(fcal, 1), "copy_write_kib": round(wcal, 1)}
 
 
+def want_live_counters(args, only, environ) -> bool:
+    """Whether this run measures the scale-add kernel's traffic itself: only
+    when it times that kernel over the whole buffer, was not told not to, and
+    is not itself under rocprofv3 (which sets ROCPROF_OUTPUT_PATH for the
+    program it runs, and does not nest)."""
+    if args.per_rank_only or args.no_live_counters or (only and "scale_add" not in only):
+        return False
+    if "ROCPROF_OUTPUT_PATH" in environ:
+        log("live counters: skipped under rocprofv3")
+        return False
+    return True
+
+
 def counter_pass(args):
     """The child of live_counters: two whole-buffer scale-add launches and a
     plain 1 GiB device copy (torch), nothing else."""
@@ -597,16 +610,11 @@ def main():
 
     # The counter passes run before this process touches the GPU, so the
     # profiler they start (which replaces itself with the program it
-    # profiles) descends from a process without GPU state.  None run under
-    # a profiler, which does not nest: rocprofv3 sets ROCPROF_OUTPUT_PATH
-    # for the program it runs.
+    # profiles) descends from a process without GPU state.
     only = [o for o in args.only.split(",") if o]
     live = None
-    if not args.per_rank_only and not args.no_live_counters and (not only or "scale_add" in only):
-        if "ROCPROF_OUTPUT_PATH" in os.environ:
-            log("live counters: skipped under rocprofv3")
-        else:
-            live = live_counters(args.workload, args.align, args.chunk)
+    if want_live_counters(args, only, os.environ):
+        live = live_counters(args.workload, args.align, args.chunk)
 
     import torch
 

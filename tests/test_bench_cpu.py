@@ -1,6 +1,9 @@
-"""Host-side checks of bench.py's byte accounting (CPU only): the per-rank
-algorithmic bytes of every operation sum to the whole-buffer bytes on every
-group, and the whole-buffer bytes follow their definitions."""
+"""Host-side checks of bench.py (CPU only): the per-rank algorithmic bytes
+of every operation sum to the whole-buffer bytes on every group, the
+whole-buffer bytes follow their definitions, and the HBM counter passes run
+only where they can."""
+import argparse
+
 import pytest
 
 import bench as Bn
@@ -30,3 +33,17 @@ def test_rank_bytes_sum_to_whole_buffer(name):
     Eq = sum(t.numel for t in w.tensors if t.q_rows)
     assert whole["scale_add"] == 12 * E and whole["zero"] == 4 * w.m * S
     assert whole["block_quant"] == 5 * Eq + 4 * nt
+
+
+def test_live_counters_only_where_they_can_run():
+    def a(**kw):
+        d = dict(per_rank_only=False, no_live_counters=False)
+        d.update(kw)
+        return argparse.Namespace(**d)
+
+    assert Bn.want_live_counters(a(), [], {})
+    assert Bn.want_live_counters(a(), ["pack", "scale_add"], {})
+    assert not Bn.want_live_counters(a(), ["block_quant"], {})          # scale/add not timed
+    assert not Bn.want_live_counters(a(per_rank_only=True), [], {})
+    assert not Bn.want_live_counters(a(no_live_counters=True), [], {})
+    assert not Bn.want_live_counters(a(), [], {"ROCPROF_OUTPUT_PATH": "out"})   # under rocprofv3
