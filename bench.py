@@ -457,11 +457,15 @@ class Group:
         self.bufs = self.ranged = self.ranged_extra = None
 
 
-def time_per_rank(g, names, event_ms, stream, samples):
+def time_per_rank(g, names, event_ms, stream, samples, graph=False):
     """Each operation on one rank's shard: launches over [k, k+1), cycling k
     so that each launch reads other memory than the last.  The mean comes
     from whole cycles timed at their ends only; the slowest rank from a pass
-    with an event between launches (which adds the events' own cost)."""
+    with an event between launches (which adds the events' own cost).  With
+    graph, the cycle is also captured once into a HIP graph and replayed
+    (stream must be the current stream and not the null stream): the host
+    then issues one launch per cycle, so a mean that drops says the eager
+    cycle was bound by the host's launch rate."""
     import torch
     m = g.m
     allr = dict(g.ranged, **g.ranged_extra)
@@ -470,6 +474,14 @@ def time_per_rank(g, names, event_ms, stream, samples):
         f = allr[name]
         cycle = lambda f=f: [f(k, k + 1) for k in range(m)]
         med, _, _ = event_ms(cycle, samples)
+        gmed = None
+        if graph:
+            gr = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gr, stream=stream):
+                cycle()
+            gmed, _, _ = event_ms(gr.replay, samples)
+            del gr
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(m + 1)]
         times = [[] for _ in range(m)]
         for _ in range(5):
@@ -488,8 +500,12 @@ def time_per_rank(g, names, event_ms, stream, samples):
             "GB/s": round(byt / (med * 1e-3) / 1e9, 1),
             "slowest_rank": worst, "slowest_us_with_events": round(float(each[worst]) * 1e3, 2),
             "slowest_GB/s_with_events": round(g.rb[worst][name] / (each[worst] * 1e-3) / 1e9, 1)}
+        if gmed is not None:
+            res[name]["graph_mean_us"] = round(gmed / m * 1e3, 2)
+            res[name]["graph_GB/s"] = round(byt / (gmed * 1e-3) / 1e9, 1)
         log(f"per rank {g.w.name} {name:12s} mean {med / m * 1e3:8.1f} us  "
-            f"{res[name]['GB/s']:8.1f} GB/s; slowest rank {worst}")
+            f"{res[name]['GB/s']:8.1f} GB/s; slowest rank {worst}" +
+            (f"; graph {gmed / m * 1e3:8.1f} us" if gmed is not None else ""))
     return res
 
 
@@ -585,6 +601,9 @@ def main():
     ap.add_argument("--per-rank-only", action="store_true",
                     help="only the per-rank cycles (for tracing them): no step, no whole-buffer "
                          "timings, no extras")
+    ap.add_argument("--per-rank-graph", action="store_true",
+                    help="run on a side stream and also time each per-rank cycle replayed from a "
+                         "HIP graph (per_rank[op].graph_mean_us)")
     ap.add_argument("--no-torch-ref", action="store_true",
                     help="skip timing torch's own copy/axpy/fill/fused optimizers for context")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -619,6 +638,8 @@ def main():
     import torch
 
     dev = torch.device("cuda", 0)
+    if args.per_rank_graph:  # graphs are captured on a stream of their own, not the null stream
+        torch.cuda.set_stream(torch.cuda.Stream(dev))
     stream = torch.cuda.current_stream(dev)
     event_ms = event_timer(torch, stream)
     records = []
@@ -670,7 +691,8 @@ def main():
 
     per_rank = None
     if args.per_rank or args.per_rank_only:
-        per_rank = time_per_rank(g, step_names + extra_names, event_ms, stream, args.samples)
+        per_rank = time_per_rank(g, step_names + extra_names, event_ms, stream, args.samples,
+                                 graph=args.per_rank_graph)
         if not args.no_ceiling and not args.per_rank_only:
             per_rank["ceilings_at_rank_size"] = rank_ceilings(torch, dev, stream, event_ms, g)
             with_ceiling({k: v for k, v in per_rank.items() if k in OP_MIX},
@@ -721,7 +743,8 @@ def main():
         g5 = Group("llama70b_layer", args.align, args.chunk, dev, stream)
         full = with_ceiling(time_whole(g5, ["pack", "unpack", "block_quant"], event_ms,
                                        min(args.samples, 7)), ceil)
-        pr5 = time_per_rank(g5, step_names + extra_names, event_ms, stream, min(args.samples, 7))
+        pr5 = time_per_rank(g5, step_names + extra_names, event_ms, stream, min(args.samples, 7),
+                            graph=args.per_rank_graph)
         if not args.no_ceiling:
             pr5["ceilings_at_rank_size"] = rank_ceilings(torch, dev, stream, event_ms, g5)
             with_ceiling({k: v for k, v in pr5.items() if k in OP_MIX}, pr5["ceilings_at_rank_size"])
